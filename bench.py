@@ -1,0 +1,290 @@
+#!/usr/bin/env python3
+"""Benchmark of one rank's sharded ZeRO/FSDP update on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload 7p5b|llama8b|gpt2|tiny]
+
+A step is the rank's shard update: the mean of N bf16 gradient contributions,
+fused AdamW on the fp32 master/m/v shard, and the bf16 copy into the rank's
+slot of the all-gather buffer -- one launch of the single-pass kernel
+(zs_sharded_step). Inputs are synthetic and resident in HBM before timing.
+Reported value: shard elements updated per second (Gelem/s).
+
+Also measured (in "parts"): the same update as two launches (reduce, then AdamW
+with the fused cast), each kernel alone, the unshard copy-out of one Llama-3-8B
+decoder block, and the pack of the shard. The JSON line carries the roofline of
+the dominant kernel (HIP-event time on the launch stream) and the CPU oracle
+timed on a bounded sample of the same inputs.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, AMD's published figure
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "fsdp_sharded_optimizer_flatparameter_amd", "csrc")
+
+METRIC = "shard update Gelem/s and achieved HBM GB/s (% of peak), 1 MI355X"
+
+WORKLOADS = {
+    "7p5b": dict(shapes="flat_7p5b", world=64, rank=63, wd=0.1,
+                 desc="7.5B flat parameters, N=64 simulated ranks, rank 63's shard"),
+    "llama8b": dict(shapes="llama3_8b", world=8, rank=7, wd=0.01,
+                    desc="Llama-3-8B parameter list, N=8 simulated ranks, rank 7's shard"),
+    "gpt2": dict(shapes="gpt2_small", world=8, rank=7, wd=0.01,
+                 desc="GPT-2-small parameter list, N=8 simulated ranks, rank 7's shard"),
+    "tiny": dict(shapes="tiny", world=4, rank=3, wd=0.01,
+                 desc="4 x 512x512 parameters, N=4 simulated ranks, rank 3's shard"),
+}
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str, kernel: str, src_hash: str):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it
+    was taken from the current kernel sources; None otherwise."""
+    path = os.path.join(PROFILES, f"hbm_traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("source_hash") != src_hash or vals.get("kernel") != kernel:
+        return None
+    try:
+        return float(vals["bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def event_time_ms(fn, iters: int, stream) -> float:
+    """Average ms per call of fn over `iters` calls, HIP events on `stream`."""
+    import torch
+
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(iters):
+        fn(i)
+    end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end) / iters
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="7p5b", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-parts", action="store_true", help="time only the step")
+    ap.add_argument("--cpu-windows", type=int, default=24, help="2^20-element windows for the oracle timing")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU's shard update; --gpus {args.gpus} is not supported "
+              "(the update of each rank is independent -- run one process per GPU).", file=sys.stderr)
+        return 2
+    if int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU only (WORLD_SIZE > 1 given)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import fsdp_sharded_optimizer_flatparameter_amd as zs
+    from synth import gen, shapes
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    zs.load()  # fails loudly when libzs.so is not built
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    wl = WORKLOADS[args.workload]
+    numels = shapes.numels(getattr(shapes, wl["shapes"])())
+    world, rank = wl["world"], wl["rank"]
+    _, total, padded, S = zs.zs_flat_layout(numels, world)
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=wl["wd"])
+
+    # ---- inputs, resident in HBM before any timing
+    g0 = gen.device_generator(1000 + sorted(WORKLOADS).index(args.workload), dev)
+    rows = [gen.device_normal(g0, S, gen.GRAD_SIGMA, torch.bfloat16, dev) for _ in range(world)]
+    theta = gen.device_normal(g0, S, gen.THETA_SIGMA, None, dev)
+    m = torch.zeros(S, device=dev)
+    v = torch.zeros(S, device=dev)
+    gather = torch.empty(padded, device=dev, dtype=torch.bfloat16)
+    slot = gather[rank * S:(rank + 1) * S]
+    gbuf = torch.empty(S, device=dev)
+    torch.cuda.synchronize()
+
+    # bit-identical host copies of the oracle's sample (taken before any update)
+    win = 1 << 20
+    nwin = max(1, min(args.cpu_windows, S // win)) if not args.no_cpu_baseline else 0
+    rng = np.random.default_rng(0)
+    starts = sorted(int(x) for x in rng.choice(max(1, S // win), size=nwin, replace=False)) if nwin else []
+    cpu_inputs = []
+    for s0 in starts:
+        a, b = s0 * win, min(S, s0 * win + win)
+        r_h = np.stack([r[a:b].view(torch.int16).cpu().numpy().view(np.uint16) for r in rows])
+        cpu_inputs.append((r_h, theta[a:b].cpu().numpy(), m[a:b].cpu().numpy(), v[a:b].cpu().numpy()))
+
+    step_no = [0]
+
+    def fused_step(_i):
+        step_no[0] += 1
+        zs.zs_sharded_step(rows, theta, m, v, step=step_no[0], bf16_out=slot, **hp)
+
+    # ---- the step: warmup, then exactly K timed steps between synchronisations
+    for i in range(args.warmup):
+        fused_step(i)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(args.steps):
+        fused_step(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / args.steps
+    gelem = S / (ms_step * 1e-3) / 1e9
+
+    n_rows_bytes = 2 * world
+    fused_bpe = n_rows_bytes + 26          # rows + read theta,m,v + write theta,m,v + bf16
+    reduce_bpe = n_rows_bytes + 4          # rows + write g
+    adamw_bpe = 30                         # read g,theta,m,v + write theta,m,v + bf16
+    cast_bpe = 6
+    achieved = fused_bpe * S / (ms_step * 1e-3) / 1e9
+    src_hash = source_hash()
+    kernel_name = "k_fused"
+    traffic = read_traffic(args.workload, kernel_name, src_hash)
+
+    parts = {}
+    if not args.no_parts:
+        iters = max(10, args.steps)
+        t_reduce = event_time_ms(lambda i: zs.zs_reduce_grads(rows, gbuf), iters, stream)
+
+        def adamw_call(i):
+            step_no[0] += 1
+            zs.zs_adamw_step(theta, m, v, gbuf, step=step_no[0], bf16_out=slot, **hp)
+
+        t_adamw = event_time_ms(adamw_call, iters, stream)
+        t_cast = event_time_ms(lambda i: zs.zs_cast_for_gather(theta, slot), iters, stream)
+        parts["two_call_step"] = dict(ms=t_reduce + t_adamw, gelem_s=S / ((t_reduce + t_adamw) * 1e-3) / 1e9,
+                                      bytes_per_elem=reduce_bpe + adamw_bpe)
+        for name, t, bpe in (("reduce", t_reduce, reduce_bpe), ("adamw_cast", t_adamw, adamw_bpe),
+                             ("cast", t_cast, cast_bpe), ("fused_step", ms_step, fused_bpe)):
+            gbs = bpe * S / (t * 1e-3) / 1e9
+            parts[name] = dict(ms=round(t, 5), bytes_per_elem=bpe, gb_s=round(gbs, 1),
+                               frac_of_peak=round(gbs / PEAK_HBM_GBS, 4))
+        del gbuf
+
+        # unshard copy-out of one Llama-3-8B decoder block (218,112,000 elements)
+        blk = shapes.llama3_8b_block()
+        bn = shapes.numels(blk)
+        gathered_blk = gen.device_normal(g0, sum(bn), 1.0, torch.bfloat16, dev)
+        dst = [torch.empty(s, device=dev, dtype=torch.bfloat16) for _, s in blk]
+        table = zs.ParamTable(dst)
+        t_co = event_time_ms(lambda i: zs.zs_copy_out(gathered_blk, table), 10, stream)
+        gbs = 4 * sum(bn) / (t_co * 1e-3) / 1e9
+        parts["copy_out_llama8b_block"] = dict(ms=round(t_co, 5), elems=sum(bn), bytes_per_elem=4,
+                                               gb_s=round(gbs, 1), frac_of_peak=round(gbs / PEAK_HBM_GBS, 4))
+        del gathered_blk, dst, table
+
+        # pack of this shard from per-parameter fp32 tensors (one-time setup work);
+        # a single 7.5e9-element parameter is represented by the rank's slice of it
+        if args.workload == "7p5b":
+            src = [gen.device_normal(g0, S, gen.THETA_SIGMA, None, dev)]
+            ptable, pworld, prank = zs.ParamTable(src), 1, 0
+        else:
+            src = [gen.device_normal(g0, n, gen.THETA_SIGMA, None, dev) for n in numels]
+            ptable, pworld, prank = zs.ParamTable(src), world, rank
+        t_pack = event_time_ms(lambda i: zs.zs_pack_shard(ptable, pworld, prank, theta, m, v), 5, stream)
+        gbs = 16 * S / (t_pack * 1e-3) / 1e9
+        parts["pack_shard"] = dict(ms=round(t_pack, 5), bytes_per_elem=16, gb_s=round(gbs, 1),
+                                   frac_of_peak=round(gbs / PEAK_HBM_GBS, 4))
+        del src, ptable
+        torch.cuda.synchronize()
+
+    # ---- CPU oracle on a bounded sample of the same inputs
+    cpu = None
+    if cpu_inputs:
+        from oracle import adamw as oadamw
+        from oracle import step as ostep
+
+        hpo = oadamw.HParams(**hp)
+        c0, w0 = time.process_time(), time.perf_counter()
+        done = 0
+        for r_h, th_h, m_h, v_h in cpu_inputs:
+            ostep.sharded_step(r_h, th_h, m_h, v_h, 1, hpo)
+            done += th_h.size
+        wall = time.perf_counter() - w0
+        cpu_s = time.process_time() - c0
+        cpu = {"value": round(done / wall / 1e9, 6), "unit": "Gelem/s",
+               "cores": max(1, round(cpu_s / wall)), "kind": "oracle",
+               "sample": f"{len(cpu_inputs)} windows of {win} shard elements x {world} bf16 rows "
+                         f"(the GPU's own inputs), fp64 NumPy oracle: exact mean, AdamW, bf16 cast; "
+                         f"{wall:.1f} s wall"}
+
+    out = {
+        "metric": METRIC,
+        "value": round(gelem, 4),
+        "unit": "Gelem/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": wl["desc"],
+            "shard_elems": S,
+            "world": world,
+            "rank": rank,
+            "contributions": "bf16",
+            "step": "mean of N contributions + AdamW (fp32 master/m/v) + bf16 cast, one pass",
+            "adamw": hp,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": kernel_name,
+            "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "algorithmic_bytes_per_elem": fused_bpe,
+            "traffic": traffic,
+        },
+        "cpu_baseline": cpu,
+        "parts": parts,
+        "source_hash": src_hash,
+    }
+    print(json.dumps(out))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,219 @@
+"""Python binding of libzs: the C-ABI calls under the same names, taking torch tensors.
+
+Argument marshalling only -- every step of the update runs in the HIP kernels
+of libzs. PyTorch supplies device memory and the stream (by default the
+current stream of the tensors' device); every call is asynchronous on it.
+
+Errors from the library raise ZsArgumentError (a ValueError) for bad
+arguments and ZsError (a RuntimeError) for HIP failures; tensors that are not
+contiguous device tensors of the expected dtype raise ValueError before the
+library is called.
+"""
+from __future__ import annotations
+
+import ctypes as C
+
+import torch
+
+from . import _lib as L
+from ._lib import ZS_BF16, ZS_F32, ZsArgumentError, ZsError  # noqa: F401
+
+_DTYPES = {torch.float32: ZS_F32, torch.bfloat16: ZS_BF16}
+
+
+def _lib():
+    return L.load()
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(stream, device):
+    if stream is None:
+        return C.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return C.c_void_p(stream.cuda_stream)
+    return C.c_void_p(int(stream))
+
+
+def _hparams(lr, beta1, beta2, eps, weight_decay, step) -> L.AdamWHParams:
+    return L.AdamWHParams(float(lr), float(beta1), float(beta2), float(eps), float(weight_decay),
+                          int(step))
+
+
+# ---------------------------------------------------------------- layout
+
+def zs_flat_layout(numels, world: int):
+    """(offsets, total T, padded P, shard S) of a FlatParameter over `world` ranks."""
+    n = len(numels)
+    arr = (C.c_int64 * max(n, 1))(*[int(x) for x in numels])
+    offs = (C.c_int64 * max(n, 1))()
+    total, padded, shard = C.c_int64(), C.c_int64(), C.c_int64()
+    L.check("zs_flat_layout", _lib().zs_flat_layout(
+        arr, n, int(world), offs, C.byref(total), C.byref(padded), C.byref(shard)))
+    return list(offs[:n]), total.value, padded.value, shard.value
+
+
+class ParamTable:
+    """Descriptor table of one unit's parameters, in flat order.
+
+    The host copy is checked by zs_check_layout; the device copy (24 bytes per
+    parameter) is what the pack and copy-out kernels read. The tensors are
+    kept referenced for the table's lifetime.
+    """
+
+    def __init__(self, tensors, device=None):
+        if len(tensors) == 0:
+            raise ValueError("a unit needs at least one parameter")
+        dtype = tensors[0].dtype
+        if dtype not in _DTYPES:
+            raise ValueError(f"unsupported parameter dtype {dtype}")
+        for i, t in enumerate(tensors):
+            _dev(t, f"param[{i}]", dtype)
+        self.tensors = list(tensors)
+        self.dtype = dtype
+        self.nparams = len(tensors)
+        self.offsets, self.total, _, _ = zs_flat_layout([t.numel() for t in tensors], 1)
+        host = (L.ParamDesc * self.nparams)()
+        for i, (t, off) in enumerate(zip(self.tensors, self.offsets)):
+            host[i].ptr = t.data_ptr()
+            host[i].flat_offset = off
+            host[i].numel = t.numel()
+        L.check("zs_check_layout", _lib().zs_check_layout(host, self.nparams, self.total))
+        device = device if device is not None else tensors[0].device
+        raw = torch.frombuffer(bytearray(bytes(host)), dtype=torch.uint8)
+        self.device_table = raw.to(device)
+        torch.cuda.current_stream(device).synchronize()  # the host staging copy is released
+
+    @property
+    def ptr(self):
+        return C.c_void_p(self.device_table.data_ptr())
+
+
+# ---------------------------------------------------------------- pack / copy-out
+
+def zs_pack_shard(table: ParamTable, world: int, rank: int, master, exp_avg=None, exp_avg_sq=None,
+                  stream=None):
+    _dev(master, "master", torch.float32)
+    for name, t in (("exp_avg", exp_avg), ("exp_avg_sq", exp_avg_sq)):
+        if t is not None:
+            _dev(t, name, torch.float32)
+            if t.numel() != master.numel():
+                raise ValueError(f"{name} must have the master's size")
+    L.check("zs_pack_shard", _lib().zs_pack_shard(
+        table.ptr, table.nparams, table.total, _DTYPES[table.dtype], int(world), int(rank),
+        master.numel(), _ptr(master), _ptr(exp_avg), _ptr(exp_avg_sq),
+        _stream(stream, master.device)))
+
+
+def zs_copy_out(gathered, table: ParamTable, stream=None):
+    _dev(gathered, "gathered", torch.bfloat16)
+    if table.dtype != torch.bfloat16:
+        raise ValueError("copy-out destinations must be bf16")
+    L.check("zs_copy_out", _lib().zs_copy_out(
+        _ptr(gathered), gathered.numel(), table.ptr, table.nparams, table.total,
+        _stream(stream, gathered.device)))
+
+
+# ---------------------------------------------------------------- reduce / AdamW / cast
+
+def _rows(rows, n):
+    if len(rows) == 0:
+        raise ValueError("need at least one gradient contribution")
+    dtype = rows[0].dtype
+    if dtype not in _DTYPES:
+        raise ValueError(f"unsupported contribution dtype {dtype}")
+    for i, r in enumerate(rows):
+        _dev(r, f"rows[{i}]", dtype)
+        if r.numel() != n:
+            raise ValueError(f"rows[{i}] has {r.numel()} elements, expected {n}")
+    arr = (C.c_void_p * len(rows))(*[r.data_ptr() for r in rows])
+    return arr, len(rows), _DTYPES[dtype]
+
+
+def zs_workspace_bytes(n: int) -> int:
+    return int(_lib().zs_workspace_bytes(int(n)))
+
+
+def zs_reduce_grads(rows, grad_out, sumsq_out=None, workspace=None, stream=None):
+    _dev(grad_out, "grad_out", torch.float32)
+    arr, world, dt = _rows(rows, grad_out.numel())
+    ws_bytes = 0
+    if sumsq_out is not None:
+        _dev(sumsq_out, "sumsq_out", torch.float64)
+    if workspace is not None:
+        _dev(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    L.check("zs_reduce_grads", _lib().zs_reduce_grads(
+        arr, world, dt, grad_out.numel(), _ptr(grad_out), _ptr(sumsq_out), _ptr(workspace),
+        ws_bytes, _stream(stream, grad_out.device)))
+
+
+def _state(master, exp_avg, exp_avg_sq):
+    _dev(master, "master", torch.float32)
+    _dev(exp_avg, "exp_avg", torch.float32)
+    _dev(exp_avg_sq, "exp_avg_sq", torch.float32)
+    n = master.numel()
+    if exp_avg.numel() != n or exp_avg_sq.numel() != n:
+        raise ValueError("master, exp_avg and exp_avg_sq must have the same size")
+    return n
+
+
+def _opt_out(bf16_out, grad_scale, n):
+    if bf16_out is not None:
+        _dev(bf16_out, "bf16_out", torch.bfloat16)
+        if bf16_out.numel() != n:
+            raise ValueError("bf16_out must have the master's size")
+    if grad_scale is not None:
+        _dev(grad_scale, "grad_scale", torch.float32)
+        if grad_scale.numel() != 1:
+            raise ValueError("grad_scale is a single fp32 value")
+
+
+def zs_adamw_step(master, exp_avg, exp_avg_sq, grad, *, lr, beta1, beta2, eps, weight_decay, step,
+                  grad_scale=None, bf16_out=None, stream=None):
+    n = _state(master, exp_avg, exp_avg_sq)
+    _dev(grad, "grad", torch.float32)
+    if grad.numel() != n:
+        raise ValueError("grad must have the master's size")
+    _opt_out(bf16_out, grad_scale, n)
+    hp = _hparams(lr, beta1, beta2, eps, weight_decay, step)
+    L.check("zs_adamw_step", _lib().zs_adamw_step(
+        _ptr(master), _ptr(exp_avg), _ptr(exp_avg_sq), _ptr(grad), n, C.byref(hp),
+        _ptr(grad_scale), _ptr(bf16_out), _stream(stream, master.device)))
+
+
+def zs_cast_for_gather(master, gather_slot, stream=None):
+    _dev(master, "master", torch.float32)
+    _dev(gather_slot, "gather_slot", torch.bfloat16)
+    if gather_slot.numel() != master.numel():
+        raise ValueError("gather_slot must have the master's size")
+    L.check("zs_cast_for_gather", _lib().zs_cast_for_gather(
+        _ptr(master), master.numel(), _ptr(gather_slot), _stream(stream, master.device)))
+
+
+def zs_sharded_step(rows, master, exp_avg, exp_avg_sq, *, lr, beta1, beta2, eps, weight_decay,
+                    step, grad_scale=None, bf16_out=None, stream=None):
+    n = _state(master, exp_avg, exp_avg_sq)
+    arr, world, dt = _rows(rows, n)
+    _opt_out(bf16_out, grad_scale, n)
+    hp = _hparams(lr, beta1, beta2, eps, weight_decay, step)
+    L.check("zs_sharded_step", _lib().zs_sharded_step(
+        arr, world, dt, n, _ptr(master), _ptr(exp_avg), _ptr(exp_avg_sq), C.byref(hp),
+        _ptr(grad_scale), _ptr(bf16_out), _stream(stream, master.device)))
+
+
+def zs_version() -> int:
+    return int(_lib().zs_version())

@@ -1,0 +1,214 @@
+// AdamW on the rank's fp32 master/m/v slice, with the bf16 copy for the
+// all-gather fused into the same pass; and the standalone fp32 -> bf16 cast.
+//
+// Pages: "Lesson 5: ZeRO and FSDP" s3 (ZeRO-1/2 step 2: each rank updates its
+// own 1/N of the fp32 state and master weights locally and converts them to
+// BF16; ZeRO-3 item 4: no communication) and Fig. 5-4 (write back the BF16
+// parameter shard); "Data parallelism and ZeRO memory sharding" s4.2 (the
+// bias-corrected step, eps outside the square root); "FSDP" (Latent Atlas)
+// s8.2 step 6 and s9.3 (hyper-parameters). Decoupled weight decay.
+//
+// HBM-bound: 28 bytes per element (read g, theta, m, v; write theta, m, v),
+// +2 with the fused bf16 store. Lanes move 16-byte vectors of 4 fp32 and
+// 8-byte vectors of 4 bf16 (the bf16 slot of an odd rank can sit on an
+// 8-byte boundary when S is 4 mod 8).
+#include <cmath>
+
+#include "zs_device.hpp"
+#include "zs_launch.hpp"
+
+namespace zs {
+
+AdamConsts adam_consts(const zs_adamw_hparams& hp) {
+  const double t = (double)hp.step;
+  const double bc1 = 1.0 - std::pow(hp.beta1, t);
+  const double bc2 = 1.0 - std::pow(hp.beta2, t);
+  AdamConsts c;
+  c.b1 = (float)hp.beta1;
+  c.omb1 = (float)(1.0 - hp.beta1);
+  c.b2 = (float)hp.beta2;
+  c.omb2 = (float)(1.0 - hp.beta2);
+  c.step_size = (float)(hp.lr / bc1);
+  c.decay = (float)(1.0 - hp.lr * hp.weight_decay);
+  c.inv_sqrt_bc2 = (float)(1.0 / std::sqrt(bc2));
+  c.eps = (float)hp.eps;
+  return c;
+}
+
+namespace {
+
+template <int V, bool CAST, bool SCALE>
+__global__ __launch_bounds__(kThreads) void k_adamw(float* __restrict__ th, float* __restrict__ m,
+                                                    float* __restrict__ v,
+                                                    const float* __restrict__ g, int64_t ngroups,
+                                                    int64_t n, AdamConsts c,
+                                                    const float* __restrict__ scale,
+                                                    uint16_t* __restrict__ out) {
+  const float sc = SCALE ? *scale : 1.0f;
+  const int64_t tile = (int64_t)kThreads * V;
+  for (int64_t base = (int64_t)blockIdx.x * tile; base < ngroups;
+       base += (int64_t)gridDim.x * tile) {
+    int64_t q[V];
+    f32x4 G[V], T[V], M[V], W[V];
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      const int64_t qq = base + threadIdx.x + (int64_t)j * kThreads;
+      q[j] = qq < ngroups ? qq : ngroups - 1;
+      G[j] = ld_nt(reinterpret_cast<const f32x4*>(g) + q[j]);
+      T[j] = ld_nt(reinterpret_cast<const f32x4*>(th) + q[j]);
+      M[j] = ld_nt(reinterpret_cast<const f32x4*>(m) + q[j]);
+      W[j] = ld_nt(reinterpret_cast<const f32x4*>(v) + q[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      if (base + threadIdx.x + (int64_t)j * kThreads >= ngroups) continue;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float tt = T[j][e], mm = M[j][e], vv = W[j][e];
+        const float gg = SCALE ? G[j][e] * sc : G[j][e];
+        adamw_elem(tt, mm, vv, gg, c);
+        T[j][e] = tt;
+        M[j][e] = mm;
+        W[j][e] = vv;
+      }
+      st_nt(T[j], reinterpret_cast<f32x4*>(th) + q[j]);
+      st_nt(M[j], reinterpret_cast<f32x4*>(m) + q[j]);
+      st_nt(W[j], reinterpret_cast<f32x4*>(v) + q[j]);
+      if (CAST) {
+        const u32x2 b{pack_bf16x2(T[j][0], T[j][1]), pack_bf16x2(T[j][2], T[j][3])};
+        st_nt(b, reinterpret_cast<u32x2*>(out) + q[j]);
+      }
+    }
+  }
+  if (blockIdx.x == 0) {  // ragged tail
+    for (int64_t i = ngroups * 4 + threadIdx.x; i < n; i += kThreads) {
+      float tt = th[i], mm = m[i], vv = v[i];
+      const float gg = SCALE ? g[i] * sc : g[i];
+      adamw_elem(tt, mm, vv, gg, c);
+      th[i] = tt;
+      m[i] = mm;
+      v[i] = vv;
+      if (CAST) out[i] = (uint16_t)f32_to_bf16(tt);
+    }
+  }
+}
+
+// Element-wise variant for pointers off the vector grid; identical arithmetic.
+template <bool CAST, bool SCALE>
+__global__ __launch_bounds__(kThreads) void k_adamw_scalar(float* __restrict__ th,
+                                                           float* __restrict__ m,
+                                                           float* __restrict__ v,
+                                                           const float* __restrict__ g, int64_t n,
+                                                           AdamConsts c,
+                                                           const float* __restrict__ scale,
+                                                           uint16_t* __restrict__ out) {
+  const float sc = SCALE ? *scale : 1.0f;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * kThreads) {
+    float tt = th[i], mm = m[i], vv = v[i];
+    const float gg = SCALE ? g[i] * sc : g[i];
+    adamw_elem(tt, mm, vv, gg, c);
+    th[i] = tt;
+    m[i] = mm;
+    v[i] = vv;
+    if (CAST) out[i] = (uint16_t)f32_to_bf16(tt);
+  }
+}
+
+template <int V>
+__global__ __launch_bounds__(kThreads) void k_cast(const float* __restrict__ src, int64_t ngroups,
+                                                   int64_t n, uint16_t* __restrict__ out) {
+  const int64_t tile = (int64_t)kThreads * V;
+  for (int64_t base = (int64_t)blockIdx.x * tile; base < ngroups;
+       base += (int64_t)gridDim.x * tile) {
+    f32x4 x[V];
+    int64_t q[V];
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      const int64_t qq = base + threadIdx.x + (int64_t)j * kThreads;
+      q[j] = qq < ngroups ? qq : ngroups - 1;
+      x[j] = ld_nt(reinterpret_cast<const f32x4*>(src) + q[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      if (base + threadIdx.x + (int64_t)j * kThreads >= ngroups) continue;
+      const u32x2 b{pack_bf16x2(x[j][0], x[j][1]), pack_bf16x2(x[j][2], x[j][3])};
+      st_nt(b, reinterpret_cast<u32x2*>(out) + q[j]);
+    }
+  }
+  if (blockIdx.x == 0)
+    for (int64_t i = ngroups * 4 + threadIdx.x; i < n; i += kThreads)
+      out[i] = (uint16_t)f32_to_bf16(src[i]);
+}
+
+__global__ __launch_bounds__(kThreads) void k_cast_scalar(const float* __restrict__ src, int64_t n,
+                                                          uint16_t* __restrict__ out) {
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * kThreads)
+    out[i] = (uint16_t)f32_to_bf16(src[i]);
+}
+
+bool al(const void* p, unsigned a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int64_t grid_for(int64_t units, int64_t per_block) {
+  int64_t gsz = (units + per_block - 1) / per_block;
+  if (gsz > tuning().grid_cap) gsz = tuning().grid_cap;
+  return gsz < 1 ? 1 : gsz;
+}
+
+template <int V, bool CAST, bool SCALE>
+void run_adamw(float* th, float* m, float* v, const float* g, int64_t n, const AdamConsts& c,
+               const float* scale, uint16_t* out, hipStream_t s) {
+  const int64_t ngroups = n / 4;
+  const int64_t grid = grid_for(ngroups, (int64_t)kThreads * V);
+  hipLaunchKernelGGL((k_adamw<V, CAST, SCALE>), dim3((unsigned)grid), dim3(kThreads), 0, s, th, m,
+                     v, g, ngroups, n, c, scale, out);
+}
+
+template <bool CAST, bool SCALE>
+void pick_v(float* th, float* m, float* v, const float* g, int64_t n, const AdamConsts& c,
+            const float* scale, uint16_t* out, hipStream_t s) {
+  switch (tuning().adamw_v) {
+    case 1: run_adamw<1, CAST, SCALE>(th, m, v, g, n, c, scale, out, s); break;
+    case 4: run_adamw<4, CAST, SCALE>(th, m, v, g, n, c, scale, out, s); break;
+    default: run_adamw<2, CAST, SCALE>(th, m, v, g, n, c, scale, out, s); break;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_adamw(float* th, float* m, float* v, const float* g, int64_t n,
+                        const zs_adamw_hparams& hp, const float* scale, uint16_t* out,
+                        hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const AdamConsts c = adam_consts(hp);
+  const bool vec = al(th, 16) && al(m, 16) && al(v, 16) && al(g, 16) && (!out || al(out, 8));
+  if (vec) {
+    if (out && scale) pick_v<true, true>(th, m, v, g, n, c, scale, out, s);
+    else if (out) pick_v<true, false>(th, m, v, g, n, c, scale, out, s);
+    else if (scale) pick_v<false, true>(th, m, v, g, n, c, scale, out, s);
+    else pick_v<false, false>(th, m, v, g, n, c, scale, out, s);
+  } else {
+    const dim3 gd((unsigned)grid_for(n, 4 * kThreads)), bd(kThreads);
+    if (out && scale) hipLaunchKernelGGL((k_adamw_scalar<true, true>), gd, bd, 0, s, th, m, v, g, n, c, scale, out);
+    else if (out) hipLaunchKernelGGL((k_adamw_scalar<true, false>), gd, bd, 0, s, th, m, v, g, n, c, scale, out);
+    else if (scale) hipLaunchKernelGGL((k_adamw_scalar<false, true>), gd, bd, 0, s, th, m, v, g, n, c, scale, out);
+    else hipLaunchKernelGGL((k_adamw_scalar<false, false>), gd, bd, 0, s, th, m, v, g, n, c, scale, out);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_cast(const float* src, int64_t n, uint16_t* out, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  if (al(src, 16) && al(out, 8)) {
+    const int64_t ngroups = n / 4;
+    const dim3 gd((unsigned)grid_for(ngroups, 2 * kThreads));
+    hipLaunchKernelGGL((k_cast<2>), gd, dim3(kThreads), 0, s, src, ngroups, n, out);
+  } else {
+    const dim3 gd((unsigned)grid_for(n, 4 * kThreads));
+    hipLaunchKernelGGL(k_cast_scalar, gd, dim3(kThreads), 0, s, src, n, out);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace zs

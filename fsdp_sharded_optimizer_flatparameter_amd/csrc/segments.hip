@@ -1,0 +1,203 @@
+// FlatParameter pack (per-parameter tensors -> the rank's fp32 master slice)
+// and unshard copy-out (gathered flat bf16 buffer -> per-parameter tensors).
+//
+// Pages: "Lesson 5: ZeRO and FSDP" s7.1 point 1 (all parameters of a wrapped
+// unit flattened into one 1-D tensor that is split along DP; contiguous slice
+// views of the gathered tensor become the parameters) and point 3 (tail
+// padding when the count does not divide by the world size); "FSDP" (Latent
+// Atlas) s5.1 (even, contiguous split); "03 - FSDP (ZeRO-3)" s1 and s3 (the
+// all-gather result is copied out per parameter).
+//
+// Both kernels walk a contiguous flat range in chunks of kChunk elements, one
+// chunk per workgroup iteration. The workgroup finds the parameters that
+// overlap its chunk by binary search over the parameter offsets (staged in LDS
+// when the table is small), then copies each overlap with 16-byte vectors when
+// source and destination reach 16-byte alignment at the same element, and
+// with lane-contiguous element accesses otherwise (still coalesced: 64 lanes
+// touch 64 consecutive elements). Every access lies inside the parameter's own
+// [0, numel) range, inside [0, total) of the flat buffer, or inside the shard.
+#include "zs_device.hpp"
+#include "zs_launch.hpp"
+
+namespace zs {
+namespace {
+
+constexpr int64_t kChunk = 8192;   // elements per workgroup iteration
+constexpr int kLdsParams = 1024;   // offsets cached in LDS up to this many parameters
+
+// Largest p with off[p] <= f (off ascending, off[0] == 0 <= f).
+__device__ __forceinline__ int find_param(const int64_t* off_lds, const zs_param_desc* desc,
+                                          int nparams, bool use_lds, int64_t f) {
+  int lo = 0, hi = nparams - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    const int64_t o = use_lds ? off_lds[mid] : desc[mid].flat_offset;
+    if (o <= f) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ float widen(float x) { return x; }
+__device__ __forceinline__ float widen(uint16_t h) { return bf16_to_f32(h); }
+
+// 4 source elements -> one fp32 16-byte vector.
+__device__ __forceinline__ f32x4 load4(const float* p) {
+  return ld_nt(reinterpret_cast<const f32x4*>(p));
+}
+__device__ __forceinline__ f32x4 load4(const uint16_t* p) {
+  const u32x2 w = ld_nt(reinterpret_cast<const u32x2*>(p));
+  return f32x4{bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y)};
+}
+
+// Workgroup-cooperative copy of len elements src -> dst (fp32 destination).
+template <typename Src>
+__device__ void seg_to_f32(const Src* __restrict__ src, float* __restrict__ dst, int64_t len) {
+  const uintptr_t da = reinterpret_cast<uintptr_t>(dst);
+  int64_t head = (int64_t)(((16u - (da & 15u)) & 15u) / 4u);
+  if (head > len) head = len;
+  const bool vec = (reinterpret_cast<uintptr_t>(src + head) & (4 * sizeof(Src) - 1)) == 0;
+  if (!vec) {
+    for (int64_t i = threadIdx.x; i < len; i += kThreads) dst[i] = widen(src[i]);
+    return;
+  }
+  for (int64_t i = threadIdx.x; i < head; i += kThreads) dst[i] = widen(src[i]);
+  const int64_t nv = (len - head) / 4;
+  const Src* s = src + head;
+  float* d = dst + head;
+  for (int64_t i = threadIdx.x; i < nv; i += kThreads)
+    st_nt(load4(s + 4 * i), reinterpret_cast<f32x4*>(d + 4 * i));
+  for (int64_t i = head + 4 * nv + threadIdx.x; i < len; i += kThreads) dst[i] = widen(src[i]);
+}
+
+// Workgroup-cooperative copy of len bf16 elements.
+__device__ void seg_bf16(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst,
+                         int64_t len) {
+  const uintptr_t da = reinterpret_cast<uintptr_t>(dst);
+  int64_t head = (int64_t)(((16u - (da & 15u)) & 15u) / 2u);
+  if (head > len) head = len;
+  const bool vec = (reinterpret_cast<uintptr_t>(src + head) & 15u) == 0;
+  if (!vec) {
+    for (int64_t i = threadIdx.x; i < len; i += kThreads) dst[i] = src[i];
+    return;
+  }
+  for (int64_t i = threadIdx.x; i < head; i += kThreads) dst[i] = src[i];
+  const int64_t nv = (len - head) / 8;
+  const u32x4* s = reinterpret_cast<const u32x4*>(src + head);
+  u32x4* d = reinterpret_cast<u32x4*>(dst + head);
+  for (int64_t i = threadIdx.x; i < nv; i += kThreads) st_nt(ld_nt(s + i), d + i);
+  for (int64_t i = head + 8 * nv + threadIdx.x; i < len; i += kThreads) dst[i] = src[i];
+}
+
+__device__ void zero_f32(float* __restrict__ p, int64_t len) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  int64_t head = (int64_t)(((16u - (a & 15u)) & 15u) / 4u);
+  if (head > len) head = len;
+  for (int64_t i = threadIdx.x; i < head; i += kThreads) p[i] = 0.0f;
+  const int64_t nv = (len - head) / 4;
+  f32x4* d = reinterpret_cast<f32x4*>(p + head);
+  for (int64_t i = threadIdx.x; i < nv; i += kThreads) st_nt(f32x4{0.f, 0.f, 0.f, 0.f}, d + i);
+  for (int64_t i = head + 4 * nv + threadIdx.x; i < len; i += kThreads) p[i] = 0.0f;
+}
+
+// Stage parameter offsets in LDS when the table fits.
+__device__ bool stage_offsets(int64_t* off_lds, const zs_param_desc* desc, int nparams) {
+  const bool use = nparams <= kLdsParams;
+  if (use)
+    for (int i = threadIdx.x; i < nparams; i += kThreads) off_lds[i] = desc[i].flat_offset;
+  __syncthreads();
+  return use;
+}
+
+// Flat range [f0, fe) -> inclusive parameter index range, shared through LDS.
+__device__ void chunk_params(const int64_t* off_lds, const zs_param_desc* desc, int nparams,
+                             bool use_lds, int64_t f0, int64_t fe, int* lo, int* hi) {
+  __shared__ int s_lo, s_hi;
+  if (threadIdx.x == 0) s_lo = find_param(off_lds, desc, nparams, use_lds, f0);
+  if (threadIdx.x == 64) s_hi = find_param(off_lds, desc, nparams, use_lds, fe - 1);
+  __syncthreads();
+  *lo = __builtin_amdgcn_readfirstlane(s_lo);
+  *hi = __builtin_amdgcn_readfirstlane(s_hi);
+  __syncthreads();  // s_lo / s_hi are rewritten by the next chunk
+}
+
+template <typename Src>
+__global__ __launch_bounds__(kThreads) void k_pack(const zs_param_desc* __restrict__ desc,
+                                                   int nparams, int64_t total, int64_t flat_begin,
+                                                   int64_t shard, float* __restrict__ master,
+                                                   float* __restrict__ m, float* __restrict__ v) {
+  __shared__ int64_t off_lds[kLdsParams];
+  const bool use_lds = nparams > 0 ? stage_offsets(off_lds, desc, nparams) : false;
+  for (int64_t k0 = (int64_t)blockIdx.x * kChunk; k0 < shard; k0 += (int64_t)gridDim.x * kChunk) {
+    const int64_t k1 = k0 + kChunk < shard ? k0 + kChunk : shard;
+    const int64_t f0 = flat_begin + k0, f1 = flat_begin + k1;
+    const int64_t fe = f1 < total ? f1 : total;  // end of real data inside the chunk
+    if (m) zero_f32(m + k0, k1 - k0);
+    if (v) zero_f32(v + k0, k1 - k0);
+    if (f0 < fe) {
+      int lo, hi;
+      chunk_params(off_lds, desc, nparams, use_lds, f0, fe, &lo, &hi);
+      for (int p = lo; p <= hi; ++p) {
+        const int64_t off = desc[p].flat_offset, cnt = desc[p].numel;
+        const int64_t a = f0 > off ? f0 : off;
+        const int64_t b = fe < off + cnt ? fe : off + cnt;
+        if (a >= b) continue;
+        const Src* src = static_cast<const Src*>(desc[p].ptr) + (a - off);
+        seg_to_f32<Src>(src, master + (a - flat_begin), b - a);
+      }
+    }
+    const int64_t z0 = f0 > total ? f0 : total;  // tail padding -> +0.0
+    if (z0 < f1) zero_f32(master + (z0 - flat_begin), f1 - z0);
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void k_copy_out(const uint16_t* __restrict__ gathered,
+                                                       const zs_param_desc* __restrict__ desc,
+                                                       int nparams, int64_t total) {
+  __shared__ int64_t off_lds[kLdsParams];
+  const bool use_lds = stage_offsets(off_lds, desc, nparams);
+  for (int64_t f0 = (int64_t)blockIdx.x * kChunk; f0 < total; f0 += (int64_t)gridDim.x * kChunk) {
+    const int64_t fe = f0 + kChunk < total ? f0 + kChunk : total;
+    int lo, hi;
+    chunk_params(off_lds, desc, nparams, use_lds, f0, fe, &lo, &hi);
+    for (int p = lo; p <= hi; ++p) {
+      const int64_t off = desc[p].flat_offset, cnt = desc[p].numel;
+      const int64_t a = f0 > off ? f0 : off;
+      const int64_t b = fe < off + cnt ? fe : off + cnt;
+      if (a >= b) continue;
+      seg_bf16(gathered + a, static_cast<uint16_t*>(desc[p].ptr) + (a - off), b - a);
+    }
+  }
+}
+
+int64_t grid_for(int64_t elems) {
+  int64_t gsz = (elems + kChunk - 1) / kChunk;
+  if (gsz > tuning().grid_cap) gsz = tuning().grid_cap;
+  return gsz < 1 ? 1 : gsz;
+}
+
+}  // namespace
+
+hipError_t launch_pack(const zs_param_desc* d_desc, int nparams, int64_t total, int src_dtype,
+                       int64_t flat_begin, int64_t shard, float* master, float* m, float* v,
+                       hipStream_t s) {
+  if (shard == 0) return hipSuccess;
+  const dim3 gd((unsigned)grid_for(shard)), bd(kThreads);
+  if (src_dtype == ZS_BF16)
+    hipLaunchKernelGGL((k_pack<uint16_t>), gd, bd, 0, s, d_desc, nparams, total, flat_begin, shard,
+                       master, m, v);
+  else
+    hipLaunchKernelGGL((k_pack<float>), gd, bd, 0, s, d_desc, nparams, total, flat_begin, shard,
+                       master, m, v);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_out(const uint16_t* gathered, const zs_param_desc* d_desc, int nparams,
+                           int64_t total, hipStream_t s) {
+  if (total == 0 || nparams == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_copy_out, dim3((unsigned)grid_for(total)), dim3(kThreads), 0, s, gathered,
+                     d_desc, nparams, total);
+  return hipGetLastError();
+}
+
+}  // namespace zs

@@ -1,0 +1,149 @@
+// Device-side building blocks shared by the zs kernels (gfx950, wave64).
+//
+// Every kernel of the sharded update is a streaming pass over HBM: each lane
+// moves whole 16-byte vectors (global_load_dwordx4 / global_store_dwordx4),
+// single-use streams carry the nontemporal hint so they do not evict lines
+// that are reused, and arithmetic is plain fp32 VALU work (no MFMA: there is
+// no contraction on this path).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "zs.h"
+
+namespace zs {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kThreads = 256;  // 4 wave64 per workgroup
+
+// ---- streaming memory access -------------------------------------------------
+
+template <typename T>
+__device__ __forceinline__ T ld_nt(const T* p) {
+  return __builtin_nontemporal_load(p);
+}
+template <typename T>
+__device__ __forceinline__ void st_nt(T v, T* p) {
+  __builtin_nontemporal_store(v, p);
+}
+
+// ---- bf16 <-> fp32 -----------------------------------------------------------
+// bf16 is the upper half of an IEEE fp32 pattern; widening is exact.
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// fp32 -> bf16, round to nearest with ties to even, computed on the integer
+// pattern: adding 0x7fff plus the lowest kept bit carries into the kept half
+// exactly when the dropped half is above one half, or equal to it with an odd
+// kept half. NaN keeps its sign and top payload and gets the quiet bit.
+// Overflow carries into the exponent and yields infinity.
+__device__ __forceinline__ uint32_t f32_to_bf16(float x) {
+  const uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// ---- gradient contributions ----------------------------------------------------
+
+// Row pointers travel in the kernel-argument segment: uniform across the grid,
+// they land in SGPRs and every row load is a global_load with a scalar base.
+template <int CAP>
+struct RowTable {
+  const void* p[CAP];
+};
+
+// One 16-byte vector of contributions decoded to fp32: 8 bf16 or 4 fp32 elements.
+template <typename In>
+struct Lanes;
+template <>
+struct Lanes<uint16_t> {
+  static constexpr int E = 8;
+  __device__ __forceinline__ static void decode(const u32x4& w, float* out) {
+    out[0] = bf16_lo(w.x); out[1] = bf16_hi(w.x);
+    out[2] = bf16_lo(w.y); out[3] = bf16_hi(w.y);
+    out[4] = bf16_lo(w.z); out[5] = bf16_hi(w.z);
+    out[6] = bf16_lo(w.w); out[7] = bf16_hi(w.w);
+  }
+  __device__ __forceinline__ static void add(const u32x4& w, float* acc) {
+    acc[0] += bf16_lo(w.x); acc[1] += bf16_hi(w.x);
+    acc[2] += bf16_lo(w.y); acc[3] += bf16_hi(w.y);
+    acc[4] += bf16_lo(w.z); acc[5] += bf16_hi(w.z);
+    acc[6] += bf16_lo(w.w); acc[7] += bf16_hi(w.w);
+  }
+  __device__ __forceinline__ static float scalar(const void* row, int64_t i) {
+    return bf16_to_f32(static_cast<const uint16_t*>(row)[i]);
+  }
+};
+template <>
+struct Lanes<float> {
+  static constexpr int E = 4;
+  __device__ __forceinline__ static void decode(const u32x4& w, float* out) {
+    out[0] = __uint_as_float(w.x); out[1] = __uint_as_float(w.y);
+    out[2] = __uint_as_float(w.z); out[3] = __uint_as_float(w.w);
+  }
+  __device__ __forceinline__ static void add(const u32x4& w, float* acc) {
+    acc[0] += __uint_as_float(w.x); acc[1] += __uint_as_float(w.y);
+    acc[2] += __uint_as_float(w.z); acc[3] += __uint_as_float(w.w);
+  }
+  __device__ __forceinline__ static float scalar(const void* row, int64_t i) {
+    return static_cast<const float*>(row)[i];
+  }
+};
+
+// Division of the rank sum by N. For N a power of two the product with the
+// exact reciprocal is the same correctly rounded value, so both branches give
+// the IEEE quotient.
+struct MeanDiv {
+  float inv;   // 1/N, exact when pow2
+  float n;     // N as fp32
+  int pow2;
+  __device__ __forceinline__ float operator()(float s) const { return pow2 ? s * inv : s / n; }
+};
+
+// ---- AdamW ---------------------------------------------------------------------
+
+// fp32 constants derived on the host (in double) from zs_adamw_hparams.
+struct AdamConsts {
+  float b1, omb1;         // beta1, 1 - beta1
+  float b2, omb2;         // beta2, 1 - beta2
+  float step_size;        // lr / (1 - beta1^t)
+  float decay;            // 1 - lr * weight_decay
+  float inv_sqrt_bc2;     // 1 / sqrt(1 - beta2^t)
+  float eps;
+};
+
+// One element of the decoupled-decay, bias-corrected AdamW step.
+//   m' = b1 m + (1-b1) g,  v' = b2 v + (1-b2) g^2,
+//   theta' = theta (1 - lr wd) - step_size m' / (sqrt(v') / sqrt(1-b2^t) + eps)
+__device__ __forceinline__ void adamw_elem(float& th, float& m, float& v, float g,
+                                           const AdamConsts& c) {
+  m = fmaf(c.b1, m, c.omb1 * g);
+  v = fmaf(c.b2, v, c.omb2 * (g * g));
+  const float denom = fmaf(sqrtf(v), c.inv_sqrt_bc2, c.eps);
+  th = fmaf(th, c.decay, -((c.step_size * m) / denom));
+}
+
+// ---- block reduction of per-thread fp64 partials (fixed order) ------------------
+
+__device__ __forceinline__ double block_sum_fixed(double x, double* lds /* >= kThreads/64 */) {
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) lds[wave] = x;
+  __syncthreads();
+  double s = 0.0;
+  if (threadIdx.x == 0) {
+    for (int w = 0; w < kThreads / 64; ++w) s += lds[w];
+  }
+  return s;  // valid in thread 0
+}
+
+}  // namespace zs

@@ -1,0 +1,50 @@
+// Host-side launchers of the zs kernels (internal to libzs; the public surface is zs.h).
+// Each launcher assumes its arguments were validated by the C-ABI entry point.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "zs.h"
+
+namespace zs {
+
+struct AdamConsts;
+
+// Launch-shape knobs. Defaults are the measured best on MI355X; each can be
+// overridden once per process through the environment (ZS_REDUCE_V,
+// ZS_ADAMW_V, ZS_GRID_CAP) for sweeps. None of them changes any result.
+struct Tuning {
+  int reduce_v;    // 16-byte groups per lane per tile in the reduce / fused kernels (1 or 2)
+  int adamw_v;     // 16-byte groups per lane per tile in AdamW / cast (1, 2 or 4)
+  int64_t grid_cap;  // upper bound on workgroups of the streaming kernels
+};
+const Tuning& tuning();
+
+// Largest number of per-workgroup partial sums a sum-of-squares launch over n
+// elements writes; the workspace holds that many doubles.
+int64_t max_partials(int64_t n);
+
+AdamConsts adam_consts(const zs_adamw_hparams& hp);
+
+hipError_t launch_reduce(const void* const* rows, int world, int dtype, int64_t n, float* g,
+                         double* sumsq, double* partials, hipStream_t s);
+
+hipError_t launch_adamw(float* th, float* m, float* v, const float* g, int64_t n,
+                        const zs_adamw_hparams& hp, const float* scale, uint16_t* out,
+                        hipStream_t s);
+
+hipError_t launch_cast(const float* src, int64_t n, uint16_t* out, hipStream_t s);
+
+hipError_t launch_fused(const void* const* rows, int world, int dtype, int64_t n, float* th,
+                        float* m, float* v, const zs_adamw_hparams& hp, const float* scale,
+                        uint16_t* out, hipStream_t s);
+
+hipError_t launch_pack(const zs_param_desc* d_desc, int nparams, int64_t total, int src_dtype,
+                       int64_t flat_begin, int64_t shard, float* master, float* m, float* v,
+                       hipStream_t s);
+
+hipError_t launch_copy_out(const uint16_t* gathered, const zs_param_desc* d_desc, int nparams,
+                           int64_t total, hipStream_t s);
+
+}  // namespace zs

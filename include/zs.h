@@ -1,0 +1,266 @@
+/*
+ * zs.h -- C ABI of one data-parallel rank's sharded ZeRO/FSDP update on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The update of one rank, in the order the pages give it:
+ *   1. pack     zs_flat_layout + zs_pack_shard: the rank's fp32 slice of a
+ *               FlatParameter (all parameters of a unit laid end to end and
+ *               padded at the tail to a multiple of N).
+ *   2. reduce   zs_reduce_grads: the fp32 mean of N per-rank gradient
+ *               contributions for that slice -- the arithmetic a
+ *               reduce-scatter performs for this rank.
+ *   3. AdamW    zs_adamw_step: the local AdamW update of the fp32 master, m
+ *               and v slice, optionally writing the bf16 result straight
+ *               into the rank's slot of the all-gather buffer.
+ *   4. cast and copy-out
+ *               zs_cast_for_gather: fp32 master -> bf16 slot of the gather
+ *               buffer; zs_copy_out: a gathered flat buffer -> per-parameter
+ *               tensors (the unshard copy-out).
+ *   Fused       zs_sharded_step: steps 2-3 (and the cast) in one pass.
+ *
+ * Pages (title, address) cited below:
+ *   [L5]  "Lesson 5: ZeRO and FSDP", hpc.payai.win/train/lesson05.html
+ *   [ZvF] "ZeRO vs FSDP", muhenan.com/post/zero-vs-fsdp
+ *   [FZ3] "03 - FSDP (ZeRO-3): per-layer all-gather and reshard",
+ *         llm-infra-atlas.github.io/parallel/01_dp/03_fsdp/
+ *   [LAF] "FSDP" (Latent Atlas), process-cxr.github.io/ai-library/training/
+ *         distributed-training/fsdp
+ *   [DPZ] "Data parallelism and ZeRO memory sharding", jefxiong.cn/index.php/
+ *         archives/aigc-fundamentals-zero.html
+ *
+ * Conventions common to every entry point:
+ *   - Ownership: the caller owns every buffer (device data, descriptor tables,
+ *     workspace). The library allocates no memory and keeps no state between
+ *     calls, so calls on different streams are independent.
+ *   - Execution: device work is enqueued on `stream` (NULL = the legacy
+ *     default stream) and is asynchronous; results are valid once the
+ *     stream has completed. No call synchronises.
+ *   - Errors: arguments are checked on the host before anything is enqueued;
+ *     a failed check returns a negative ZS_ERR_* code and enqueues nothing.
+ *     A HIP launch failure returns ZS_ERR_HIP. zs_status_string() names
+ *     every code.
+ *   - Sizes are element counts (int64_t); n == 0 is a valid no-op.
+ *   - bf16 values are passed as uint16_t bit patterns (the top half of an
+ *     IEEE fp32). fp32 -> bf16 is round-to-nearest-even; NaN stays a quiet
+ *     NaN with its sign; overflow goes to infinity.
+ *   - Alignment: any element-aligned pointer is accepted. Pointers on
+ *     16-byte boundaries (8-byte for bf16 outputs) take the vector path;
+ *     others take an element-wise path with the same results.
+ */
+#ifndef ZS_H_
+#define ZS_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t zs_status;
+
+#define ZS_OK 0
+#define ZS_ERR_NULL (-1)      /* a required pointer is NULL                       */
+#define ZS_ERR_SIZE (-2)      /* negative or inconsistent element count           */
+#define ZS_ERR_WORLD (-3)     /* world size outside [1, ZS_MAX_WORLD]             */
+#define ZS_ERR_RANK (-4)      /* rank outside [0, world)                          */
+#define ZS_ERR_DTYPE (-5)     /* dtype code is not ZS_F32 or ZS_BF16              */
+#define ZS_ERR_HPARAM (-6)    /* hyper-parameter not finite / out of range, step<1 */
+#define ZS_ERR_SHARD (-7)     /* shard_numel != ceil(total / world)               */
+#define ZS_ERR_WORKSPACE (-8) /* workspace missing or smaller than required       */
+#define ZS_ERR_LAYOUT (-9)    /* descriptor table does not tile [0, total)        */
+#define ZS_ERR_ALIGN (-10)    /* pointer not aligned to its element size          */
+#define ZS_ERR_OVERLAP (-11)  /* an output buffer overlaps an input it may not     */
+#define ZS_ERR_HIP (-100)     /* a HIP runtime call or kernel launch failed       */
+
+/* Element types of gradient contributions and parameters. */
+#define ZS_F32 0
+#define ZS_BF16 1
+
+/* Largest number of simulated ranks one reduce may combine. */
+#define ZS_MAX_WORLD 256
+
+/*
+ * One parameter of a unit, as laid out in its FlatParameter ([L5] s7.1 point 1;
+ * [ZvF] s3, difference 1; [LAF] s5.1). Tables of these live in DEVICE memory
+ * when passed to zs_pack_shard / zs_copy_out, and in HOST memory when passed
+ * to zs_check_layout.
+ *   ptr          device address of the parameter's contiguous (C-order) storage
+ *   flat_offset  element offset of the parameter inside the flat buffer
+ *   numel        element count of the parameter
+ * A valid table lists the parameters in flat order and tiles [0, total):
+ * flat_offset[0] == 0 and flat_offset[i+1] == flat_offset[i] + numel[i].
+ */
+typedef struct zs_param_desc {
+  void* ptr;
+  int64_t flat_offset;
+  int64_t numel;
+} zs_param_desc;
+
+/*
+ * AdamW hyper-parameters ([LAF] s9.3 lists lr, beta1, beta2, epsilon,
+ * weight_decay). Given in double; the kernels derive fp32 constants from
+ * them on the host. `step` is the 1-based step count t used for bias
+ * correction 1 - beta^t.
+ */
+typedef struct zs_adamw_hparams {
+  double lr;
+  double beta1;
+  double beta2;
+  double eps;
+  double weight_decay;
+  int64_t step;
+} zs_adamw_hparams;
+
+/*
+ * zs_flat_layout -- FlatParameter layout of a unit (host only, no device work).
+ * [L5] s7.1 points 1 and 3; [LAF] s5.1; [DPZ] s4.2 (contiguous split).
+ *   numels[nparams]      element count of each parameter, in registration order
+ *   world                data-parallel world size N (>= 1)
+ *   offsets_out[nparams] receives flat_offset of each parameter (exclusive
+ *                        prefix sum of numels); may be NULL
+ *   total_out            receives T = sum(numels)
+ *   padded_out           receives P = ceil(T / N) * N (tail padding only)
+ *   shard_out            receives S = P / N, the per-rank slice length
+ * All pointers are host pointers. Output pointers other than offsets_out may
+ * be NULL. Errors: ZS_ERR_NULL (numels NULL with nparams > 0), ZS_ERR_SIZE
+ * (nparams < 0, a negative numel, or T overflowing int64), ZS_ERR_WORLD.
+ */
+zs_status zs_flat_layout(const int64_t* numels, int32_t nparams, int32_t world,
+                         int64_t* offsets_out, int64_t* total_out, int64_t* padded_out,
+                         int64_t* shard_out);
+
+/*
+ * zs_check_layout -- verify on the host that a descriptor table (HOST memory)
+ * tiles [0, total) in order and that every non-empty parameter has a non-NULL
+ * pointer. Returns ZS_OK or ZS_ERR_NULL / ZS_ERR_SIZE / ZS_ERR_LAYOUT.
+ * Callers build the device copy of the table from a table that passed.
+ */
+zs_status zs_check_layout(const zs_param_desc* host_desc, int32_t nparams, int64_t total);
+
+/*
+ * zs_pack_shard -- the rank's fp32 master slice of the padded FlatParameter.
+ * [L5] s7.1 points 1 and 3; [LAF] s5.1; [L5] s2 (fp32 master, m, v per rank).
+ *   d_desc[nparams]  DEVICE table describing the unit (see zs_param_desc);
+ *                    parameters hold `src_dtype` elements (ZS_F32 or ZS_BF16)
+ *   total_numel      T of the unit (the table must tile [0, T))
+ *   world, rank      N and r; shard_numel must equal ceil(T / N)
+ *   master[S]        receives flat[r*S + k] for k < S, as fp32 (bf16 sources
+ *                    are widened exactly); positions at or past T are +0.0
+ *   exp_avg[S], exp_avg_sq[S]
+ *                    optional (NULL = untouched); set to +0.0 (fresh Adam state)
+ * Device pointers: d_desc, master, exp_avg, exp_avg_sq and the table's ptrs.
+ * master must not overlap any parameter. Errors: ZS_ERR_NULL, ZS_ERR_SIZE,
+ * ZS_ERR_WORLD, ZS_ERR_RANK, ZS_ERR_DTYPE, ZS_ERR_SHARD, ZS_ERR_HIP.
+ */
+zs_status zs_pack_shard(const zs_param_desc* d_desc, int32_t nparams, int64_t total_numel,
+                        int32_t src_dtype, int32_t world, int32_t rank, int64_t shard_numel,
+                        float* master, float* exp_avg, float* exp_avg_sq, hipStream_t stream);
+
+/*
+ * zs_reduce_grads -- mean of N gradient contributions for this rank's slice.
+ * [DPZ] s3.1 (equations for g_r and g: the mean over ranks equals the
+ * full-batch gradient); [L5] s3 ZeRO-1/2 step 1 (reduce-scatter keeps only
+ * this rank's 1/N); [L5] s7.5 (reduce_dtype = float32).
+ *   rows[world]   HOST array of `world` DEVICE pointers; rows[q] points at
+ *                 contribution q for this slice, n elements of `dtype`
+ *                 (ZS_BF16 or ZS_F32)
+ *   grad_out[n]   DEVICE fp32 output: g[k] = (c_0[k] + c_1[k] + ... ) / N,
+ *                 summed in fp32 in ascending q starting from c_0[k], then
+ *                 one IEEE division by N (bit-identical for any launch shape)
+ *   sumsq_out     optional DEVICE double: receives sum_k g[k]^2 (this
+ *                 shard's partial of a global gradient norm, [DPZ] s6),
+ *                 accumulated in fp64 in a fixed order (deterministic)
+ *   workspace     DEVICE scratch of at least zs_workspace_bytes(n) bytes,
+ *                 required only when sumsq_out != NULL
+ * grad_out may not overlap any row (ZS_ERR_OVERLAP). Errors: ZS_ERR_NULL,
+ * ZS_ERR_SIZE, ZS_ERR_WORLD, ZS_ERR_DTYPE, ZS_ERR_WORKSPACE, ZS_ERR_ALIGN,
+ * ZS_ERR_OVERLAP, ZS_ERR_HIP.
+ */
+zs_status zs_reduce_grads(const void* const* rows, int32_t world, int32_t dtype, int64_t n,
+                          float* grad_out, double* sumsq_out, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace zs_reduce_grads / zs_sharded_step need for a sum of squares over n elements. */
+size_t zs_workspace_bytes(int64_t n);
+
+/*
+ * zs_adamw_step -- AdamW on the rank's fp32 slice, in place.
+ * [L5] s3 (ZeRO-1/2 step 2; ZeRO-3 item 4: local update of the 1/N fp32
+ * state, no communication); [DPZ] s4.2 (bias-corrected first step, eps
+ * outside the root); [LAF] s8.2 step 6. Weight decay is decoupled.
+ * Per element, with t = hp->step:
+ *   m' = b1 m + (1 - b1) g;   v' = b2 v + (1 - b2) g^2
+ *   theta' = theta (1 - lr wd) - (lr / (1 - b1^t)) m' / (sqrt(v' / (1 - b2^t)) + eps)
+ *   master[n], exp_avg[n], exp_avg_sq[n]   DEVICE fp32, updated in place
+ *   grad[n]                                DEVICE fp32 (e.g. zs_reduce_grads' output)
+ *   hp                                     HOST pointer
+ *   grad_scale    optional DEVICE fp32 scalar (NULL = 1): g is multiplied by
+ *                 *grad_scale before the update (e.g. a gradient-clipping
+ *                 coefficient computed on the device from sums of squares)
+ *   bf16_out[n]   optional DEVICE bf16 output (NULL = skip): bf16(theta'),
+ *                 typically the rank's slot of the all-gather buffer
+ * Errors: ZS_ERR_NULL, ZS_ERR_SIZE, ZS_ERR_HPARAM (non-finite values, lr, eps
+ * or wd < 0, betas outside [0, 1), step < 1), ZS_ERR_ALIGN, ZS_ERR_HIP.
+ */
+zs_status zs_adamw_step(float* master, float* exp_avg, float* exp_avg_sq, const float* grad,
+                        int64_t n, const zs_adamw_hparams* hp, const float* grad_scale,
+                        uint16_t* bf16_out, hipStream_t stream);
+
+/*
+ * zs_cast_for_gather -- bf16 copy of the rank's updated fp32 slice into its
+ * slot of the all-gather buffer ([L5] s3 ZeRO-1/2 step 2 and Fig. 5-4: write
+ * back the BF16 parameter shard; the slot of rank r starts at r*S).
+ *   master[n]       DEVICE fp32 input
+ *   gather_slot[n]  DEVICE bf16 output (the caller passes gather + r*S)
+ * Errors: ZS_ERR_NULL, ZS_ERR_SIZE, ZS_ERR_ALIGN, ZS_ERR_HIP.
+ */
+zs_status zs_cast_for_gather(const float* master, int64_t n, uint16_t* gather_slot,
+                             hipStream_t stream);
+
+/*
+ * zs_copy_out -- unshard copy-out: per-parameter tensors from a gathered flat
+ * bf16 buffer ([L5] s7.1 point 1: contiguous slices of the gathered
+ * FlatParameter become each submodule's parameter; [FZ3] s1 and s3: the
+ * all-gather result is copied out before compute).
+ *   gathered[gathered_numel]  DEVICE bf16 flat buffer (P elements; the tail
+ *                             pad is ignored)
+ *   d_desc[nparams]           DEVICE table of destinations (bf16 elements);
+ *                             must tile [0, total_numel)
+ *   total_numel               T of the unit; must be <= gathered_numel
+ * param i receives gathered[flat_offset_i .. flat_offset_i + numel_i).
+ * Destinations may not overlap `gathered` or each other. Errors: ZS_ERR_NULL,
+ * ZS_ERR_SIZE, ZS_ERR_HIP.
+ */
+zs_status zs_copy_out(const uint16_t* gathered, int64_t gathered_numel, const zs_param_desc* d_desc,
+                      int32_t nparams, int64_t total_numel, hipStream_t stream);
+
+/*
+ * zs_sharded_step -- reduce, AdamW and the bf16 cast in one pass over the
+ * slice: the same arithmetic as zs_reduce_grads followed by zs_adamw_step
+ * (bit-identical results), without writing or re-reading the fp32 gradient.
+ *   rows, world, dtype, n      as zs_reduce_grads
+ *   master, exp_avg, exp_avg_sq, hp, bf16_out
+ *                              as zs_adamw_step (bf16_out may be NULL)
+ *   grad_scale    optional DEVICE fp32 scalar (NULL = 1): the mean gradient is
+ *                 multiplied by *grad_scale before the update (a clipping
+ *                 coefficient computed from a prior sum of squares)
+ * Errors: union of the two calls' errors.
+ */
+zs_status zs_sharded_step(const void* const* rows, int32_t world, int32_t dtype, int64_t n,
+                          float* master, float* exp_avg, float* exp_avg_sq,
+                          const zs_adamw_hparams* hp, const float* grad_scale,
+                          uint16_t* bf16_out, hipStream_t stream);
+
+/* Static, NUL-terminated name of a status code ("ZS_OK", "ZS_ERR_NULL", ...). */
+const char* zs_status_string(zs_status status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int32_t zs_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZS_H_ */

@@ -99,3 +99,19 @@ def copy_out(gathered: np.ndarray, shapes):
         raise ValueError("gathered buffer is shorter than the unit")
     return [gathered[off:off + n].reshape(shape).copy()
             for off, n, shape in zip(lay.offsets, sizes, shapes)]
+
+
+def flat_window(fetch, numels, f0: int, f1: int, dtype=np.float32) -> np.ndarray:
+    """flat[f0:f1] of the padded FlatParameter without materialising the whole unit.
+
+    `fetch(i, j0, j1)` returns elements [j0, j1) of parameter i (C order). Each
+    position f is parameter i's element f - off_i for the i whose range holds
+    it, and +0 past the last parameter (the tail pad).
+    """
+    lay = flat_layout(numels, 1)
+    out = np.zeros(max(f1 - f0, 0), dtype=dtype)
+    for i, (off, n) in enumerate(zip(lay.offsets, numels)):
+        a, b = max(f0, off), min(f1, off + int(n))
+        if a < b:
+            out[a - f0:b - f0] = fetch(i, a - off, b - off)
+    return out

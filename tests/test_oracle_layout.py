@@ -149,3 +149,17 @@ def test_contiguous_assignment_matches_illustration():
     for n, w in itertools.product(range(1, 20), range(1, 8)):
         fl = layout.flatten([np.arange(n, dtype=np.float32)], w)
         assert np.array_equal(np.concatenate([layout.shard_of(fl, w, r) for r in range(w)]), fl)
+
+
+def test_flat_window_equals_slices_of_flatten():
+    rng = np.random.default_rng(5)
+    for _ in range(50):
+        numels = rng.integers(0, 30, size=int(rng.integers(1, 8))).tolist()
+        params = [rng.standard_normal(n).astype(np.float32) for n in numels]
+        world = int(rng.integers(1, 9))
+        flat = layout.flatten(params, world, dtype=np.float32)
+        for _ in range(10):
+            f0 = int(rng.integers(0, flat.size + 1))
+            f1 = int(rng.integers(f0, flat.size + 1))
+            win = layout.flat_window(lambda i, a, b: params[i][a:b], numels, f0, f1)
+            assert np.array_equal(win.view(np.uint32), flat[f0:f1].view(np.uint32))
