@@ -33,6 +33,7 @@ zs_status check_rows(const void* const* rows, int32_t world, int32_t dtype, int6
   if (world < 1 || world > ZS_MAX_WORLD) return ZS_ERR_WORLD;
   if (dtype != ZS_F32 && dtype != ZS_BF16) return ZS_ERR_DTYPE;
   if (n < 0) return ZS_ERR_SIZE;
+  if (n == 0) return ZS_OK;  // nothing is read: rows (and their entries) may be NULL
   if (!rows) return ZS_ERR_NULL;
   for (int32_t q = 0; q < world; ++q) {
     if (!rows[q]) return ZS_ERR_NULL;
@@ -153,9 +154,14 @@ zs_status zs_reduce_grads(const void* const* rows, int32_t world, int32_t dtype,
     if (!workspace || workspace_bytes < zs_workspace_bytes(n)) return ZS_ERR_WORKSPACE;
     if (!aligned(workspace, 8)) return ZS_ERR_ALIGN;
   }
+  if (n == 0) {
+    if (!sumsq_out) return ZS_OK;
+    // an empty shard's sum of squares is 0; written by the finalize kernel
+    return hip_status(zs::launch_reduce(rows, world, dtype, 0, grad_out, sumsq_out,
+                                        static_cast<double*>(workspace), stream));
+  }
   for (int32_t q = 0; q < world; ++q)
     if (overlaps(grad_out, n * 4, rows[q], n * elem_size(dtype))) return ZS_ERR_OVERLAP;
-  if (n == 0 && !sumsq_out) return ZS_OK;
   return hip_status(zs::launch_reduce(rows, world, dtype, n, grad_out, sumsq_out,
                                       static_cast<double*>(workspace), stream));
 }

@@ -165,7 +165,7 @@ zs_status zs_pack_shard(const zs_param_desc* d_desc, int32_t nparams, int64_t to
  * this rank's 1/N); [L5] s7.5 (reduce_dtype = float32).
  *   rows[world]   HOST array of `world` DEVICE pointers; rows[q] points at
  *                 contribution q for this slice, n elements of `dtype`
- *                 (ZS_BF16 or ZS_F32)
+ *                 (ZS_BF16 or ZS_F32); unused (may be NULL) when n == 0
  *   grad_out[n]   DEVICE fp32 output: g[k] = (c_0[k] + c_1[k] + ... ) / N,
  *                 summed in fp32 in ascending q starting from c_0[k], then
  *                 one IEEE division by N (bit-identical for any launch shape)

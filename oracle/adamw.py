@@ -75,15 +75,21 @@ def adamw_step(theta, m, v, g, step: int, hp: HParams, state_dtype=np.float32):
 def error_scales(theta, m, g, step: int, hp: HParams, m1, v1):
     """Per-element magnitudes the update's rounding errors scale with.
 
-    m': b1|m| + (1-b1)|g|;  v': |v'|;  theta': |theta|(1 - lr wd) + lr |m_hat| / (sqrt(v_hat) + eps).
-    A relative tolerance applied to these stays meaningful under cancellation.
+    m':     b1|m| + (1-b1)|g|           (the two terms summed, not their sum)
+    v':     |v'|                         (both terms are non-negative)
+    theta': |theta|(1 - lr wd) + lr (b1|m| + (1-b1)|g|) / (1 - b1^t) / (sqrt(v_hat) + eps)
+            -- the decayed weight plus the step computed from the m'-term
+            scale, since an fp32 m' carries an error proportional to its
+            terms, which the step passes on even when m' itself cancels.
+    A relative tolerance applied to these stays meaningful under cancellation
+    and reduces to a plain relative error where none occurs.
     """
     th = np.abs(np.asarray(theta, dtype=np.float64))
     bc1 = 1.0 - hp.beta1 ** step
     bc2 = 1.0 - hp.beta2 ** step
     sm = hp.beta1 * np.abs(np.asarray(m, np.float64)) + (1 - hp.beta1) * np.abs(np.asarray(g, np.float64))
     sv = np.abs(np.asarray(v1, np.float64))
-    m_hat = np.abs(np.asarray(m1, np.float64)) / bc1
+    m_hat_scale = np.maximum(sm, np.abs(np.asarray(m1, np.float64))) / bc1
     v_hat = np.asarray(v1, np.float64) / bc2
-    st = th * (1.0 - hp.lr * hp.weight_decay) + hp.lr * m_hat / (np.sqrt(v_hat) + hp.eps)
+    st = th * (1.0 - hp.lr * hp.weight_decay) + hp.lr * m_hat_scale / (np.sqrt(v_hat) + hp.eps)
     return st, sm, sv

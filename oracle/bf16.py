@@ -57,3 +57,12 @@ def ulp_distance(a_bits, b_bits) -> np.ndarray:
         return np.where(b & 0x8000, -mag, mag)
 
     return np.abs(line(a_bits) - line(b_bits))
+
+
+def ulp(x) -> np.ndarray:
+    """Spacing of bf16 values at |x| (8 significant bits): 2^(e-7) for a normal
+    |x| in [2^e, 2^(e+1)), and 2^-133 (the subnormal spacing) below 2^-126."""
+    a = np.abs(np.asarray(x, dtype=np.float64))
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.maximum(e, -126.0)
+    return np.where(a >= 2.0 ** -126, 2.0 ** (e - 7), 2.0 ** -133)

@@ -71,3 +71,12 @@ def test_ulp_distance():
     a = np.array([0x3F80, 0x3F80, 0x0000, 0x8001, 0x7F7F], dtype=np.uint16)
     c = np.array([0x3F81, 0x3F7F, 0x8000, 0x0001, 0x7F80], dtype=np.uint16)
     assert bf16.ulp_distance(a, c).tolist() == [1, 1, 0, 2, 1]
+
+
+def test_ulp_spacing():
+    assert bf16.ulp(np.array([1.0, 1.5, 1.99, 2.0, -3.0, 0.0, 2.0 ** -130])).tolist() == [
+        2.0 ** -7, 2.0 ** -7, 2.0 ** -7, 2.0 ** -6, 2.0 ** -6, 2.0 ** -133, 2.0 ** -133]
+    # adjacent bf16 values differ by exactly ulp
+    b = np.arange(0x0080, 0x7F00, 37, dtype=np.uint16)
+    lo, hi = bf16.from_bf16_bits(b).astype(np.float64), bf16.from_bf16_bits(b + 1).astype(np.float64)
+    assert np.array_equal(hi - lo, bf16.ulp(lo))
