@@ -6,6 +6,7 @@
 // results are bit-identical to the two-call path; only the fp32 gradient's
 // round trip through HBM (8 bytes per element) disappears:
 //   bytes per element = 2N (bf16 rows) + 12 (read theta, m, v) + 12 (write) + 2.
+// Lanes own groups of 4 consecutive elements, lane-contiguous in every stream.
 // Pages: "Lesson 5: ZeRO and FSDP" s3 (ZeRO-1/2 steps 1-2, reduce-scatter
 // result -> local update -> BF16), "Data parallelism and ZeRO memory
 // sharding" s3.1 and s4.2.
@@ -15,8 +16,6 @@
 namespace zs {
 namespace {
 
-constexpr int kRankChunk = 8;
-
 MeanDiv mean_div(int world) {
   MeanDiv d;
   d.n = (float)world;
@@ -25,71 +24,64 @@ MeanDiv mean_div(int world) {
   return d;
 }
 
-template <int NW, int CAP, typename In, bool CAST, bool SCALE>
+// Two phases per workgroup over G groups per lane (G*1024 consecutive elements):
+//   1. the rank walk only -- the mean gradient of each group is parked in LDS;
+//   2. AdamW over the fp32 state of the same groups, each lane reading back its
+//      own LDS entries (no barrier), the state read and written as 16-byte
+//      vectors per group.
+// Keeping the row streams and the state read-modify-write apart in time, and
+// the LDS reservation (which caps the workgroups resident per CU), keeps fewer
+// DRAM pages open at once; both were measured to raise HBM throughput.
+template <int NW, int CAP, int G, int C, typename In, bool CAST, bool SCALE>
 __global__ __launch_bounds__(kThreads) void k_fused(RowTable<CAP> rows, int world, MeanDiv div,
                                                     int64_t ngroups, int64_t n,
                                                     float* __restrict__ th, float* __restrict__ m,
                                                     float* __restrict__ v, AdamConsts c,
                                                     const float* __restrict__ scale,
                                                     uint16_t* __restrict__ out) {
+  extern __shared__ f32x4 gl[];  // G * kThreads mean-gradient groups (plus any occupancy pad)
   using L = Lanes<In>;
-  constexpr int E = L::E;
-  constexpr int H = E / 4;  // fp32 16-byte vectors per group
   const int nw = NW > 0 ? NW : world;
   const float sc = SCALE ? *scale : 1.0f;
+  const int64_t span = (int64_t)kThreads * G;
 
-  for (int64_t base = (int64_t)blockIdx.x * kThreads; base < ngroups;
-       base += (int64_t)gridDim.x * kThreads) {
-    const int64_t qq = base + threadIdx.x;
-    const int64_t q = qq < ngroups ? qq : ngroups - 1;
-
-    // optimizer state first, so its loads are in flight during the rank sum
-    f32x4 T[H], M[H], W[H];
+  for (int64_t base = (int64_t)blockIdx.x * span; base < ngroups; base += (int64_t)gridDim.x * span) {
+    for (int k = 0; k < G; ++k) {
+      const int64_t qq = base + k * kThreads + threadIdx.x;
+      const int64_t q = qq < ngroups ? qq : ngroups - 1;  // clamped: loads stay in bounds
+      float acc[1][4];
+      rank_sum<In, C, 1, CAP>(rows, nw, &q, acc);
+      f32x4 gv;
 #pragma unroll
-    for (int h = 0; h < H; ++h) {
-      T[h] = ld_nt(reinterpret_cast<const f32x4*>(th) + q * H + h);
-      M[h] = ld_nt(reinterpret_cast<const f32x4*>(m) + q * H + h);
-      W[h] = ld_nt(reinterpret_cast<const f32x4*>(v) + q * H + h);
+      for (int e = 0; e < 4; ++e) gv[e] = SCALE ? div(acc[0][e]) * sc : div(acc[0][e]);
+      gl[k * kThreads + threadIdx.x] = gv;
     }
-
-    float acc[E];
-    L::decode(ld_nt(static_cast<const u32x4*>(rows.p[0]) + q), acc);
-#pragma unroll 1
-    for (int r0 = 1; r0 < nw; r0 += kRankChunk) {
-      u32x4 buf[kRankChunk];
-#pragma unroll
-      for (int u = 0; u < kRankChunk; ++u)
-        if (r0 + u < nw) buf[u] = ld_nt(static_cast<const u32x4*>(rows.p[r0 + u]) + q);
-#pragma unroll
-      for (int u = 0; u < kRankChunk; ++u)
-        if (r0 + u < nw) L::add(buf[u], acc);
-    }
-    if (qq >= ngroups) continue;
-#pragma unroll
-    for (int h = 0; h < H; ++h) {
+    for (int k = 0; k < G; ++k) {
+      const int64_t qq = base + k * kThreads + threadIdx.x;
+      if (qq >= ngroups) break;
+      f32x4 T = ld_nt(reinterpret_cast<const f32x4*>(th) + qq);
+      f32x4 M = ld_nt(reinterpret_cast<const f32x4*>(m) + qq);
+      f32x4 W = ld_nt(reinterpret_cast<const f32x4*>(v) + qq);
+      const f32x4 gv = gl[k * kThreads + threadIdx.x];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        float gg = div(acc[4 * h + e]);
-        if (SCALE) gg *= sc;
-        float tt = T[h][e], mm = M[h][e], vv = W[h][e];
-        adamw_elem(tt, mm, vv, gg, c);
-        T[h][e] = tt;
-        M[h][e] = mm;
-        W[h][e] = vv;
+        float tt = T[e], mm = M[e], vv = W[e];
+        adamw_elem(tt, mm, vv, gv[e], c);
+        T[e] = tt;
+        M[e] = mm;
+        W[e] = vv;
       }
-      st_nt(T[h], reinterpret_cast<f32x4*>(th) + q * H + h);
-      st_nt(M[h], reinterpret_cast<f32x4*>(m) + q * H + h);
-      st_nt(W[h], reinterpret_cast<f32x4*>(v) + q * H + h);
-      if (CAST) {
-        const u32x2 b{pack_bf16x2(T[h][0], T[h][1]), pack_bf16x2(T[h][2], T[h][3])};
-        st_nt(b, reinterpret_cast<u32x2*>(out) + q * H + h);
-      }
+      st_nt(T, reinterpret_cast<f32x4*>(th) + qq);
+      st_nt(M, reinterpret_cast<f32x4*>(m) + qq);
+      st_nt(W, reinterpret_cast<f32x4*>(v) + qq);
+      if (CAST)
+        st_nt(u32x2{pack_bf16x2(T[0], T[1]), pack_bf16x2(T[2], T[3])}, reinterpret_cast<u32x2*>(out) + qq);
     }
   }
-  if (blockIdx.x == 0) {  // ragged tail
-    for (int64_t i = ngroups * E + threadIdx.x; i < n; i += kThreads) {
-      float s = L::scalar(rows.p[0], i);
-      for (int r = 1; r < nw; ++r) s += L::scalar(rows.p[r], i);
+  if (blockIdx.x == 0) {  // ragged tail (fewer than 4 elements)
+    for (int64_t i = ngroups * 4 + threadIdx.x; i < n; i += kThreads) {
+      float s = -0.0f;
+      for (int r = 0; r < nw; ++r) s += L::scalar(rows.p[r], i);
       float gg = div(s);
       if (SCALE) gg *= sc;
       float tt = th[i], mm = m[i], vv = v[i];
@@ -114,8 +106,8 @@ __global__ __launch_bounds__(kThreads) void k_fused_scalar(RowTable<ZS_MAX_WORLD
   const float sc = SCALE ? *scale : 1.0f;
   for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n;
        i += (int64_t)gridDim.x * kThreads) {
-    float s = L::scalar(rows.p[0], i);
-    for (int r = 1; r < world; ++r) s += L::scalar(rows.p[r], i);
+    float s = -0.0f;
+    for (int r = 0; r < world; ++r) s += L::scalar(rows.p[r], i);
     float gg = div(s);
     if (SCALE) gg *= sc;
     float tt = th[i], mm = m[i], vv = v[i];
@@ -133,38 +125,77 @@ int64_t grid_for(int64_t units, int64_t per_block) {
   return gsz < 1 ? 1 : gsz;
 }
 
-template <int NW, int CAP, typename In>
+
+struct Shape {
+  int g;       // groups per lane staged in LDS
+  size_t lds;  // dynamic LDS bytes per workgroup (>= g * kThreads * 16)
+};
+
+// Measured on MI355X: with many contributions the row walk dominates and deep
+// staging (16 groups in 64 KiB) is best; with few contributions the state
+// read-modify-write dominates and shallow staging (4 groups) under the same
+// 64 KiB reservation (2 workgroups per CU) is best.
+Shape fused_shape(int world) {
+  Shape sh;
+  sh.g = tuning().fused_g > 0 ? tuning().fused_g : (world >= 16 ? 16 : 4);
+  const size_t need = (size_t)sh.g * kThreads * 16;
+  sh.lds = tuning().fused_lds > 0 ? (size_t)tuning().fused_lds : 65536;
+  if (sh.lds < need) sh.lds = need;
+  return sh;
+}
+
+template <int NW, int CAP, int G, int C, typename In>
 void run_fused(const void* const* rows, int world, int64_t n, float* th, float* m, float* v,
-               const AdamConsts& c, const float* scale, uint16_t* out, hipStream_t s) {
+               const AdamConsts& c, const float* scale, uint16_t* out, size_t lds, hipStream_t s) {
   RowTable<CAP> t;
   for (int i = 0; i < CAP; ++i) t.p[i] = i < world ? rows[i] : nullptr;
-  const int64_t ngroups = n / Lanes<In>::E;
-  const dim3 gd((unsigned)grid_for(ngroups, kThreads)), bd(kThreads);
+  const int64_t ngroups = n / 4;
+  const dim3 gd((unsigned)grid_for(ngroups, (int64_t)kThreads * G)), bd(kThreads);
   const MeanDiv d = mean_div(world);
   if (out && scale)
-    hipLaunchKernelGGL((k_fused<NW, CAP, In, true, true>), gd, bd, 0, s, t, world, d, ngroups, n, th, m, v, c, scale, out);
+    hipLaunchKernelGGL((k_fused<NW, CAP, G, C, In, true, true>), gd, bd, lds, s, t, world, d, ngroups, n, th, m, v, c, scale, out);
   else if (out)
-    hipLaunchKernelGGL((k_fused<NW, CAP, In, true, false>), gd, bd, 0, s, t, world, d, ngroups, n, th, m, v, c, scale, out);
+    hipLaunchKernelGGL((k_fused<NW, CAP, G, C, In, true, false>), gd, bd, lds, s, t, world, d, ngroups, n, th, m, v, c, scale, out);
   else if (scale)
-    hipLaunchKernelGGL((k_fused<NW, CAP, In, false, true>), gd, bd, 0, s, t, world, d, ngroups, n, th, m, v, c, scale, out);
+    hipLaunchKernelGGL((k_fused<NW, CAP, G, C, In, false, true>), gd, bd, lds, s, t, world, d, ngroups, n, th, m, v, c, scale, out);
   else
-    hipLaunchKernelGGL((k_fused<NW, CAP, In, false, false>), gd, bd, 0, s, t, world, d, ngroups, n, th, m, v, c, scale, out);
+    hipLaunchKernelGGL((k_fused<NW, CAP, G, C, In, false, false>), gd, bd, lds, s, t, world, d, ngroups, n, th, m, v, c, scale, out);
+}
+
+template <typename In, int G, int C>
+void dispatch_world(const void* const* rows, int world, int64_t n, float* th, float* m, float* v,
+                    const AdamConsts& c, const float* scale, uint16_t* out, size_t lds, hipStream_t s) {
+  switch (world) {
+    case 2: run_fused<2, 2, G, C, In>(rows, world, n, th, m, v, c, scale, out, lds, s); break;
+    case 4: run_fused<4, 4, G, C, In>(rows, world, n, th, m, v, c, scale, out, lds, s); break;
+    case 8: run_fused<8, 8, G, C, In>(rows, world, n, th, m, v, c, scale, out, lds, s); break;
+    case 16: run_fused<16, 16, G, C, In>(rows, world, n, th, m, v, c, scale, out, lds, s); break;
+    case 32: run_fused<32, 32, G, C, In>(rows, world, n, th, m, v, c, scale, out, lds, s); break;
+    case 64: run_fused<64, 64, G, C, In>(rows, world, n, th, m, v, c, scale, out, lds, s); break;
+    default:
+      if (world <= 64) run_fused<0, 64, G, C, In>(rows, world, n, th, m, v, c, scale, out, lds, s);
+      else run_fused<0, ZS_MAX_WORLD, G, C, In>(rows, world, n, th, m, v, c, scale, out, lds, s);
+  }
+}
+
+template <typename In, int C>
+void dispatch_g(int g, const void* const* rows, int world, int64_t n, float* th, float* m, float* v,
+                const AdamConsts& c, const float* scale, uint16_t* out, size_t lds, hipStream_t s) {
+  switch (g) {
+    case 1: dispatch_world<In, 1, C>(rows, world, n, th, m, v, c, scale, out, lds, s); break;
+    case 2: dispatch_world<In, 2, C>(rows, world, n, th, m, v, c, scale, out, lds, s); break;
+    case 8: dispatch_world<In, 8, C>(rows, world, n, th, m, v, c, scale, out, lds, s); break;
+    case 16: dispatch_world<In, 16, C>(rows, world, n, th, m, v, c, scale, out, lds, s); break;
+    default: dispatch_world<In, 4, C>(rows, world, n, th, m, v, c, scale, out, lds, s); break;
+  }
 }
 
 template <typename In>
 void dispatch(const void* const* rows, int world, int64_t n, float* th, float* m, float* v,
               const AdamConsts& c, const float* scale, uint16_t* out, hipStream_t s) {
-  switch (world) {
-    case 2: run_fused<2, 2, In>(rows, world, n, th, m, v, c, scale, out, s); break;
-    case 4: run_fused<4, 4, In>(rows, world, n, th, m, v, c, scale, out, s); break;
-    case 8: run_fused<8, 8, In>(rows, world, n, th, m, v, c, scale, out, s); break;
-    case 16: run_fused<16, 16, In>(rows, world, n, th, m, v, c, scale, out, s); break;
-    case 32: run_fused<32, 32, In>(rows, world, n, th, m, v, c, scale, out, s); break;
-    case 64: run_fused<64, 64, In>(rows, world, n, th, m, v, c, scale, out, s); break;
-    default:
-      if (world <= 64) run_fused<0, 64, In>(rows, world, n, th, m, v, c, scale, out, s);
-      else run_fused<0, ZS_MAX_WORLD, In>(rows, world, n, th, m, v, c, scale, out, s);
-  }
+  const Shape sh = fused_shape(world);
+  if (tuning().rank_chunk == 4) dispatch_g<In, 4>(sh.g, rows, world, n, th, m, v, c, scale, out, sh.lds, s);
+  else dispatch_g<In, 8>(sh.g, rows, world, n, th, m, v, c, scale, out, sh.lds, s);
 }
 
 bool al(const void* p, unsigned a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -177,7 +208,7 @@ hipError_t launch_fused(const void* const* rows, int world, int dtype, int64_t n
   if (n == 0) return hipSuccess;
   const AdamConsts c = adam_consts(hp);
   bool vec = al(th, 16) && al(m, 16) && al(v, 16) && (!out || al(out, 8));
-  for (int i = 0; i < world; ++i) vec = vec && al(rows[i], 16);
+  for (int i = 0; i < world; ++i) vec = vec && al(rows[i], dtype == ZS_BF16 ? 8 : 16);
   if (vec) {
     if (dtype == ZS_BF16) dispatch<uint16_t>(rows, world, n, th, m, v, c, scale, out, s);
     else dispatch<float>(rows, world, n, th, m, v, c, scale, out, s);

@@ -9,11 +9,14 @@
 // norm needs every shard's partial).
 //
 // Design (HBM-bound, 2N+4 bytes per element for bf16 contributions):
-//   * each lane owns V 16-byte groups (8 bf16 or 4 fp32 elements each);
+//   * each lane owns groups of 4 consecutive elements, lane-contiguous in
+//     every stream (8-byte bf16 / 16-byte fp32 row loads, 16-byte g stores);
+//   * with many contributions, a workgroup parks 16 groups per lane in LDS and
+//     writes them as one burst after the rank walk;
 //   * row pointers sit in the kernel-argument segment (SGPR bases);
-//   * ranks are walked in chunks of 8: the chunk's loads are all issued before
-//     its adds, so 8*V independent 16-byte loads are in flight per lane while
-//     the fp32 sum still runs in ascending rank order starting from rank 0;
+//   * ranks are walked in double-buffered chunks of C: a chunk's loads are in
+//     flight while the previous chunk is added, and the fp32 sum still runs
+//     in ascending rank order;
 //   * one IEEE division by N (a multiply by the exact reciprocal when N is a
 //     power of two), so the result is independent of the launch shape;
 //   * rows are read with the nontemporal hint (each byte is used once).
@@ -26,12 +29,21 @@ namespace zs {
 
 const Tuning& tuning() {
   static const Tuning t = [] {
-    Tuning x{0, 0, 0};
+    Tuning x{0, 0, 0, 0, 0, 0, 0};
     const char* e;
-    x.reduce_v = (e = std::getenv("ZS_REDUCE_V")) ? std::atoi(e) : 0;
-    if (x.reduce_v != 1 && x.reduce_v != 2) x.reduce_v = 0;  // 0 = pick by world size
-    x.adamw_v = (e = std::getenv("ZS_ADAMW_V")) ? std::atoi(e) : 2;
-    if (x.adamw_v != 1 && x.adamw_v != 2 && x.adamw_v != 4) x.adamw_v = 2;
+    x.adamw_v = (e = std::getenv("ZS_ADAMW_V")) ? std::atoi(e) : 1;
+    if (x.adamw_v != 1 && x.adamw_v != 2 && x.adamw_v != 4) x.adamw_v = 1;
+    // a 32 KiB reservation (4 workgroups per CU) measured best for AdamW and the cast
+    x.adamw_lds = (e = std::getenv("ZS_ADAMW_LDS")) ? std::atoll(e) : 32768;
+    if (x.adamw_lds < 0 || x.adamw_lds > 65536) x.adamw_lds = 32768;
+    x.rank_chunk = (e = std::getenv("ZS_RANK_CHUNK")) ? std::atoi(e) : 8;
+    if (x.rank_chunk != 4 && x.rank_chunk != 8) x.rank_chunk = 8;
+    x.fused_g = (e = std::getenv("ZS_FUSED_G")) ? std::atoi(e) : 0;
+    if (x.fused_g != 1 && x.fused_g != 2 && x.fused_g != 4 && x.fused_g != 8 && x.fused_g != 16) x.fused_g = 0;
+    x.fused_lds = (e = std::getenv("ZS_FUSED_LDS")) ? std::atoll(e) : 0;
+    if (x.fused_lds < 0 || x.fused_lds > 65536) x.fused_lds = 0;
+    x.reduce_g = (e = std::getenv("ZS_REDUCE_G")) ? std::atoi(e) : 0;
+    if (x.reduce_g != 1 && x.reduce_g != 4 && x.reduce_g != 16) x.reduce_g = 0;
     x.grid_cap = (e = std::getenv("ZS_GRID_CAP")) ? std::atoll(e) : 0;
     // gridDim.x * blockDim.x must stay below 2^32; grid-stride loops cover the rest
     const int64_t kHardCap = int64_t(1) << 22;
@@ -50,6 +62,7 @@ int64_t max_partials(int64_t n) {
 
 namespace {
 
+// ranks per load chunk of the double-buffered rank walk
 constexpr int kRankChunk = 8;
 
 MeanDiv mean_div(int world) {
@@ -60,73 +73,53 @@ MeanDiv mean_div(int world) {
   return d;
 }
 
-template <int NW, int CAP, int V, typename In, bool SUMSQ>
+// G groups per lane: with G > 1 the lane's mean-gradient groups are parked in
+// LDS during the rank walk and written out afterwards as one burst of
+// nontemporal 16-byte stores (the LDS reservation also caps the workgroups
+// resident per CU); with G == 1 each group is stored as soon as it is summed.
+template <int NW, int CAP, int G, int C, typename In, bool SUMSQ>
 __global__ __launch_bounds__(kThreads) void k_reduce(RowTable<CAP> rows, int world, MeanDiv div,
                                                      int64_t ngroups, int64_t n,
                                                      float* __restrict__ g,
                                                      double* __restrict__ partials) {
+  extern __shared__ f32x4 gl[];  // G * kThreads groups when G > 1
   using L = Lanes<In>;
-  constexpr int E = L::E;
   const int nw = NW > 0 ? NW : world;
-  const int64_t tile = (int64_t)kThreads * V;
+  const int64_t span = (int64_t)kThreads * G;
   double ss = 0.0;
 
-  for (int64_t base = (int64_t)blockIdx.x * tile; base < ngroups;
-       base += (int64_t)gridDim.x * tile) {
-    int64_t q[V];
+  for (int64_t base = (int64_t)blockIdx.x * span; base < ngroups; base += (int64_t)gridDim.x * span) {
+    for (int k = 0; k < G; ++k) {
+      const int64_t qq = base + k * kThreads + threadIdx.x;
+      const int64_t q = qq < ngroups ? qq : ngroups - 1;  // clamped: loads stay in bounds
+      float acc[1][4];
+      rank_sum<In, C, 1, CAP>(rows, nw, &q, acc);
+      f32x4 o;
 #pragma unroll
-    for (int j = 0; j < V; ++j) {
-      const int64_t qq = base + threadIdx.x + (int64_t)j * kThreads;
-      q[j] = qq < ngroups ? qq : ngroups - 1;  // clamped: loads stay in bounds, stores skipped
-    }
-    float acc[V][E];
-#pragma unroll
-    for (int j = 0; j < V; ++j)
-      L::decode(ld_nt(static_cast<const u32x4*>(rows.p[0]) + q[j]), acc[j]);
-
-    // one chunk of ranks at a time: bounds the registers held by loads in flight
-#pragma unroll 1
-    for (int r0 = 1; r0 < nw; r0 += kRankChunk) {
-      u32x4 buf[kRankChunk][V];
-#pragma unroll
-      for (int u = 0; u < kRankChunk; ++u) {
-        if (r0 + u < nw) {
-          const u32x4* row = static_cast<const u32x4*>(rows.p[r0 + u]);
-#pragma unroll
-          for (int j = 0; j < V; ++j) buf[u][j] = ld_nt(row + q[j]);
-        }
+      for (int e = 0; e < 4; ++e) {
+        o[e] = div(acc[0][e]);
+        if (SUMSQ && qq < ngroups) ss = fma((double)o[e], (double)o[e], ss);
       }
-#pragma unroll
-      for (int u = 0; u < kRankChunk; ++u) {
-        if (r0 + u < nw) {
-#pragma unroll
-          for (int j = 0; j < V; ++j) L::add(buf[u][j], acc[j]);
-        }
+      if (G == 1) {
+        if (qq < ngroups) st_nt(o, reinterpret_cast<f32x4*>(g) + qq);
+      } else {
+        gl[k * kThreads + threadIdx.x] = o;
       }
     }
-
-#pragma unroll
-    for (int j = 0; j < V; ++j) {
-      if (base + threadIdx.x + (int64_t)j * kThreads < ngroups) {
-        float o[E];
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          o[e] = div(acc[j][e]);
-          if (SUMSQ) ss = fma((double)o[e], (double)o[e], ss);
-        }
-        f32x4* dst = reinterpret_cast<f32x4*>(g) + q[j] * (E / 4);
-#pragma unroll
-        for (int h = 0; h < E / 4; ++h)
-          dst[h] = f32x4{o[4 * h], o[4 * h + 1], o[4 * h + 2], o[4 * h + 3]};
+    if (G > 1) {
+      for (int k = 0; k < G; ++k) {  // each lane writes back only its own entries
+        const int64_t qq = base + k * kThreads + threadIdx.x;
+        if (qq >= ngroups) break;
+        st_nt(gl[k * kThreads + threadIdx.x], reinterpret_cast<f32x4*>(g) + qq);
       }
     }
   }
 
-  // ragged tail (fewer than E elements), same order of operations
+  // ragged tail (fewer than 4 elements), same order of operations
   if (blockIdx.x == 0) {
-    for (int64_t i = ngroups * E + threadIdx.x; i < n; i += kThreads) {
-      float s = L::scalar(rows.p[0], i);
-      for (int r = 1; r < nw; ++r) s += L::scalar(rows.p[r], i);
+    for (int64_t i = ngroups * 4 + threadIdx.x; i < n; i += kThreads) {
+      float s = -0.0f;
+      for (int r = 0; r < nw; ++r) s += L::scalar(rows.p[r], i);
       s = div(s);
       g[i] = s;
       if (SUMSQ) ss = fma((double)s, (double)s, ss);
@@ -150,8 +143,8 @@ __global__ __launch_bounds__(kThreads) void k_reduce_scalar(RowTable<ZS_MAX_WORL
   double ss = 0.0;
   for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n;
        i += (int64_t)gridDim.x * kThreads) {
-    float s = L::scalar(rows.p[0], i);
-    for (int r = 1; r < world; ++r) s += L::scalar(rows.p[r], i);
+    float s = -0.0f;
+    for (int r = 0; r < world; ++r) s += L::scalar(rows.p[r], i);
     s = div(s);
     g[i] = s;
     if (SUMSQ) ss = fma((double)s, (double)s, ss);
@@ -174,41 +167,61 @@ __global__ __launch_bounds__(kThreads) void k_sumsq_finalize(const double* __res
   if (threadIdx.x == 0) *out = b;
 }
 
-template <int NW, int CAP, int V, typename In>
+template <int NW, int CAP, int G, int C, typename In>
 hipError_t run_vec(const void* const* rows, int world, int64_t n, float* g, double* partials,
                    int64_t* grid_out, hipStream_t s) {
   RowTable<CAP> t;
   for (int i = 0; i < CAP; ++i) t.p[i] = i < world ? rows[i] : nullptr;
-  constexpr int E = Lanes<In>::E;
-  const int64_t ngroups = n / E;
-  const int64_t tile = (int64_t)kThreads * V;
-  int64_t grid = (ngroups + tile - 1) / tile;
+  const int64_t ngroups = n / 4;
+  const int64_t span = (int64_t)kThreads * G;
+  int64_t grid = (ngroups + span - 1) / span;
   if (grid > tuning().grid_cap) grid = tuning().grid_cap;
   if (partials && grid > max_partials(n)) grid = max_partials(n);
   if (grid < 1) grid = 1;
   *grid_out = grid;
+  const size_t lds = G > 1 ? (size_t)G * kThreads * 16 : 0;
   if (partials)
-    hipLaunchKernelGGL((k_reduce<NW, CAP, V, In, true>), dim3((unsigned)grid), dim3(kThreads), 0,
+    hipLaunchKernelGGL((k_reduce<NW, CAP, G, C, In, true>), dim3((unsigned)grid), dim3(kThreads), lds,
                        s, t, world, mean_div(world), ngroups, n, g, partials);
   else
-    hipLaunchKernelGGL((k_reduce<NW, CAP, V, In, false>), dim3((unsigned)grid), dim3(kThreads), 0,
+    hipLaunchKernelGGL((k_reduce<NW, CAP, G, C, In, false>), dim3((unsigned)grid), dim3(kThreads), lds,
                        s, t, world, mean_div(world), ngroups, n, g, partials);
   return hipGetLastError();
 }
 
-template <int V, typename In>
+template <int G, int C, typename In>
 hipError_t dispatch_world(const void* const* rows, int world, int64_t n, float* g,
                           double* partials, int64_t* grid, hipStream_t s) {
   switch (world) {
-    case 2: return run_vec<2, 2, V, In>(rows, world, n, g, partials, grid, s);
-    case 4: return run_vec<4, 4, V, In>(rows, world, n, g, partials, grid, s);
-    case 8: return run_vec<8, 8, V, In>(rows, world, n, g, partials, grid, s);
-    case 16: return run_vec<16, 16, V, In>(rows, world, n, g, partials, grid, s);
-    case 32: return run_vec<32, 32, V, In>(rows, world, n, g, partials, grid, s);
-    case 64: return run_vec<64, 64, V, In>(rows, world, n, g, partials, grid, s);
+    case 2: return run_vec<2, 2, G, C, In>(rows, world, n, g, partials, grid, s);
+    case 4: return run_vec<4, 4, G, C, In>(rows, world, n, g, partials, grid, s);
+    case 8: return run_vec<8, 8, G, C, In>(rows, world, n, g, partials, grid, s);
+    case 16: return run_vec<16, 16, G, C, In>(rows, world, n, g, partials, grid, s);
+    case 32: return run_vec<32, 32, G, C, In>(rows, world, n, g, partials, grid, s);
+    case 64: return run_vec<64, 64, G, C, In>(rows, world, n, g, partials, grid, s);
     default:
-      if (world <= 64) return run_vec<0, 64, V, In>(rows, world, n, g, partials, grid, s);
-      return run_vec<0, ZS_MAX_WORLD, V, In>(rows, world, n, g, partials, grid, s);
+      if (world <= 64) return run_vec<0, 64, G, C, In>(rows, world, n, g, partials, grid, s);
+      return run_vec<0, ZS_MAX_WORLD, G, C, In>(rows, world, n, g, partials, grid, s);
+  }
+}
+
+// Measured on MI355X: deep staging (16 groups, 64 KiB) pays off when the
+// rank walk is long; with few contributions direct stores are as fast.
+template <typename In>
+hipError_t dispatch_shape(const void* const* rows, int world, int64_t n, float* g,
+                          double* partials, int64_t* grid, hipStream_t s) {
+  const int gsel = tuning().reduce_g > 0 ? tuning().reduce_g : (world >= 16 ? 16 : 1);
+  const bool c4 = tuning().rank_chunk == 4;
+  switch (gsel) {
+    case 16:
+      return c4 ? dispatch_world<16, 4, In>(rows, world, n, g, partials, grid, s)
+                : dispatch_world<16, 8, In>(rows, world, n, g, partials, grid, s);
+    case 4:
+      return c4 ? dispatch_world<4, 4, In>(rows, world, n, g, partials, grid, s)
+                : dispatch_world<4, 8, In>(rows, world, n, g, partials, grid, s);
+    default:
+      return c4 ? dispatch_world<1, 4, In>(rows, world, n, g, partials, grid, s)
+                : dispatch_world<1, 8, In>(rows, world, n, g, partials, grid, s);
   }
 }
 
@@ -222,16 +235,12 @@ hipError_t launch_reduce(const void* const* rows, int world, int dtype, int64_t 
   hipError_t err = hipSuccess;
   if (n > 0) {
     bool vec = aligned16(g);
-    for (int i = 0; i < world; ++i) vec = vec && aligned16(rows[i]);
+    const uintptr_t ra = dtype == ZS_BF16 ? 7u : 15u;  // one lane group: 8 B of bf16, 16 B of fp32
+    for (int i = 0; i < world; ++i) vec = vec && (reinterpret_cast<uintptr_t>(rows[i]) & ra) == 0;
     double* parts = sumsq ? partials : nullptr;
     if (vec) {
-      const int v = tuning().reduce_v ? tuning().reduce_v : (world <= 16 ? 2 : 1);
-      if (dtype == ZS_BF16)
-        err = v == 2 ? dispatch_world<2, uint16_t>(rows, world, n, g, parts, &grid, s)
-                     : dispatch_world<1, uint16_t>(rows, world, n, g, parts, &grid, s);
-      else
-        err = v == 2 ? dispatch_world<2, float>(rows, world, n, g, parts, &grid, s)
-                     : dispatch_world<1, float>(rows, world, n, g, parts, &grid, s);
+      err = dtype == ZS_BF16 ? dispatch_shape<uint16_t>(rows, world, n, g, parts, &grid, s)
+                             : dispatch_shape<float>(rows, world, n, g, parts, &grid, s);
     } else {
       RowTable<ZS_MAX_WORLD> t;
       for (int i = 0; i < ZS_MAX_WORLD; ++i) t.p[i] = i < world ? rows[i] : nullptr;

@@ -22,13 +22,27 @@ constexpr int kThreads = 256;  // 4 wave64 per workgroup
 
 // ---- streaming memory access -------------------------------------------------
 
+#ifndef ZS_NT_LOADS
+#define ZS_NT_LOADS 1
+#endif
 template <typename T>
 __device__ __forceinline__ T ld_nt(const T* p) {
+#if ZS_NT_LOADS
   return __builtin_nontemporal_load(p);
+#else
+  return *p;
+#endif
 }
+#ifndef ZS_NT_STORES
+#define ZS_NT_STORES 1
+#endif
 template <typename T>
 __device__ __forceinline__ void st_nt(T v, T* p) {
+#if ZS_NT_STORES
   __builtin_nontemporal_store(v, p);
+#else
+  *p = v;
+#endif
 }
 
 // ---- bf16 <-> fp32 -----------------------------------------------------------
@@ -61,23 +75,19 @@ struct RowTable {
   const void* p[CAP];
 };
 
-// One 16-byte vector of contributions decoded to fp32: 8 bf16 or 4 fp32 elements.
+// A lane's unit of work is a group of 4 consecutive elements in every stream:
+// 8 bytes of bf16 or 16 bytes of fp32 contributions, 16 bytes of each fp32
+// state array and 8 bytes of bf16 output. Lane i of a wave takes group
+// base + i, so every load and store instruction of a wave covers one
+// contiguous span (512 B or 1 KiB) of its stream.
 template <typename In>
 struct Lanes;
 template <>
 struct Lanes<uint16_t> {
-  static constexpr int E = 8;
-  __device__ __forceinline__ static void decode(const u32x4& w, float* out) {
-    out[0] = bf16_lo(w.x); out[1] = bf16_hi(w.x);
-    out[2] = bf16_lo(w.y); out[3] = bf16_hi(w.y);
-    out[4] = bf16_lo(w.z); out[5] = bf16_hi(w.z);
-    out[6] = bf16_lo(w.w); out[7] = bf16_hi(w.w);
-  }
-  __device__ __forceinline__ static void add(const u32x4& w, float* acc) {
+  typedef u32x2 Vec;  // 4 bf16
+  __device__ __forceinline__ static void add(const Vec& w, float* acc) {
     acc[0] += bf16_lo(w.x); acc[1] += bf16_hi(w.x);
     acc[2] += bf16_lo(w.y); acc[3] += bf16_hi(w.y);
-    acc[4] += bf16_lo(w.z); acc[5] += bf16_hi(w.z);
-    acc[6] += bf16_lo(w.w); acc[7] += bf16_hi(w.w);
   }
   __device__ __forceinline__ static float scalar(const void* row, int64_t i) {
     return bf16_to_f32(static_cast<const uint16_t*>(row)[i]);
@@ -85,12 +95,8 @@ struct Lanes<uint16_t> {
 };
 template <>
 struct Lanes<float> {
-  static constexpr int E = 4;
-  __device__ __forceinline__ static void decode(const u32x4& w, float* out) {
-    out[0] = __uint_as_float(w.x); out[1] = __uint_as_float(w.y);
-    out[2] = __uint_as_float(w.z); out[3] = __uint_as_float(w.w);
-  }
-  __device__ __forceinline__ static void add(const u32x4& w, float* acc) {
+  typedef u32x4 Vec;  // 4 fp32
+  __device__ __forceinline__ static void add(const Vec& w, float* acc) {
     acc[0] += __uint_as_float(w.x); acc[1] += __uint_as_float(w.y);
     acc[2] += __uint_as_float(w.z); acc[3] += __uint_as_float(w.w);
   }
@@ -98,6 +104,55 @@ struct Lanes<float> {
     return static_cast<const float*>(row)[i];
   }
 };
+
+// Rank sums of V groups per lane, double-buffered: the loads of the next chunk
+// of C ranks are in flight while the current chunk is added, so a lane keeps
+// C*V to 2*C*V independent loads outstanding through the whole walk. Each sum
+// starts from -0.0, the additive identity of IEEE addition (-0 + x == x for
+// every x, signed zeros included), so it equals c_0 + c_1 + ... + c_{N-1}
+// evaluated left to right in fp32.
+template <typename In, int C, int V, int CAP>
+__device__ __forceinline__ void rank_sum(const RowTable<CAP>& rows, int nw, const int64_t* q,
+                                         float (*acc)[4]) {
+  using L = Lanes<In>;
+  using Vec = typename L::Vec;
+#pragma unroll
+  for (int j = 0; j < V; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[j][e] = -0.0f;
+  Vec a[C][V], b[C][V];
+#pragma unroll
+  for (int u = 0; u < C; ++u)
+    if (u < nw)
+#pragma unroll
+      for (int j = 0; j < V; ++j) a[u][j] = ld_nt(static_cast<const Vec*>(rows.p[u]) + q[j]);
+#pragma unroll 1
+  for (int r0 = 0; r0 < nw; r0 += 2 * C) {
+#pragma unroll
+    for (int u = 0; u < C; ++u)
+      if (r0 + C + u < nw)
+#pragma unroll
+        for (int j = 0; j < V; ++j)
+          b[u][j] = ld_nt(static_cast<const Vec*>(rows.p[r0 + C + u]) + q[j]);
+#pragma unroll
+    for (int u = 0; u < C; ++u)
+      if (r0 + u < nw)
+#pragma unroll
+        for (int j = 0; j < V; ++j) L::add(a[u][j], acc[j]);
+    if (r0 + C >= nw) break;
+#pragma unroll
+    for (int u = 0; u < C; ++u)
+      if (r0 + 2 * C + u < nw)
+#pragma unroll
+        for (int j = 0; j < V; ++j)
+          a[u][j] = ld_nt(static_cast<const Vec*>(rows.p[r0 + 2 * C + u]) + q[j]);
+#pragma unroll
+    for (int u = 0; u < C; ++u)
+      if (r0 + C + u < nw)
+#pragma unroll
+        for (int j = 0; j < V; ++j) L::add(b[u][j], acc[j]);
+  }
+}
 
 // Division of the rank sum by N. For N a power of two the product with the
 // exact reciprocal is the same correctly rounded value, so both branches give

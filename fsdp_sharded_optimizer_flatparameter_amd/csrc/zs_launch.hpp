@@ -12,11 +12,16 @@ namespace zs {
 struct AdamConsts;
 
 // Launch-shape knobs. Defaults are the measured best on MI355X; each can be
-// overridden once per process through the environment (ZS_REDUCE_V,
-// ZS_ADAMW_V, ZS_GRID_CAP) for sweeps. None of them changes any result.
+// overridden once per process through the environment (ZS_ADAMW_V,
+// ZS_ADAMW_LDS, ZS_RANK_CHUNK, ZS_FUSED_G,
+// ZS_FUSED_LDS, ZS_REDUCE_G, ZS_GRID_CAP) for sweeps. None of them changes any result.
 struct Tuning {
-  int reduce_v;    // 16-byte groups per lane per tile in the reduce / fused kernels (1 or 2)
-  int adamw_v;     // 16-byte groups per lane per tile in AdamW / cast (1, 2 or 4)
+  int adamw_v;     // 16-byte groups per lane per tile in AdamW (1, 2 or 4)
+  int64_t adamw_lds;  // LDS bytes reserved per AdamW / cast workgroup (caps residency)
+  int rank_chunk;  // ranks per load chunk of the double-buffered rank walk (4 or 8)
+  int fused_g;     // groups per lane staged in LDS by the single-pass kernel (0 = by world size)
+  int64_t fused_lds;  // LDS bytes reserved per workgroup of the single-pass kernel (0 = default)
+  int reduce_g;    // groups per lane staged in LDS by the reduce kernel (0 = by world size)
   int64_t grid_cap;  // upper bound on workgroups of the streaming kernels
 };
 const Tuning& tuning();
