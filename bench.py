@@ -45,9 +45,16 @@ WORKLOADS = {
 }
 
 
-def source_hash() -> str:
+# Sources that define each timed kernel and its launch shape; counter-derived
+# traffic is reported only while these are unchanged since the counters were taken.
+KERNEL_SOURCES = {
+    "k_fused": ("fused.hip", "zs_device.hpp", "zs_launch.hpp", "tuning.cpp"),
+}
+
+
+def source_hash(kernel: str) -> str:
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
+    for name in KERNEL_SOURCES[kernel]:
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
@@ -97,6 +104,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parts", action="store_true", help="time only the step")
     ap.add_argument("--cpu-windows", type=int, default=24, help="2^20-element windows for the oracle timing")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="before timing, run one plain 1 GiB device copy (torch copy_) as the known-size "
+                         "reference for HBM byte counters")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -155,6 +165,13 @@ def main() -> int:
         step_no[0] += 1
         zs.zs_sharded_step(rows, theta, m, v, step=step_no[0], bf16_out=slot, **hp)
 
+    if args.calibrate_copy:
+        src = torch.ones(1 << 28, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)  # reads 1 GiB, writes 1 GiB
+        torch.cuda.synchronize()
+        del src, dst
+
     # ---- the step: warmup, then exactly K timed steps between synchronisations
     for i in range(args.warmup):
         fused_step(i)
@@ -175,8 +192,8 @@ def main() -> int:
     adamw_bpe = 30                         # read g,theta,m,v + write theta,m,v + bf16
     cast_bpe = 6
     achieved = fused_bpe * S / (ms_step * 1e-3) / 1e9
-    src_hash = source_hash()
     kernel_name = "k_fused"
+    src_hash = source_hash(kernel_name)
     traffic = read_traffic(args.workload, kernel_name, src_hash)
 
     parts = {}

@@ -28,7 +28,7 @@ COMMON = [
 # Device code: gfx950 only. Packed-fp32 VALU ops are kept out of the generated code.
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
-SOURCES = ["abi.cpp", "reduce.hip", "adamw.hip", "fused.hip", "segments.hip"]
+SOURCES = ["abi.cpp", "tuning.cpp", "reduce.hip", "adamw.hip", "fused.hip", "segments.hip"]
 
 
 def hipcc() -> str:

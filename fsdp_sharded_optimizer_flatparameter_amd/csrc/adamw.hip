@@ -202,8 +202,8 @@ hipError_t launch_cast(const float* src, int64_t n, uint16_t* out, hipStream_t s
   if (n == 0) return hipSuccess;
   if (al(src, 16) && al(out, 8)) {
     const int64_t ngroups = n / 4;
-    const dim3 gd((unsigned)grid_for(ngroups, kThreads));
-    hipLaunchKernelGGL((k_cast<1>), gd, dim3(kThreads), (size_t)tuning().adamw_lds, s, src, ngroups, n, out);
+    const dim3 gd((unsigned)grid_for(ngroups, 2 * kThreads));
+    hipLaunchKernelGGL((k_cast<2>), gd, dim3(kThreads), 0, s, src, ngroups, n, out);
   } else {
     const dim3 gd((unsigned)grid_for(n, 4 * kThreads));
     hipLaunchKernelGGL(k_cast_scalar, gd, dim3(kThreads), 0, s, src, n, out);

@@ -20,45 +20,10 @@
 //   * one IEEE division by N (a multiply by the exact reciprocal when N is a
 //     power of two), so the result is independent of the launch shape;
 //   * rows are read with the nontemporal hint (each byte is used once).
-#include <cstdlib>
-
 #include "zs_device.hpp"
 #include "zs_launch.hpp"
 
 namespace zs {
-
-const Tuning& tuning() {
-  static const Tuning t = [] {
-    Tuning x{0, 0, 0, 0, 0, 0, 0};
-    const char* e;
-    x.adamw_v = (e = std::getenv("ZS_ADAMW_V")) ? std::atoi(e) : 1;
-    if (x.adamw_v != 1 && x.adamw_v != 2 && x.adamw_v != 4) x.adamw_v = 1;
-    // a 32 KiB reservation (4 workgroups per CU) measured best for AdamW and the cast
-    x.adamw_lds = (e = std::getenv("ZS_ADAMW_LDS")) ? std::atoll(e) : 32768;
-    if (x.adamw_lds < 0 || x.adamw_lds > 65536) x.adamw_lds = 32768;
-    x.rank_chunk = (e = std::getenv("ZS_RANK_CHUNK")) ? std::atoi(e) : 8;
-    if (x.rank_chunk != 4 && x.rank_chunk != 8) x.rank_chunk = 8;
-    x.fused_g = (e = std::getenv("ZS_FUSED_G")) ? std::atoi(e) : 0;
-    if (x.fused_g != 1 && x.fused_g != 2 && x.fused_g != 4 && x.fused_g != 8 && x.fused_g != 16) x.fused_g = 0;
-    x.fused_lds = (e = std::getenv("ZS_FUSED_LDS")) ? std::atoll(e) : 0;
-    if (x.fused_lds < 0 || x.fused_lds > 65536) x.fused_lds = 0;
-    x.reduce_g = (e = std::getenv("ZS_REDUCE_G")) ? std::atoi(e) : 0;
-    if (x.reduce_g != 1 && x.reduce_g != 4 && x.reduce_g != 16) x.reduce_g = 0;
-    x.grid_cap = (e = std::getenv("ZS_GRID_CAP")) ? std::atoll(e) : 0;
-    // gridDim.x * blockDim.x must stay below 2^32; grid-stride loops cover the rest
-    const int64_t kHardCap = int64_t(1) << 22;
-    if (x.grid_cap <= 0 || x.grid_cap > kHardCap) x.grid_cap = kHardCap;
-    return x;
-  }();
-  return t;
-}
-
-int64_t max_partials(int64_t n) {
-  // every sum-of-squares launch uses at most one workgroup per 1024 elements
-  const int64_t b = (n + 1023) / 1024;
-  const int64_t kMax = 65536;
-  return b < 1 ? 1 : (b > kMax ? kMax : b);
-}
 
 namespace {
 

@@ -17,7 +17,7 @@ struct AdamConsts;
 // ZS_FUSED_LDS, ZS_REDUCE_G, ZS_GRID_CAP) for sweeps. None of them changes any result.
 struct Tuning {
   int adamw_v;     // 16-byte groups per lane per tile in AdamW (1, 2 or 4)
-  int64_t adamw_lds;  // LDS bytes reserved per AdamW / cast workgroup (caps residency)
+  int64_t adamw_lds;  // LDS bytes reserved per AdamW workgroup (caps residency)
   int rank_chunk;  // ranks per load chunk of the double-buffered rank walk (4 or 8)
   int fused_g;     // groups per lane staged in LDS by the single-pass kernel (0 = by world size)
   int64_t fused_lds;  // LDS bytes reserved per workgroup of the single-pass kernel (0 = default)
