@@ -46,22 +46,24 @@ __global__ __launch_bounds__(kThreads) void k_fused(RowTable<CAP> rows, int worl
   const int64_t span = (int64_t)kThreads * G;
 
   for (int64_t base = (int64_t)blockIdx.x * span; base < ngroups; base += (int64_t)gridDim.x * span) {
-    for (int k = 0; k < G; ++k) {
-      const int64_t qq = base + k * kThreads + threadIdx.x;
-      const int64_t q = qq < ngroups ? qq : ngroups - 1;  // clamped: loads stay in bounds
-      float acc[1][4];
-      rank_sum<In, C, 1, CAP>(rows, nw, &q, acc);
+    rank_sums_streamed<In, C, G, CAP>(rows, nw, base, ngroups, [&](int k, const float* acc) {
       f32x4 gv;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) gv[e] = SCALE ? div(acc[0][e]) * sc : div(acc[0][e]);
+      for (int e = 0; e < 4; ++e) gv[e] = SCALE ? div(acc[e]) * sc : div(acc[e]);
       gl[k * kThreads + threadIdx.x] = gv;
-    }
-    for (int k = 0; k < G; ++k) {
-      const int64_t qq = base + k * kThreads + threadIdx.x;
-      if (qq >= ngroups) break;
-      f32x4 T = ld_nt(reinterpret_cast<const f32x4*>(th) + qq);
-      f32x4 M = ld_nt(reinterpret_cast<const f32x4*>(m) + qq);
-      f32x4 W = ld_nt(reinterpret_cast<const f32x4*>(v) + qq);
+    });
+    // phase 2, double-buffered: group k+1's state loads are in flight while
+    // group k is updated and stored
+    auto qidx = [&](int k) { return base + (int64_t)k * kThreads + threadIdx.x; };
+    auto load = [&](int k, f32x4& T, f32x4& M, f32x4& W) {
+      const int64_t q = qidx(k) < ngroups ? qidx(k) : ngroups - 1;
+      T = ld_nt(reinterpret_cast<const f32x4*>(th) + q);
+      M = ld_nt(reinterpret_cast<const f32x4*>(m) + q);
+      W = ld_nt(reinterpret_cast<const f32x4*>(v) + q);
+    };
+    auto update = [&](int k, f32x4& T, f32x4& M, f32x4& W) {
+      const int64_t qq = qidx(k);
+      if (qq >= ngroups) return;
       const f32x4 gv = gl[k * kThreads + threadIdx.x];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -76,6 +78,16 @@ __global__ __launch_bounds__(kThreads) void k_fused(RowTable<CAP> rows, int worl
       st_nt(W, reinterpret_cast<f32x4*>(v) + qq);
       if (CAST)
         st_nt(u32x2{pack_bf16x2(T[0], T[1]), pack_bf16x2(T[2], T[3])}, reinterpret_cast<u32x2*>(out) + qq);
+    };
+    f32x4 T0, M0, W0, T1, M1, W1;
+    load(0, T0, M0, W0);
+#pragma unroll 1
+    for (int k = 0; k < G; k += 2) {
+      if (k + 1 < G) load(k + 1, T1, M1, W1);
+      update(k, T0, M0, W0);
+      if (k + 1 >= G) break;
+      if (k + 2 < G) load(k + 2, T0, M0, W0);
+      update(k + 1, T1, M1, W1);
     }
   }
   if (blockIdx.x == 0) {  // ragged tail (fewer than 4 elements)
@@ -133,11 +145,11 @@ struct Shape {
 
 // Measured on MI355X: with many contributions the row walk dominates and deep
 // staging (16 groups in 64 KiB) is best; with few contributions the state
-// read-modify-write dominates and shallow staging (4 groups) under the same
+// read-modify-write dominates and shallow staging (2 groups) under the same
 // 64 KiB reservation (2 workgroups per CU) is best.
 Shape fused_shape(int world) {
   Shape sh;
-  sh.g = tuning().fused_g > 0 ? tuning().fused_g : (world >= 16 ? 16 : 4);
+  sh.g = tuning().fused_g > 0 ? tuning().fused_g : (world >= 16 ? 16 : 2);
   const size_t need = (size_t)sh.g * kThreads * 16;
   sh.lds = tuning().fused_lds > 0 ? (size_t)tuning().fused_lds : 65536;
   if (sh.lds < need) sh.lds = need;

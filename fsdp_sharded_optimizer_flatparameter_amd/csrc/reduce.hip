@@ -54,15 +54,12 @@ __global__ __launch_bounds__(kThreads) void k_reduce(RowTable<CAP> rows, int wor
   double ss = 0.0;
 
   for (int64_t base = (int64_t)blockIdx.x * span; base < ngroups; base += (int64_t)gridDim.x * span) {
-    for (int k = 0; k < G; ++k) {
-      const int64_t qq = base + k * kThreads + threadIdx.x;
-      const int64_t q = qq < ngroups ? qq : ngroups - 1;  // clamped: loads stay in bounds
-      float acc[1][4];
-      rank_sum<In, C, 1, CAP>(rows, nw, &q, acc);
+    rank_sums_streamed<In, C, G, CAP>(rows, nw, base, ngroups, [&](int k, const float* acc) {
+      const int64_t qq = base + (int64_t)k * kThreads + threadIdx.x;
       f32x4 o;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        o[e] = div(acc[0][e]);
+        o[e] = div(acc[e]);
         if (SUMSQ && qq < ngroups) ss = fma((double)o[e], (double)o[e], ss);
       }
       if (G == 1) {
@@ -70,7 +67,7 @@ __global__ __launch_bounds__(kThreads) void k_reduce(RowTable<CAP> rows, int wor
       } else {
         gl[k * kThreads + threadIdx.x] = o;
       }
-    }
+    });
     if (G > 1) {
       for (int k = 0; k < G; ++k) {  // each lane writes back only its own entries
         const int64_t qq = base + k * kThreads + threadIdx.x;

@@ -154,6 +154,54 @@ __device__ __forceinline__ void rank_sum(const RowTable<CAP>& rows, int nw, cons
   }
 }
 
+// Rank sums of G groups per lane -- group k at index base + k*kThreads + lane --
+// streamed as one double-buffered sequence of rank chunks that runs across
+// group boundaries: while chunk i is added, chunk i+1 (the next ranks of the
+// same group, or the first ranks of the next group) is already in flight, so a
+// lane never waits a full memory round trip between two groups. Each group's
+// sum starts from -0.0 and adds ranks in ascending order (the same fp32 result
+// as rank_sum). sink(k, acc) receives group k's finished sums.
+template <typename In, int C, int G, int CAP, typename Sink>
+__device__ __forceinline__ void rank_sums_streamed(const RowTable<CAP>& rows, int nw, int64_t base,
+                                                   int64_t ngroups, Sink&& sink) {
+  using L = Lanes<In>;
+  using Vec = typename L::Vec;
+  const int nch = (nw + C - 1) / C;  // chunks per group
+  const int total = G * nch;
+  auto load = [&](int idx, Vec* buf) {
+    const int k = idx / nch;
+    const int r0 = (idx - k * nch) * C;
+    const int64_t qq = base + (int64_t)k * kThreads + threadIdx.x;
+    const int64_t q = qq < ngroups ? qq : ngroups - 1;  // clamped: loads stay in bounds
+#pragma unroll
+    for (int u = 0; u < C; ++u)
+      if (r0 + u < nw) buf[u] = ld_nt(static_cast<const Vec*>(rows.p[r0 + u]) + q);
+  };
+  float acc[4] = {-0.0f, -0.0f, -0.0f, -0.0f};
+  auto consume = [&](int idx, const Vec* buf) {
+    const int k = idx / nch;
+    const int r0 = (idx - k * nch) * C;
+#pragma unroll
+    for (int u = 0; u < C; ++u)
+      if (r0 + u < nw) L::add(buf[u], acc);
+    if (r0 + C >= nw) {
+      sink(k, acc);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = -0.0f;
+    }
+  };
+  Vec a[C], b[C];
+  load(0, a);
+#pragma unroll 1
+  for (int idx = 0; idx < total; idx += 2) {
+    if (idx + 1 < total) load(idx + 1, b);
+    consume(idx, a);
+    if (idx + 1 >= total) break;
+    if (idx + 2 < total) load(idx + 2, a);
+    consume(idx + 1, b);
+  }
+}
+
 // Division of the rank sum by N. For N a power of two the product with the
 // exact reciprocal is the same correctly rounded value, so both branches give
 // the IEEE quotient.
