@@ -48,14 +48,15 @@ WORKLOADS = {
 # Sources that define each timed kernel and its launch shape; counter-derived
 # traffic is reported only while these are unchanged since the counters were taken.
 KERNEL_SOURCES = {
-    "k_fused": ("fused.hip", "zs_device.hpp", "zs_launch.hpp", "tuning.cpp"),
+    "k_fused": ("csrc/fused.hip", "csrc/zs_device.hpp", "csrc/zs_launch.hpp", "csrc/tuning.cpp",
+                "build.py"),
 }
 
 
 def source_hash(kernel: str) -> str:
     h = hashlib.sha256()
     for name in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(CSRC, name), "rb") as f:
+        with open(os.path.join(os.path.dirname(CSRC), name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 

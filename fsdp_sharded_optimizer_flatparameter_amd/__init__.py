@@ -9,8 +9,11 @@ from .api import (  # noqa: F401
     ParamTable,
     ZsArgumentError,
     ZsError,
+    zs_accumulate_grads,
+    zs_accumulate_local,
     zs_adamw_step,
     zs_cast_for_gather,
+    zs_clip_coefficient,
     zs_copy_out,
     zs_flat_layout,
     zs_pack_shard,

@@ -49,6 +49,13 @@ SIGNATURES = {
     "zs_sharded_step": (C.c_int32, [C.POINTER(C.c_void_p), C.c_int32, C.c_int32, C.c_int64,
                                     C.c_void_p, C.c_void_p, C.c_void_p, C.POINTER(AdamWHParams),
                                     C.c_void_p, C.c_void_p, C.c_void_p]),
+    "zs_accumulate_grads": (C.c_int32, [C.POINTER(C.c_void_p), C.c_int32, C.c_int32, C.c_int64,
+                                        C.c_void_p, C.c_float, C.c_int32, C.c_void_p, C.c_void_p,
+                                        C.c_size_t, C.c_void_p]),
+    "zs_accumulate_local": (C.c_int32, [C.c_void_p, C.c_int32, C.c_int64, C.c_void_p, C.c_int32,
+                                        C.c_void_p]),
+    "zs_clip_coefficient": (C.c_int32, [C.c_void_p, C.c_int32, C.c_double, C.c_void_p, C.c_void_p,
+                                        C.c_void_p]),
     "zs_status_string": (C.c_char_p, [C.c_int32]),
     "zs_version": (C.c_int32, []),
 }

@@ -215,5 +215,44 @@ def zs_sharded_step(rows, master, exp_avg, exp_avg_sq, *, lr, beta1, beta2, eps,
         _ptr(grad_scale), _ptr(bf16_out), _stream(stream, master.device)))
 
 
+def zs_accumulate_grads(rows, acc, *, scale=1.0, first=False, sumsq_out=None, workspace=None,
+                        stream=None):
+    _dev(acc, "acc", torch.float32)
+    arr, world, dt = _rows(rows, acc.numel())
+    ws_bytes = 0
+    if sumsq_out is not None:
+        _dev(sumsq_out, "sumsq_out", torch.float64)
+    if workspace is not None:
+        _dev(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    L.check("zs_accumulate_grads", _lib().zs_accumulate_grads(
+        arr, world, dt, acc.numel(), _ptr(acc), float(scale), int(bool(first)), _ptr(sumsq_out),
+        _ptr(workspace), ws_bytes, _stream(stream, acc.device)))
+
+
+def zs_accumulate_local(grad, acc, *, first=False, stream=None):
+    _dev(acc, "acc", torch.float32)
+    _dev(grad, "grad")
+    if grad.dtype not in _DTYPES:
+        raise ValueError(f"unsupported gradient dtype {grad.dtype}")
+    if grad.numel() != acc.numel():
+        raise ValueError("grad and acc must have the same size")
+    L.check("zs_accumulate_local", _lib().zs_accumulate_local(
+        _ptr(grad), _DTYPES[grad.dtype], acc.numel(), _ptr(acc), int(bool(first)),
+        _stream(stream, acc.device)))
+
+
+def zs_clip_coefficient(partials, max_norm, coef_out, norm_out=None, stream=None):
+    _dev(partials, "partials", torch.float64)
+    _dev(coef_out, "coef_out", torch.float32)
+    if coef_out.numel() != 1:
+        raise ValueError("coef_out is a single fp32 value")
+    if norm_out is not None:
+        _dev(norm_out, "norm_out", torch.float64)
+    L.check("zs_clip_coefficient", _lib().zs_clip_coefficient(
+        _ptr(partials), partials.numel(), float(max_norm), _ptr(coef_out), _ptr(norm_out),
+        _stream(stream, partials.device)))
+
+
 def zs_version() -> int:
     return int(_lib().zs_version())

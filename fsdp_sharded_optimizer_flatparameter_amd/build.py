@@ -25,10 +25,14 @@ COMMON = [
     "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
-# Device code: gfx950 only. Packed-fp32 VALU ops are kept out of the generated code.
-DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Device code: gfx950 only. Packed-fp32 VALU ops are kept out of the generated code, and
+# floating-point contraction is off: every operation rounds as written, fused
+# multiply-adds appear only where the source calls fmaf/fma.
+DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-ffp-contract=off"]
 
-SOURCES = ["abi.cpp", "tuning.cpp", "reduce.hip", "adamw.hip", "fused.hip", "segments.hip"]
+SOURCES = ["abi.cpp", "tuning.cpp", "reduce.hip", "adamw.hip", "fused.hip", "accumulate.hip",
+           "segments.hip"]
 
 
 def hipcc() -> str:

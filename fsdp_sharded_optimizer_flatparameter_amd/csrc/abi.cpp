@@ -241,4 +241,45 @@ zs_status zs_sharded_step(const void* const* rows, int32_t world, int32_t dtype,
                                      grad_scale, bf16_out, stream));
 }
 
+zs_status zs_accumulate_grads(const void* const* rows, int32_t world, int32_t dtype, int64_t n,
+                              float* acc, float scale, int32_t first, double* sumsq_out,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  zs_status st = check_rows(rows, world, dtype, n);
+  if (st != ZS_OK) return st;
+  if (!std::isfinite(scale)) return ZS_ERR_HPARAM;
+  if (n > 0 && !acc) return ZS_ERR_NULL;
+  if (acc && !aligned(acc, 4)) return ZS_ERR_ALIGN;
+  if (sumsq_out) {
+    if (!aligned(sumsq_out, 8)) return ZS_ERR_ALIGN;
+    if (!workspace || workspace_bytes < zs_workspace_bytes(n)) return ZS_ERR_WORKSPACE;
+    if (!aligned(workspace, 8)) return ZS_ERR_ALIGN;
+  }
+  if (n == 0 && !sumsq_out) return ZS_OK;
+  for (int32_t q = 0; q < world && n > 0; ++q)
+    if (overlaps(acc, n * 4, rows[q], n * elem_size(dtype))) return ZS_ERR_OVERLAP;
+  return hip_status(zs::launch_accumulate(rows, world, dtype, n, acc, scale, first != 0, sumsq_out,
+                                          static_cast<double*>(workspace), stream));
+}
+
+zs_status zs_accumulate_local(const void* grad, int32_t dtype, int64_t n, float* acc,
+                              int32_t first, hipStream_t stream) {
+  if (dtype != ZS_F32 && dtype != ZS_BF16) return ZS_ERR_DTYPE;
+  if (n < 0) return ZS_ERR_SIZE;
+  if (n == 0) return ZS_OK;
+  if (!grad || !acc) return ZS_ERR_NULL;
+  if (!aligned(grad, (uintptr_t)elem_size(dtype)) || !aligned(acc, 4)) return ZS_ERR_ALIGN;
+  if (overlaps(grad, n * elem_size(dtype), acc, n * 4)) return ZS_ERR_OVERLAP;
+  return hip_status(zs::launch_accumulate_local(grad, dtype, n, acc, first != 0, stream));
+}
+
+zs_status zs_clip_coefficient(const double* partials, int32_t count, double max_norm,
+                              float* coef_out, double* norm_out, hipStream_t stream) {
+  if (count < 1) return ZS_ERR_SIZE;
+  if (!std::isfinite(max_norm) || !(max_norm > 0)) return ZS_ERR_HPARAM;
+  if (!partials || !coef_out) return ZS_ERR_NULL;
+  if (!aligned(partials, 8) || !aligned(coef_out, 4) || (norm_out && !aligned(norm_out, 8)))
+    return ZS_ERR_ALIGN;
+  return hip_status(zs::launch_clip(partials, count, max_norm, coef_out, norm_out, stream));
+}
+
 }  // extern "C"

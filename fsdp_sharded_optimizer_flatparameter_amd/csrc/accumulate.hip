@@ -1,0 +1,263 @@
+// Gradient accumulation over micro-batches and the global-norm clip coefficient.
+//
+// Pages: "Lesson 5: ZeRO and FSDP" s3 (under gradient accumulation ZeRO-1 sums
+// each rank's full local gradient and reduce-scatters once, ZeRO-2
+// reduce-scatters every micro-batch and accumulates its 1/N) and s2 (the fp32
+// accumulation buffer: 4P for ZeRO-0/1, 4P/N for ZeRO-2/3); "Data parallelism
+// and ZeRO memory sharding" s6 (a global norm needs every shard's partial).
+//
+//   k_accum        acc = (first ? scale*mean : acc + scale*mean)   [sharded]
+//                  2N + 8 bytes per element (2N + 4 on the first micro-batch)
+//   k_accum_local  acc = (first ? g : acc + g), g bf16 or fp32      [unsharded]
+//   k_clip         coefficient = min(1, max_norm / (sqrt(sum of partials) + 1e-6))
+#include <cmath>
+
+#include "zs_device.hpp"
+#include "zs_launch.hpp"
+
+namespace zs {
+namespace {
+
+constexpr int kAccumG = 4;  // groups per lane; their previous sums are loaded before the walk
+
+MeanDiv mean_div(int world) {
+  MeanDiv d;
+  d.n = (float)world;
+  d.pow2 = (world & (world - 1)) == 0;
+  d.inv = 1.0f / (float)world;
+  return d;
+}
+
+template <int NW, int CAP, typename In, bool SUMSQ, bool FIRST, bool SCALE>
+__global__ __launch_bounds__(kThreads) void k_accum(RowTable<CAP> rows, int world, MeanDiv div,
+                                                    float scale, int64_t ngroups, int64_t n,
+                                                    float* __restrict__ acc,
+                                                    double* __restrict__ partials) {
+  using L = Lanes<In>;
+  constexpr int G = kAccumG;
+  const int nw = NW > 0 ? NW : world;
+  const int64_t span = (int64_t)kThreads * G;
+  double ss = 0.0;
+  __shared__ f32x4 old[G * kThreads];  // each lane's previous sums (lane-private slots)
+  for (int64_t base = (int64_t)blockIdx.x * span; base < ngroups; base += (int64_t)gridDim.x * span) {
+    if (!FIRST) {
+#pragma unroll
+      for (int k = 0; k < G; ++k) {
+        const int64_t qq = base + (int64_t)k * kThreads + threadIdx.x;
+        const int64_t q = qq < ngroups ? qq : ngroups - 1;
+        old[k * kThreads + threadIdx.x] = ld_nt(reinterpret_cast<const f32x4*>(acc) + q);
+      }
+    }
+    rank_sums_streamed<In, 8, G, CAP>(rows, nw, base, ngroups, [&](int k, const float* s) {
+      const int64_t qq = base + (int64_t)k * kThreads + threadIdx.x;
+      if (qq >= ngroups) return;
+      f32x4 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float u = div(s[e]);
+        if (SCALE) u *= scale;
+        o[e] = FIRST ? u : old[k * kThreads + threadIdx.x][e] + u;
+        if (SUMSQ) ss = fma((double)o[e], (double)o[e], ss);
+      }
+      st_nt(o, reinterpret_cast<f32x4*>(acc) + qq);
+    });
+  }
+  if (blockIdx.x == 0) {  // ragged tail
+    for (int64_t i = ngroups * 4 + threadIdx.x; i < n; i += kThreads) {
+      float s = -0.0f;
+      for (int r = 0; r < nw; ++r) s += L::scalar(rows.p[r], i);
+      float u = div(s);
+      if (SCALE) u *= scale;
+      const float o = FIRST ? u : acc[i] + u;
+      acc[i] = o;
+      if (SUMSQ) ss = fma((double)o, (double)o, ss);
+    }
+  }
+  if (SUMSQ) {
+    __shared__ double lds[kThreads / 64];
+    const double b = block_sum_fixed(ss, lds);
+    if (threadIdx.x == 0) partials[blockIdx.x] = b;
+  }
+}
+
+// Element-wise variant for pointers off the vector grid; identical arithmetic.
+template <typename In, bool SUMSQ, bool FIRST, bool SCALE>
+__global__ __launch_bounds__(kThreads) void k_accum_scalar(RowTable<ZS_MAX_WORLD> rows, int world,
+                                                           MeanDiv div, float scale, int64_t n,
+                                                           float* __restrict__ acc,
+                                                           double* __restrict__ partials) {
+  using L = Lanes<In>;
+  double ss = 0.0;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * kThreads) {
+    float s = -0.0f;
+    for (int r = 0; r < world; ++r) s += L::scalar(rows.p[r], i);
+    float u = div(s);
+    if (SCALE) u *= scale;
+    const float o = FIRST ? u : acc[i] + u;
+    acc[i] = o;
+    if (SUMSQ) ss = fma((double)o, (double)o, ss);
+  }
+  if (SUMSQ) {
+    __shared__ double lds[kThreads / 64];
+    const double b = block_sum_fixed(ss, lds);
+    if (threadIdx.x == 0) partials[blockIdx.x] = b;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void k_sumsq_finalize2(const double* __restrict__ partials,
+                                                              int64_t count,
+                                                              double* __restrict__ out) {
+  double s = 0.0;
+  for (int64_t i = threadIdx.x; i < count; i += kThreads) s += partials[i];
+  __shared__ double lds[kThreads / 64];
+  const double b = block_sum_fixed(s, lds);
+  if (threadIdx.x == 0) *out = b;
+}
+
+template <typename In, bool FIRST>
+__global__ __launch_bounds__(kThreads) void k_accum_local(const In* __restrict__ g, int64_t ngroups,
+                                                          int64_t n, float* __restrict__ acc,
+                                                          int vec) {
+  using L = Lanes<In>;
+  using Vec = typename L::Vec;
+  if (vec) {
+    for (int64_t q = (int64_t)blockIdx.x * kThreads + threadIdx.x; q < ngroups;
+         q += (int64_t)gridDim.x * kThreads) {
+      const Vec w = ld_nt(reinterpret_cast<const Vec*>(g) + q);
+      float x[4] = {-0.0f, -0.0f, -0.0f, -0.0f};
+      L::add(w, x);  // -0 + g == g exactly: the widened gradient
+      f32x4 o;
+      if (FIRST) {
+        o = f32x4{x[0], x[1], x[2], x[3]};
+      } else {
+        const f32x4 a = ld_nt(reinterpret_cast<const f32x4*>(acc) + q);
+        o = f32x4{a[0] + x[0], a[1] + x[1], a[2] + x[2], a[3] + x[3]};
+      }
+      st_nt(o, reinterpret_cast<f32x4*>(acc) + q);
+    }
+  }
+  const int64_t start = vec ? ngroups * 4 : 0;
+  for (int64_t i = start + (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * kThreads) {
+    const float x = L::scalar(g, i);
+    acc[i] = FIRST ? x : acc[i] + x;
+  }
+}
+
+__global__ void k_clip(const double* __restrict__ partials, int count, double max_norm,
+                       float* __restrict__ coef, double* __restrict__ norm_out) {
+  if (blockIdx.x != 0 || threadIdx.x != 0) return;
+  double total = 0.0;
+  for (int i = 0; i < count; ++i) total += partials[i];  // fixed order
+  const double norm = sqrt(total);
+  double c = max_norm / (norm + 1e-6);
+  if (c > 1.0) c = 1.0;  // a NaN norm keeps a NaN coefficient
+  *coef = (float)c;
+  if (norm_out) *norm_out = norm;
+}
+
+int64_t grid_for(int64_t units, int64_t per_block) {
+  int64_t gsz = (units + per_block - 1) / per_block;
+  if (gsz > tuning().grid_cap) gsz = tuning().grid_cap;
+  return gsz < 1 ? 1 : gsz;
+}
+
+template <int NW, int CAP, typename In, bool SUMSQ, bool FIRST, bool SCALE>
+void run_accum(const void* const* rows, int world, int64_t n, float* acc, float scale,
+               double* partials, int64_t* grid_out, hipStream_t s) {
+  RowTable<CAP> t;
+  for (int i = 0; i < CAP; ++i) t.p[i] = i < world ? rows[i] : nullptr;
+  const int64_t ngroups = n / 4;
+  int64_t grid = grid_for(ngroups, (int64_t)kThreads * kAccumG);
+  if (SUMSQ && grid > max_partials(n)) grid = max_partials(n);
+  *grid_out = grid;
+  hipLaunchKernelGGL((k_accum<NW, CAP, In, SUMSQ, FIRST, SCALE>), dim3((unsigned)grid), dim3(kThreads),
+                     0, s, t, world, mean_div(world), scale, ngroups, n, acc, partials);
+}
+
+template <typename In, bool SUMSQ, bool FIRST, bool SCALE>
+void dispatch_world(const void* const* rows, int world, int64_t n, float* acc, float scale,
+                    double* partials, int64_t* grid, hipStream_t s) {
+  switch (world) {
+    case 8: run_accum<8, 8, In, SUMSQ, FIRST, SCALE>(rows, world, n, acc, scale, partials, grid, s); break;
+    case 64: run_accum<64, 64, In, SUMSQ, FIRST, SCALE>(rows, world, n, acc, scale, partials, grid, s); break;
+    default:
+      if (world <= 64) run_accum<0, 64, In, SUMSQ, FIRST, SCALE>(rows, world, n, acc, scale, partials, grid, s);
+      else run_accum<0, ZS_MAX_WORLD, In, SUMSQ, FIRST, SCALE>(rows, world, n, acc, scale, partials, grid, s);
+  }
+}
+
+template <typename In, bool SUMSQ>
+void dispatch_flags(bool first, bool scaled, bool vec, const void* const* rows, int world, int64_t n,
+                    float* acc, float scale, double* partials, int64_t* grid, hipStream_t s) {
+  if (!vec) {
+    RowTable<ZS_MAX_WORLD> t;
+    for (int i = 0; i < ZS_MAX_WORLD; ++i) t.p[i] = i < world ? rows[i] : nullptr;
+    *grid = max_partials(n);
+    const dim3 gd((unsigned)*grid), bd(kThreads);
+    const MeanDiv d = mean_div(world);
+    if (first && scaled) hipLaunchKernelGGL((k_accum_scalar<In, SUMSQ, true, true>), gd, bd, 0, s, t, world, d, scale, n, acc, partials);
+    else if (first) hipLaunchKernelGGL((k_accum_scalar<In, SUMSQ, true, false>), gd, bd, 0, s, t, world, d, scale, n, acc, partials);
+    else if (scaled) hipLaunchKernelGGL((k_accum_scalar<In, SUMSQ, false, true>), gd, bd, 0, s, t, world, d, scale, n, acc, partials);
+    else hipLaunchKernelGGL((k_accum_scalar<In, SUMSQ, false, false>), gd, bd, 0, s, t, world, d, scale, n, acc, partials);
+    return;
+  }
+  if (first && scaled) dispatch_world<In, SUMSQ, true, true>(rows, world, n, acc, scale, partials, grid, s);
+  else if (first) dispatch_world<In, SUMSQ, true, false>(rows, world, n, acc, scale, partials, grid, s);
+  else if (scaled) dispatch_world<In, SUMSQ, false, true>(rows, world, n, acc, scale, partials, grid, s);
+  else dispatch_world<In, SUMSQ, false, false>(rows, world, n, acc, scale, partials, grid, s);
+}
+
+bool al(const void* p, unsigned a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+}  // namespace
+
+hipError_t launch_accumulate(const void* const* rows, int world, int dtype, int64_t n, float* acc,
+                             float scale, bool first, double* sumsq, double* partials,
+                             hipStream_t s) {
+  int64_t grid = 0;
+  if (n > 0) {
+    bool vec = al(acc, 16);
+    for (int i = 0; i < world; ++i) vec = vec && al(rows[i], dtype == ZS_BF16 ? 8 : 16);
+    const bool scaled = scale != 1.0f;
+    if (dtype == ZS_BF16) {
+      if (sumsq) dispatch_flags<uint16_t, true>(first, scaled, vec, rows, world, n, acc, scale, partials, &grid, s);
+      else dispatch_flags<uint16_t, false>(first, scaled, vec, rows, world, n, acc, scale, partials, &grid, s);
+    } else {
+      if (sumsq) dispatch_flags<float, true>(first, scaled, vec, rows, world, n, acc, scale, partials, &grid, s);
+      else dispatch_flags<float, false>(first, scaled, vec, rows, world, n, acc, scale, partials, &grid, s);
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (sumsq) {
+    hipLaunchKernelGGL(k_sumsq_finalize2, dim3(1), dim3(kThreads), 0, s, partials, grid, sumsq);
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_accumulate_local(const void* g, int dtype, int64_t n, float* acc, bool first,
+                                   hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const bool vec = al(acc, 16) && al(g, dtype == ZS_BF16 ? 8 : 16);
+  const int64_t ngroups = n / 4;
+  const dim3 gd((unsigned)grid_for(vec ? ngroups : n, kThreads)), bd(kThreads);
+  if (dtype == ZS_BF16) {
+    if (first) hipLaunchKernelGGL((k_accum_local<uint16_t, true>), gd, bd, 0, s, static_cast<const uint16_t*>(g), ngroups, n, acc, (int)vec);
+    else hipLaunchKernelGGL((k_accum_local<uint16_t, false>), gd, bd, 0, s, static_cast<const uint16_t*>(g), ngroups, n, acc, (int)vec);
+  } else {
+    if (first) hipLaunchKernelGGL((k_accum_local<float, true>), gd, bd, 0, s, static_cast<const float*>(g), ngroups, n, acc, (int)vec);
+    else hipLaunchKernelGGL((k_accum_local<float, false>), gd, bd, 0, s, static_cast<const float*>(g), ngroups, n, acc, (int)vec);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_clip(const double* partials, int count, double max_norm, float* coef,
+                       double* norm, hipStream_t s) {
+  hipLaunchKernelGGL(k_clip, dim3(1), dim3(64), 0, s, partials, count, max_norm, coef, norm);
+  return hipGetLastError();
+}
+
+}  // namespace zs

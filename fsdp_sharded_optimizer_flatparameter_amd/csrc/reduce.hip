@@ -27,9 +27,6 @@ namespace zs {
 
 namespace {
 
-// ranks per load chunk of the double-buffered rank walk
-constexpr int kRankChunk = 8;
-
 MeanDiv mean_div(int world) {
   MeanDiv d;
   d.n = (float)world;

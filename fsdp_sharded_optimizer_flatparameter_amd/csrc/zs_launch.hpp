@@ -45,6 +45,16 @@ hipError_t launch_fused(const void* const* rows, int world, int dtype, int64_t n
                         float* m, float* v, const zs_adamw_hparams& hp, const float* scale,
                         uint16_t* out, hipStream_t s);
 
+hipError_t launch_accumulate(const void* const* rows, int world, int dtype, int64_t n, float* acc,
+                             float scale, bool first, double* sumsq, double* partials,
+                             hipStream_t s);
+
+hipError_t launch_accumulate_local(const void* g, int dtype, int64_t n, float* acc, bool first,
+                                   hipStream_t s);
+
+hipError_t launch_clip(const double* partials, int count, double max_norm, float* coef,
+                       double* norm, hipStream_t s);
+
 hipError_t launch_pack(const zs_param_desc* d_desc, int nparams, int64_t total, int src_dtype,
                        int64_t flat_begin, int64_t shard, float* master, float* m, float* v,
                        hipStream_t s);

@@ -253,6 +253,58 @@ zs_status zs_sharded_step(const void* const* rows, int32_t world, int32_t dtype,
                           const zs_adamw_hparams* hp, const float* grad_scale,
                           uint16_t* bf16_out, hipStream_t stream);
 
+/*
+ * zs_accumulate_grads -- sharded (ZeRO-2) gradient accumulation over micro-
+ * batches: reduce this micro-batch's N contributions and add the mean into the
+ * rank's fp32 accumulator ([L5] s3: ZeRO-2 reduce-scatters every micro-batch
+ * and keeps only its 1/N; [L5] s2: the fp32 buffer costs 4P/N).
+ *   rows, world, dtype, n     as zs_reduce_grads
+ *   acc[n]        DEVICE fp32 accumulator:
+ *                   first != 0:  acc = scale * mean
+ *                   first == 0:  acc = acc + scale * mean
+ *                 mean as in zs_reduce_grads (bit-identical); the product with
+ *                 scale is skipped when scale == 1 (e.g. scale = 1/K for a
+ *                 mean over K micro-batches)
+ *   sumsq_out, workspace, workspace_bytes
+ *                 optional: sum of squares of the updated acc (fp64), as in
+ *                 zs_reduce_grads -- on the last micro-batch this is the
+ *                 shard's partial of the global gradient norm
+ * Errors: those of zs_reduce_grads, ZS_ERR_HPARAM (scale not finite).
+ */
+zs_status zs_accumulate_grads(const void* const* rows, int32_t world, int32_t dtype, int64_t n,
+                              float* acc, float scale, int32_t first, double* sumsq_out,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * zs_accumulate_local -- unsharded (ZeRO-1) accumulation of one micro-batch's
+ * local gradient in fp32 ([L5] s3: ZeRO-1 sums the full local gradient and
+ * reduce-scatters once after the last micro-batch; [L5] s2: 4P per rank).
+ *   grad[n]   DEVICE gradient of `dtype` (ZS_BF16 or ZS_F32)
+ *   acc[n]    DEVICE fp32: first != 0: acc = grad (widened exactly);
+ *             first == 0: acc = acc + grad
+ * The accumulators of all ranks then go through zs_accumulate_grads (first=1,
+ * scale=1/K) or zs_reduce_grads as fp32 contributions.
+ * Errors: ZS_ERR_NULL, ZS_ERR_SIZE, ZS_ERR_DTYPE, ZS_ERR_ALIGN, ZS_ERR_OVERLAP, ZS_ERR_HIP.
+ */
+zs_status zs_accumulate_local(const void* grad, int32_t dtype, int64_t n, float* acc,
+                              int32_t first, hipStream_t stream);
+
+/*
+ * zs_clip_coefficient -- global-norm clipping factor from per-shard sums of
+ * squares ([DPZ] s6: the global norm needs every shard's partial; the combine
+ * across ranks is an all-reduce in a multi-GPU job).
+ *   partials[count]  DEVICE fp64 sums of squares (e.g. each rank's sumsq_out),
+ *                    added in index order
+ *   max_norm         the clipping threshold (finite, > 0)
+ *   coef_out         DEVICE fp32: min(1, max_norm / (sqrt(total) + 1e-6)),
+ *                    NaN if the total is NaN; pass it as grad_scale to
+ *                    zs_adamw_step
+ *   norm_out         optional DEVICE fp64: sqrt(total)
+ * Errors: ZS_ERR_NULL, ZS_ERR_SIZE (count < 1), ZS_ERR_HPARAM, ZS_ERR_ALIGN, ZS_ERR_HIP.
+ */
+zs_status zs_clip_coefficient(const double* partials, int32_t count, double max_norm,
+                              float* coef_out, double* norm_out, hipStream_t stream);
+
 /* Static, NUL-terminated name of a status code ("ZS_OK", "ZS_ERR_NULL", ...). */
 const char* zs_status_string(zs_status status);
 

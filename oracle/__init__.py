@@ -23,6 +23,8 @@ Modules:
   adamw   decoupled-decay Adam on the fp32 shard       ([L5] s3, [DPZ] s4.2)
   bf16    fp32 -> bf16 round-to-nearest-even           ([L5] s3 step 2)
   step    the composed update: reduce, AdamW, cast
+  accumulate  micro-batch accumulation (ZeRO-1 / ZeRO-2 orders), global-norm
+          clipping                                     ([L5] s2-3, [DPZ] s6)
   ledger  per-rank state and communication formulas    ([L5] s2-3, [DPZ] s3.2-3.4)
 
 Parity unpinned (no page value or closed form fixes it): the last-ulp fp32
@@ -30,4 +32,4 @@ result of AdamW under a different but algebraically equal arrangement, and the
 association order of the sum of squares. Tests accept any result within the
 stated tolerances for those.
 """
-from . import adamw, bf16, layout, ledger, reduce, step  # noqa: F401
+from . import accumulate, adamw, bf16, layout, ledger, reduce, step  # noqa: F401

@@ -205,3 +205,27 @@ def test_sharded_step_argument_errors(lib):
     assert f(_rows(8), 8, 1, 10, None, b, c, C.byref(_hp()), None, None, None) == -1
     assert f(_rows(8), 8, 1, 10, C.c_void_p(FAKE + 4), b, c, C.byref(_hp()), None, None, None) == -11
     assert f(_rows(8), 8, 1, 10, a, b, c, C.byref(_hp()), None, C.c_void_p(FAKE + 2), None) == -11
+
+
+def test_accumulate_and_clip_argument_errors(lib):
+    f = lib.zs_accumulate_grads
+    a = C.c_void_p(FAKE + (1 << 40))
+    assert f(_rows(4), 0, 1, 100, a, C.c_float(1.0), 0, None, None, 0, None) == -3
+    assert f(_rows(4), 4, 3, 100, a, C.c_float(1.0), 0, None, None, 0, None) == -5
+    assert f(_rows(4), 4, 1, 100, a, C.c_float(float("nan")), 0, None, None, 0, None) == -6
+    assert f(_rows(4), 4, 1, 100, None, C.c_float(1.0), 0, None, None, 0, None) == -1
+    assert f(_rows(4), 4, 1, 4096, a, C.c_float(1.0), 0, C.c_void_p(FAKE + (1 << 41)), None, 0, None) == -8
+    assert f(_rows(4), 4, 1, 100, C.c_void_p(FAKE + 8), C.c_float(1.0), 1, None, None, 0, None) == -11
+    g = lib.zs_accumulate_local
+    assert g(a, 2, 10, a, 0, None) == -5
+    assert g(a, 1, -1, a, 0, None) == -2
+    assert g(None, 1, 10, a, 0, None) == -1
+    assert g(C.c_void_p(FAKE + 1), 1, 10, a, 0, None) == -10
+    assert g(a, 1, 10, C.c_void_p(FAKE + (1 << 40) + 4), 0, None) == -11
+    assert g(None, 1, 0, None, 0, None) == 0
+    h = lib.zs_clip_coefficient
+    assert h(a, 0, 1.0, a, None, None) == -2
+    assert h(a, 4, 0.0, a, None, None) == -6
+    assert h(a, 4, float("inf"), a, None, None) == -6
+    assert h(None, 4, 1.0, a, None, None) == -1
+    assert h(C.c_void_p(FAKE + 4), 4, 1.0, a, None, None) == -10
