@@ -6,6 +6,7 @@ does not load the library; the first call does, and fails loudly if it has
 not been built.
 """
 from .api import (  # noqa: F401
+    Dim0Table,
     ParamTable,
     ZsArgumentError,
     ZsError,
@@ -15,8 +16,11 @@ from .api import (  # noqa: F401
     zs_cast_for_gather,
     zs_clip_coefficient,
     zs_copy_out,
+    zs_copy_out_dim0,
+    zs_dim0_layout,
     zs_flat_layout,
     zs_pack_shard,
+    zs_pack_shard_dim0,
     zs_reduce_grads,
     zs_sharded_step,
     zs_version,

@@ -25,6 +25,11 @@ class ParamDesc(C.Structure):
     _fields_ = [("ptr", C.c_void_p), ("flat_offset", C.c_int64), ("numel", C.c_int64)]
 
 
+class Dim0Desc(C.Structure):
+    _fields_ = [("ptr", C.c_void_p), ("flat_offset", C.c_int64), ("numel", C.c_int64),
+                ("chunk", C.c_int64), ("local_offset", C.c_int64)]
+
+
 class AdamWHParams(C.Structure):
     _fields_ = [("lr", C.c_double), ("beta1", C.c_double), ("beta2", C.c_double),
                 ("eps", C.c_double), ("weight_decay", C.c_double), ("step", C.c_int64)]
@@ -56,6 +61,13 @@ SIGNATURES = {
                                         C.c_void_p]),
     "zs_clip_coefficient": (C.c_int32, [C.c_void_p, C.c_int32, C.c_double, C.c_void_p, C.c_void_p,
                                         C.c_void_p]),
+    "zs_dim0_layout": (C.c_int32, [_I64P, _I64P, C.c_int32, C.c_int32, _I64P, _I64P, _I64P]),
+    "zs_check_dim0_layout": (C.c_int32, [C.POINTER(Dim0Desc), C.c_int32, C.c_int32, C.c_int64,
+                                         C.c_int64]),
+    "zs_pack_shard_dim0": (C.c_int32, [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
+                                       C.c_int64, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]),
+    "zs_copy_out_dim0": (C.c_int32, [C.c_void_p, C.c_int64, C.c_void_p, C.c_int32, C.c_int32,
+                                     C.c_int64, C.c_int64, C.c_void_p]),
     "zs_status_string": (C.c_char_p, [C.c_int32]),
     "zs_version": (C.c_int32, []),
 }

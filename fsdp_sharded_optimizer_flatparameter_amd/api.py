@@ -127,6 +127,96 @@ def zs_copy_out(gathered, table: ParamTable, stream=None):
         _stream(stream, gathered.device)))
 
 
+# ---------------------------------------------------------------- per-parameter dim-0 sharding
+
+def zs_dim0_layout(shapes, world: int):
+    """(chunks, local offsets, local total L) of per-parameter dim-0 sharding over `world` ranks.
+
+    A 0-d parameter is one row of one element.
+    """
+    n = len(shapes)
+    d0 = [int(s[0]) if len(s) else 1 for s in shapes]
+    rs = []
+    for s in shapes:
+        r = 1
+        for x in s[1:]:
+            r *= int(x)
+        rs.append(r)
+    a = (C.c_int64 * max(n, 1))(*d0)
+    b = (C.c_int64 * max(n, 1))(*rs)
+    chunk = (C.c_int64 * max(n, 1))()
+    loff = (C.c_int64 * max(n, 1))()
+    lt = C.c_int64()
+    L.check("zs_dim0_layout", _lib().zs_dim0_layout(a, b, n, int(world), chunk, loff, C.byref(lt)))
+    return list(chunk[:n]), list(loff[:n]), lt.value
+
+
+class Dim0Table:
+    """Descriptor table of one unit's parameters under dim-0 sharding over `world` ranks.
+
+    The host copy is checked by zs_check_dim0_layout; the device copy (40 bytes
+    per parameter) is what the pack and copy-out kernels read. The tensors are
+    kept referenced for the table's lifetime.
+    """
+
+    def __init__(self, tensors, world: int, device=None):
+        if len(tensors) == 0:
+            raise ValueError("a unit needs at least one parameter")
+        dtype = tensors[0].dtype
+        if dtype not in _DTYPES:
+            raise ValueError(f"unsupported parameter dtype {dtype}")
+        for i, t in enumerate(tensors):
+            _dev(t, f"param[{i}]", dtype)
+        self.tensors = list(tensors)
+        self.dtype = dtype
+        self.world = int(world)
+        self.nparams = len(tensors)
+        self.chunks, self.local_offsets, self.local_total = zs_dim0_layout(
+            [tuple(t.shape) for t in tensors], self.world)
+        self.offsets, self.total, _, _ = zs_flat_layout([t.numel() for t in tensors], 1)
+        host = (L.Dim0Desc * self.nparams)()
+        for i, t in enumerate(self.tensors):
+            host[i].ptr = t.data_ptr()
+            host[i].flat_offset = self.offsets[i]
+            host[i].numel = t.numel()
+            host[i].chunk = self.chunks[i]
+            host[i].local_offset = self.local_offsets[i]
+        L.check("zs_check_dim0_layout", _lib().zs_check_dim0_layout(
+            host, self.nparams, self.world, self.total, self.local_total))
+        device = device if device is not None else tensors[0].device
+        raw = torch.frombuffer(bytearray(bytes(host)), dtype=torch.uint8)
+        self.device_table = raw.to(device)
+        torch.cuda.current_stream(device).synchronize()  # the host staging copy is released
+
+    @property
+    def ptr(self):
+        return C.c_void_p(self.device_table.data_ptr())
+
+
+def zs_pack_shard_dim0(table: Dim0Table, rank: int, master, exp_avg=None, exp_avg_sq=None,
+                       stream=None):
+    _dev(master, "master", torch.float32)
+    if master.numel() != table.local_total:
+        raise ValueError(f"master must hold the rank's {table.local_total} elements")
+    for name, t in (("exp_avg", exp_avg), ("exp_avg_sq", exp_avg_sq)):
+        if t is not None:
+            _dev(t, name, torch.float32)
+            if t.numel() != master.numel():
+                raise ValueError(f"{name} must have the master's size")
+    L.check("zs_pack_shard_dim0", _lib().zs_pack_shard_dim0(
+        table.ptr, table.nparams, _DTYPES[table.dtype], table.world, int(rank), table.local_total,
+        _ptr(master), _ptr(exp_avg), _ptr(exp_avg_sq), _stream(stream, master.device)))
+
+
+def zs_copy_out_dim0(gathered, table: Dim0Table, stream=None):
+    _dev(gathered, "gathered", torch.bfloat16)
+    if table.dtype != torch.bfloat16:
+        raise ValueError("copy-out destinations must be bf16")
+    L.check("zs_copy_out_dim0", _lib().zs_copy_out_dim0(
+        _ptr(gathered), gathered.numel(), table.ptr, table.nparams, table.world, table.total,
+        table.local_total, _stream(stream, gathered.device)))
+
+
 # ---------------------------------------------------------------- reduce / AdamW / cast
 
 def _rows(rows, n):

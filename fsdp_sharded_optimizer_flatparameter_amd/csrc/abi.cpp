@@ -211,6 +211,85 @@ zs_status zs_copy_out(const uint16_t* gathered, int64_t gathered_numel, const zs
   return hip_status(zs::launch_copy_out(gathered, d_desc, nparams, total_numel, stream));
 }
 
+zs_status zs_dim0_layout(const int64_t* dim0, const int64_t* rowsize, int32_t nparams, int32_t world,
+                         int64_t* chunk_out, int64_t* local_offsets_out, int64_t* local_total_out) {
+  if (nparams < 0) return ZS_ERR_SIZE;
+  if (world < 1) return ZS_ERR_WORLD;
+  if (nparams > 0 && (!dim0 || !rowsize)) return ZS_ERR_NULL;
+  int64_t t = 0;
+  for (int32_t i = 0; i < nparams; ++i) {
+    if (dim0[i] < 0 || rowsize[i] < 0) return ZS_ERR_SIZE;
+    const int64_t rows = dim0[i] / world + (dim0[i] % world != 0);
+    if (rowsize[i] > 0 && rows > INT64_MAX / world / rowsize[i]) return ZS_ERR_SIZE;
+    const int64_t c = rows * rowsize[i];
+    if (c > INT64_MAX - t) return ZS_ERR_SIZE;
+    if (chunk_out) chunk_out[i] = c;
+    if (local_offsets_out) local_offsets_out[i] = t;
+    t += c;
+  }
+  if (local_total_out) *local_total_out = t;
+  return ZS_OK;
+}
+
+zs_status zs_check_dim0_layout(const zs_dim0_desc* host_desc, int32_t nparams, int32_t world,
+                               int64_t total, int64_t local_total) {
+  if (nparams < 0 || total < 0 || local_total < 0) return ZS_ERR_SIZE;
+  if (world < 1) return ZS_ERR_WORLD;
+  if (nparams == 0) return total == 0 && local_total == 0 ? ZS_OK : ZS_ERR_LAYOUT;
+  if (!host_desc) return ZS_ERR_NULL;
+  int64_t run = 0, lrun = 0;
+  for (int32_t i = 0; i < nparams; ++i) {
+    const zs_dim0_desc& d = host_desc[i];
+    if (d.numel < 0 || d.chunk < 0) return ZS_ERR_SIZE;
+    if (d.flat_offset != run || d.local_offset != lrun) return ZS_ERR_LAYOUT;
+    if (d.numel > 0 && !d.ptr) return ZS_ERR_NULL;
+    // the N chunks must cover the parameter: numel <= world * chunk
+    if (d.chunk < d.numel / world + (d.numel % world != 0)) return ZS_ERR_LAYOUT;
+    if (d.numel > INT64_MAX - run || d.chunk > INT64_MAX - lrun) return ZS_ERR_SIZE;
+    run += d.numel;
+    lrun += d.chunk;
+  }
+  if (lrun > INT64_MAX / world) return ZS_ERR_SIZE;
+  return run == total && lrun == local_total ? ZS_OK : ZS_ERR_LAYOUT;
+}
+
+zs_status zs_pack_shard_dim0(const zs_dim0_desc* d_desc, int32_t nparams, int32_t src_dtype,
+                             int32_t world, int32_t rank, int64_t local_total, float* master,
+                             float* exp_avg, float* exp_avg_sq, hipStream_t stream) {
+  if (nparams < 0 || local_total < 0) return ZS_ERR_SIZE;
+  if (nparams == 0 && local_total != 0) return ZS_ERR_SIZE;
+  if (world < 1) return ZS_ERR_WORLD;
+  if (rank < 0 || rank >= world) return ZS_ERR_RANK;
+  if (src_dtype != ZS_F32 && src_dtype != ZS_BF16) return ZS_ERR_DTYPE;
+  if (local_total == 0) return ZS_OK;
+  if (!master || !d_desc) return ZS_ERR_NULL;
+  if (!aligned(master, 4) || (exp_avg && !aligned(exp_avg, 4)) ||
+      (exp_avg_sq && !aligned(exp_avg_sq, 4)) || !aligned(d_desc, 8))
+    return ZS_ERR_ALIGN;
+  const int64_t b = local_total * 4;
+  if (overlaps(master, b, exp_avg, exp_avg ? b : 0) ||
+      overlaps(master, b, exp_avg_sq, exp_avg_sq ? b : 0) ||
+      overlaps(exp_avg, exp_avg ? b : 0, exp_avg_sq, exp_avg_sq ? b : 0))
+    return ZS_ERR_OVERLAP;
+  return hip_status(zs::launch_pack_dim0(d_desc, nparams, src_dtype, rank, local_total, master,
+                                         exp_avg, exp_avg_sq, stream));
+}
+
+zs_status zs_copy_out_dim0(const uint16_t* gathered, int64_t gathered_numel,
+                           const zs_dim0_desc* d_desc, int32_t nparams, int32_t world,
+                           int64_t total, int64_t local_total, hipStream_t stream) {
+  if (nparams < 0 || total < 0 || local_total < 0 || gathered_numel < 0) return ZS_ERR_SIZE;
+  if (world < 1) return ZS_ERR_WORLD;
+  if (nparams == 0 && (total != 0 || local_total != 0)) return ZS_ERR_SIZE;
+  if (local_total > INT64_MAX / world || world * local_total > gathered_numel) return ZS_ERR_SIZE;
+  if (total > world * local_total) return ZS_ERR_SIZE;
+  if (total == 0) return ZS_OK;
+  if (!gathered || !d_desc) return ZS_ERR_NULL;
+  if (!aligned(gathered, 2) || !aligned(d_desc, 8)) return ZS_ERR_ALIGN;
+  return hip_status(
+      zs::launch_copy_out_dim0(gathered, d_desc, nparams, total, local_total, stream));
+}
+
 zs_status zs_sharded_step(const void* const* rows, int32_t world, int32_t dtype, int64_t n,
                           float* master, float* exp_avg, float* exp_avg_sq,
                           const zs_adamw_hparams* hp, const float* grad_scale,

@@ -1,6 +1,9 @@
 // FlatParameter pack (per-parameter tensors -> the rank's fp32 master slice)
 // and unshard copy-out (gathered flat bf16 buffer -> per-parameter tensors).
 //
+// Also the per-parameter dim-0 variants ("Lesson 5: ZeRO and FSDP" s7.2 and
+// Fig. 5-5: each parameter sharded on dim 0; "03 - FSDP (ZeRO-3)" s4).
+//
 // Pages: "Lesson 5: ZeRO and FSDP" s7.1 point 1 (all parameters of a wrapped
 // unit flattened into one 1-D tensor that is split along DP; contiguous slice
 // views of the gathered tensor become the parameters) and point 3 (tail
@@ -170,6 +173,103 @@ __global__ __launch_bounds__(kThreads) void k_copy_out(const uint16_t* __restric
   }
 }
 
+// ---- per-parameter dim-0 sharding ------------------------------------------------
+
+// Largest p with key(p) <= f over a table sorted by that key.
+template <typename Key>
+__device__ __forceinline__ int find_by(const int64_t* key_lds, bool use_lds, int nparams, int64_t f,
+                                       Key key) {
+  int lo = 0, hi = nparams - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    const int64_t o = use_lds ? key_lds[mid] : key(mid);
+    if (o <= f) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ int64_t valid_part(const zs_dim0_desc& d, int rank) {
+  const int64_t v = d.numel - (int64_t)rank * d.chunk;
+  return v < 0 ? 0 : (v > d.chunk ? d.chunk : v);
+}
+
+// Rank r's shard: for each parameter its rows [r*c, (r+1)*c), zero past dim 0.
+template <typename Src>
+__global__ __launch_bounds__(kThreads) void k_pack_dim0(const zs_dim0_desc* __restrict__ desc,
+                                                        int nparams, int rank, int64_t local_total,
+                                                        float* __restrict__ master,
+                                                        float* __restrict__ m,
+                                                        float* __restrict__ v) {
+  __shared__ int64_t key[kLdsParams];
+  __shared__ int s_lo, s_hi;
+  const bool use_lds = nparams <= kLdsParams;
+  if (use_lds)
+    for (int i = threadIdx.x; i < nparams; i += kThreads) key[i] = desc[i].local_offset;
+  __syncthreads();
+  auto lkey = [&](int i) { return desc[i].local_offset; };
+  for (int64_t k0 = (int64_t)blockIdx.x * kChunk; k0 < local_total; k0 += (int64_t)gridDim.x * kChunk) {
+    const int64_t k1 = k0 + kChunk < local_total ? k0 + kChunk : local_total;
+    if (m) zero_f32(m + k0, k1 - k0);
+    if (v) zero_f32(v + k0, k1 - k0);
+    if (threadIdx.x == 0) s_lo = find_by(key, use_lds, nparams, k0, lkey);
+    if (threadIdx.x == 64) s_hi = find_by(key, use_lds, nparams, k1 - 1, lkey);
+    __syncthreads();
+    const int lo = __builtin_amdgcn_readfirstlane(s_lo), hi = __builtin_amdgcn_readfirstlane(s_hi);
+    __syncthreads();
+    for (int p = lo; p <= hi; ++p) {
+      const zs_dim0_desc d = desc[p];
+      const int64_t a = k0 > d.local_offset ? k0 : d.local_offset;
+      const int64_t b = k1 < d.local_offset + d.chunk ? k1 : d.local_offset + d.chunk;
+      if (a >= b) continue;
+      const int64_t ja = a - d.local_offset, jb = b - d.local_offset;  // within the chunk
+      const int64_t val = valid_part(d, rank);
+      const int64_t je = jb < val ? jb : val;  // real rows end
+      if (ja < je)
+        seg_to_f32<Src>(static_cast<const Src*>(d.ptr) + (int64_t)rank * d.chunk + ja, master + a, je - ja);
+      const int64_t z0 = ja > val ? ja : val;  // padding rows
+      if (z0 < jb) zero_f32(master + d.local_offset + z0, jb - z0);
+    }
+  }
+}
+
+// Full parameters from the rank-major gathered buffer [N * L].
+__global__ __launch_bounds__(kThreads) void k_copy_out_dim0(const uint16_t* __restrict__ gathered,
+                                                            const zs_dim0_desc* __restrict__ desc,
+                                                            int nparams, int64_t total,
+                                                            int64_t local_total) {
+  __shared__ int64_t key[kLdsParams];
+  __shared__ int s_lo, s_hi;
+  const bool use_lds = nparams <= kLdsParams;
+  if (use_lds)
+    for (int i = threadIdx.x; i < nparams; i += kThreads) key[i] = desc[i].flat_offset;
+  __syncthreads();
+  auto fkey = [&](int i) { return desc[i].flat_offset; };
+  for (int64_t f0 = (int64_t)blockIdx.x * kChunk; f0 < total; f0 += (int64_t)gridDim.x * kChunk) {
+    const int64_t fe = f0 + kChunk < total ? f0 + kChunk : total;
+    if (threadIdx.x == 0) s_lo = find_by(key, use_lds, nparams, f0, fkey);
+    if (threadIdx.x == 64) s_hi = find_by(key, use_lds, nparams, fe - 1, fkey);
+    __syncthreads();
+    const int lo = __builtin_amdgcn_readfirstlane(s_lo), hi = __builtin_amdgcn_readfirstlane(s_hi);
+    __syncthreads();
+    for (int p = lo; p <= hi; ++p) {
+      const zs_dim0_desc d = desc[p];
+      const int64_t a = f0 > d.flat_offset ? f0 : d.flat_offset;
+      const int64_t b = fe < d.flat_offset + d.numel ? fe : d.flat_offset + d.numel;
+      if (a >= b) continue;
+      int64_t e = a - d.flat_offset;
+      const int64_t e1 = b - d.flat_offset;
+      while (e < e1) {  // split at rank boundaries: each piece is contiguous on both sides
+        const int64_t r = e / d.chunk;
+        const int64_t end = (r + 1) * d.chunk < e1 ? (r + 1) * d.chunk : e1;
+        seg_bf16(gathered + r * local_total + d.local_offset + (e - r * d.chunk),
+                 static_cast<uint16_t*>(d.ptr) + e, end - e);
+        e = end;
+      }
+    }
+  }
+}
+
 int64_t grid_for(int64_t elems) {
   int64_t gsz = (elems + kChunk - 1) / kChunk;
   if (gsz > tuning().grid_cap) gsz = tuning().grid_cap;
@@ -189,6 +289,25 @@ hipError_t launch_pack(const zs_param_desc* d_desc, int nparams, int64_t total, 
   else
     hipLaunchKernelGGL((k_pack<float>), gd, bd, 0, s, d_desc, nparams, total, flat_begin, shard,
                        master, m, v);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_dim0(const zs_dim0_desc* d_desc, int nparams, int src_dtype, int rank,
+                            int64_t local_total, float* master, float* m, float* v, hipStream_t s) {
+  if (local_total == 0) return hipSuccess;
+  const dim3 gd((unsigned)grid_for(local_total)), bd(kThreads);
+  if (src_dtype == ZS_BF16)
+    hipLaunchKernelGGL((k_pack_dim0<uint16_t>), gd, bd, 0, s, d_desc, nparams, rank, local_total, master, m, v);
+  else
+    hipLaunchKernelGGL((k_pack_dim0<float>), gd, bd, 0, s, d_desc, nparams, rank, local_total, master, m, v);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_out_dim0(const uint16_t* gathered, const zs_dim0_desc* d_desc, int nparams,
+                                int64_t total, int64_t local_total, hipStream_t s) {
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_copy_out_dim0, dim3((unsigned)grid_for(total)), dim3(kThreads), 0, s, gathered,
+                     d_desc, nparams, total, local_total);
   return hipGetLastError();
 }
 

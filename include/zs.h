@@ -305,6 +305,77 @@ zs_status zs_accumulate_local(const void* grad, int32_t dtype, int64_t n, float*
 zs_status zs_clip_coefficient(const double* partials, int32_t count, double max_norm,
                               float* coef_out, double* norm_out, hipStream_t stream);
 
+/*
+ * Per-parameter dim-0 sharding (FSDP2 Shard(0); [L5] s7.2 and Fig. 5-5: each
+ * parameter keeps its shape and is split on dim 0, a rank holding [H/N, D];
+ * [FZ3] s4: DTensor sharded on dim 0, batched all-gather). A parameter with d0
+ * rows of `rowsize` elements gives each rank c = ceil(d0/N) rows, rank r
+ * holding rows [r*c, min((r+1)*c, d0)) zero-padded to c rows. A rank's shard
+ * of a unit (also the all-gather input) is its padded chunks concatenated in
+ * registration order, L elements; the all-gather output is the N shards one
+ * after the other (N * L elements).
+ *
+ *   ptr           device address of the full parameter (C order)
+ *   flat_offset   offset of the parameter in the unsharded unit (prefix sum of numels)
+ *   numel         elements of the parameter (d0 * rowsize)
+ *   chunk         elements per rank: ceil(d0 / N) * rowsize
+ *   local_offset  offset of the parameter's chunk inside a rank's shard
+ */
+typedef struct zs_dim0_desc {
+  void* ptr;
+  int64_t flat_offset;
+  int64_t numel;
+  int64_t chunk;
+  int64_t local_offset;
+} zs_dim0_desc;
+
+/*
+ * zs_dim0_layout -- per-parameter chunk sizes and the rank-shard layout (host only).
+ *   dim0[nparams], rowsize[nparams]  HOST arrays (a 0-d parameter: dim0 = rowsize = 1)
+ *   chunk_out[nparams]               receives ceil(dim0/N) * rowsize (may be NULL)
+ *   local_offsets_out[nparams]       receives the chunk offsets in a rank's shard (may be NULL)
+ *   local_total_out                  receives L (may be NULL)
+ * Errors: ZS_ERR_NULL, ZS_ERR_SIZE (negative or overflowing sizes), ZS_ERR_WORLD.
+ */
+zs_status zs_dim0_layout(const int64_t* dim0, const int64_t* rowsize, int32_t nparams, int32_t world,
+                         int64_t* chunk_out, int64_t* local_offsets_out, int64_t* local_total_out);
+
+/*
+ * zs_check_dim0_layout -- verify a HOST table: flat offsets tile [0, total),
+ * local offsets tile [0, local_total) with the chunk sizes, numel <= world *
+ * chunk, and non-empty parameters have storage. Returns ZS_OK or
+ * ZS_ERR_NULL / ZS_ERR_SIZE / ZS_ERR_WORLD / ZS_ERR_LAYOUT.
+ */
+zs_status zs_check_dim0_layout(const zs_dim0_desc* host_desc, int32_t nparams, int32_t world,
+                               int64_t total, int64_t local_total);
+
+/*
+ * zs_pack_shard_dim0 -- rank r's fp32 master shard under dim-0 sharding
+ * (padding rows +0.0), with optional zeroed Adam moments.
+ *   d_desc[nparams]  DEVICE table (see zs_dim0_desc); parameters hold src_dtype
+ *   local_total      L; master, exp_avg, exp_avg_sq hold L fp32 elements (DEVICE)
+ * The AdamW, cast and fused-step entry points apply to the shard unchanged.
+ * Errors: ZS_ERR_NULL, ZS_ERR_SIZE, ZS_ERR_WORLD, ZS_ERR_RANK, ZS_ERR_DTYPE,
+ * ZS_ERR_ALIGN, ZS_ERR_OVERLAP, ZS_ERR_HIP.
+ */
+zs_status zs_pack_shard_dim0(const zs_dim0_desc* d_desc, int32_t nparams, int32_t src_dtype,
+                             int32_t world, int32_t rank, int64_t local_total, float* master,
+                             float* exp_avg, float* exp_avg_sq, hipStream_t stream);
+
+/*
+ * zs_copy_out_dim0 -- unshard under dim-0 sharding: every parameter's rows
+ * from the N ranks' regions of the gathered bf16 buffer (padding rows
+ * dropped). A real scatter: parameter i's rows [r*c, ...) come from
+ * gathered[r*L + local_offset_i ...].
+ *   gathered[gathered_numel]  DEVICE bf16, gathered_numel >= world * local_total
+ *   d_desc[nparams]           DEVICE table of bf16 destinations
+ *   total                     T of the unit (sum of numels)
+ * Errors: ZS_ERR_NULL, ZS_ERR_SIZE, ZS_ERR_WORLD, ZS_ERR_ALIGN, ZS_ERR_HIP.
+ */
+zs_status zs_copy_out_dim0(const uint16_t* gathered, int64_t gathered_numel,
+                           const zs_dim0_desc* d_desc, int32_t nparams, int32_t world,
+                           int64_t total, int64_t local_total, hipStream_t stream);
+
 /* Static, NUL-terminated name of a status code ("ZS_OK", "ZS_ERR_NULL", ...). */
 const char* zs_status_string(zs_status status);
 

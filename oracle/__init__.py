@@ -25,6 +25,7 @@ Modules:
   step    the composed update: reduce, AdamW, cast
   accumulate  micro-batch accumulation (ZeRO-1 / ZeRO-2 orders), global-norm
           clipping                                     ([L5] s2-3, [DPZ] s6)
+  dim0    per-parameter dim-0 sharding and copy-out     ([L5] s7.2, [FZ3] s4)
   ledger  per-rank state and communication formulas    ([L5] s2-3, [DPZ] s3.2-3.4)
 
 Parity unpinned (no page value or closed form fixes it): the last-ulp fp32
@@ -32,4 +33,4 @@ result of AdamW under a different but algebraically equal arrangement, and the
 association order of the sum of squares. Tests accept any result within the
 stated tolerances for those.
 """
-from . import accumulate, adamw, bf16, layout, ledger, reduce, step  # noqa: F401
+from . import accumulate, adamw, bf16, dim0, layout, ledger, reduce, step  # noqa: F401

@@ -29,7 +29,7 @@ def lib():
 def _declared():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(zs_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(zs_[a-z0-9_]+)\s*\(", text)))
 
 
 def _defines():
@@ -229,3 +229,100 @@ def test_accumulate_and_clip_argument_errors(lib):
     assert h(a, 4, float("inf"), a, None, None) == -6
     assert h(None, 4, 1.0, a, None, None) == -1
     assert h(C.c_void_p(FAKE + 4), 4, 1.0, a, None, None) == -10
+
+
+# ---------------------------------------------------------------- per-parameter dim-0 sharding
+
+def _dim0_c(lib, shp_list, world):
+    n = len(shp_list)
+    d0 = [s[0] if len(s) else 1 for s in shp_list]
+    rs = [int(np.prod(s[1:])) if len(s) > 1 else 1 for s in shp_list]
+    a = (C.c_int64 * max(n, 1))(*d0)
+    b = (C.c_int64 * max(n, 1))(*rs)
+    ch, lo, lt = (C.c_int64 * max(n, 1))(), (C.c_int64 * max(n, 1))(), C.c_int64()
+    st = lib.zs_dim0_layout(a, b, n, world, ch, lo, C.byref(lt))
+    return st, list(ch[:n]), list(lo[:n]), lt.value
+
+
+def test_dim0_layout_matches_oracle(lib):
+    from oracle import dim0 as odim0
+    rng = np.random.default_rng(11)
+    cases = [[shp for _, shp in f()] for f in (shapes.tiny, shapes.tiny_ragged, shapes.gpt2_small,
+                                                shapes.llama3_8b, shapes.llama_70b)]
+    cases += [[(), (0, 4), (5,), (1, 1, 1)]]
+    cases += [[tuple(int(x) for x in rng.integers(0, 9, size=int(rng.integers(1, 4))))
+               for _ in range(int(rng.integers(1, 6)))] for _ in range(200)]
+    for shp in cases:
+        for world in (1, 2, 3, 4, 7, 8, 64, 256):
+            st, ch, lo, lt = _dim0_c(lib, shp, world)
+            ref = odim0.dim0_layout(shp, world)
+            assert st == 0
+            assert (ch, lo, lt) == (list(ref.chunk), list(ref.local_offsets), ref.local_total)
+
+
+def test_dim0_layout_errors(lib):
+    assert _dim0_c(lib, [(4, 2)], 0)[0] == -3
+    a = (C.c_int64 * 1)(-1)
+    b = (C.c_int64 * 1)(2)
+    assert lib.zs_dim0_layout(a, b, 1, 2, None, None, None) == -2
+    a = (C.c_int64 * 2)(2 ** 40, 2 ** 40)
+    b = (C.c_int64 * 2)(2 ** 22, 2 ** 22)
+    assert lib.zs_dim0_layout(a, b, 2, 1, None, None, None) == -2  # int64 overflow
+    assert lib.zs_dim0_layout(None, None, 1, 2, None, None, None) == -1
+    lt = C.c_int64(7)
+    assert lib.zs_dim0_layout(None, None, 0, 2, None, None, C.byref(lt)) == 0 and lt.value == 0
+
+
+def _dtable(entries):
+    arr = (L.Dim0Desc * len(entries))()
+    for i, (ptr, off, n, c, lo) in enumerate(entries):
+        arr[i].ptr, arr[i].flat_offset, arr[i].numel, arr[i].chunk, arr[i].local_offset = \
+            ptr, off, n, c, lo
+    return arr
+
+
+def test_check_dim0_layout(lib):
+    ok = _dtable([(0x1000, 0, 10, 6, 0), (0x2000, 10, 0, 0, 6), (0x3000, 10, 7, 4, 6)])
+    f = lib.zs_check_dim0_layout
+    assert f(ok, 3, 2, 17, 10) == 0
+    assert f(ok, 3, 2, 18, 10) == -9
+    assert f(ok, 3, 2, 17, 11) == -9
+    assert f(ok, 3, 1, 17, 10) == -9       # one rank cannot hold 10 elements in a chunk of 6
+    assert f(ok, 3, 0, 17, 10) == -3
+    assert f(_dtable([(0x1000, 0, 10, 4, 0)]), 1, 2, 10, 4) == -9      # 2 * 4 < 10
+    assert f(_dtable([(0x1000, 0, 10, 5, 1)]), 1, 2, 10, 6) == -9      # local offset gap
+    assert f(_dtable([(0x1000, 1, 10, 5, 0)]), 1, 2, 11, 5) == -9      # flat offset gap
+    assert f(_dtable([(None, 0, 4, 2, 0)]), 1, 2, 4, 2) == -1
+    assert f(_dtable([(None, 0, 0, 3, 0)]), 1, 2, 0, 3) == 0   # empty params need no storage
+    assert f(_dtable([(0x1000, 0, -1, 2, 0)]), 1, 2, -1, 2) == -2
+    assert f(None, 0, 2, 0, 0) == 0
+    assert f(None, 0, 2, 0, 1) == -9
+
+
+def test_dim0_pack_copy_out_errors(lib):
+    d = C.c_void_p(FAKE + (1 << 36))
+    mm = C.c_void_p(FAKE + (1 << 38))
+    p = lib.zs_pack_shard_dim0
+    assert p(d, 2, 0, 0, 0, 10, mm, None, None, None) == -3
+    assert p(d, 2, 0, 4, 4, 10, mm, None, None, None) == -4
+    assert p(d, 2, 0, 4, -1, 10, mm, None, None, None) == -4
+    assert p(d, 2, 9, 4, 0, 10, mm, None, None, None) == -5
+    assert p(d, 2, 0, 4, 0, -1, mm, None, None, None) == -2
+    assert p(d, 0, 0, 4, 0, 10, mm, None, None, None) == -2
+    assert p(d, 2, 0, 4, 0, 10, None, None, None, None) == -1
+    assert p(None, 2, 0, 4, 0, 10, mm, None, None, None) == -1
+    assert p(d, 2, 0, 4, 0, 10, C.c_void_p(FAKE + 2), None, None, None) == -10
+    assert p(d, 2, 0, 4, 0, 10, mm, C.c_void_p(FAKE + (1 << 38) + 36), None, None) == -11
+    assert p(d, 2, 0, 4, 0, 0, None, None, None, None) == 0
+
+    g = C.c_void_p(FAKE)
+    c = lib.zs_copy_out_dim0
+    assert c(g, 39, d, 2, 4, 30, 10, None) == -2   # 4 ranks x L=10 do not fit in 39
+    assert c(g, 40, d, 2, 4, 41, 10, None) == -2   # unit longer than N * L
+    assert c(g, 40, d, 2, 0, 30, 10, None) == -3
+    assert c(g, 40, d, -1, 4, 30, 10, None) == -2
+    assert c(g, 40, d, 0, 4, 30, 10, None) == -2
+    assert c(None, 40, d, 2, 4, 30, 10, None) == -1
+    assert c(g, 40, None, 2, 4, 30, 10, None) == -1
+    assert c(C.c_void_p(FAKE + 1), 40, d, 2, 4, 30, 10, None) == -10
+    assert c(g, 40, d, 0, 4, 0, 0, None) == 0

@@ -1,0 +1,167 @@
+"""GPU parity of per-parameter dim-0 sharding (FSDP2 Shard(0)): pack and unshard
+copy-out, bit-exact against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import fsdp_sharded_optimizer_flatparameter_amd as zs
+from oracle import bf16 as obf16
+from oracle import dim0 as odim0
+from synth import gen, shapes
+from _gpu import bits32, host
+
+pytestmark = pytest.mark.gpu
+
+
+def _params(shape_list, seed, dtype=torch.float32):
+    g = gen.device_generator(seed)
+    return [gen.device_normal(g, shapes.numel(s), gen.THETA_SIGMA, dtype).reshape(s)
+            for _, s in shape_list]
+
+
+def _pack(table, rank):
+    master = torch.full((table.local_total,), float("nan"), device="cuda")
+    m = torch.full_like(master, 3.0)
+    v = torch.full_like(master, 3.0)
+    zs.zs_pack_shard_dim0(table, rank, master, m, v)
+    torch.cuda.synchronize()
+    return host(master), host(m), host(v)
+
+
+@pytest.mark.parametrize("name,world", [("tiny", 4), ("tiny_ragged", 3), ("tiny_ragged", 4),
+                                        ("tiny_ragged", 7), ("tiny_ragged", 16), ("gpt2", 8),
+                                        ("gpt2", 5)])
+def test_pack_dim0_matches_oracle(name, world):
+    shp = shapes.WORKLOADS[name][0]()
+    params = _params(shp, seed=sum(map(ord, name)) + 3 * world)
+    hp = [host(p) for p in params]
+    table = zs.Dim0Table(params, world)
+    ranks = range(world) if name != "gpt2" else (0, world // 2, world - 1)
+    for r in ranks:
+        master, m, v = _pack(table, r)
+        want = odim0.shard_dim0(hp, world, r)
+        assert np.array_equal(bits32(master), bits32(want)), (name, world, r)
+        assert not bits32(m).any() and not bits32(v).any()
+
+
+def test_pack_dim0_gpt2_embedding_padding_rows():
+    # 50257 vocabulary rows over 8 ranks: 6283 rows each, the last rank holds 6276
+    # real rows and 7 rows of +0.0 padding
+    shp = shapes.gpt2_small()
+    assert shp[0][1] == (50257, 768)
+    params = _params(shp, seed=5)
+    table = zs.Dim0Table(params, 8)
+    master, _, _ = _pack(table, 7)
+    c = table.chunks[0]
+    assert c == 6283 * 768
+    emb = host(params[0]).ravel()
+    assert np.array_equal(bits32(master[:6276 * 768]), bits32(emb[7 * c:]))
+    assert not bits32(master[6276 * 768:c]).any()
+
+
+def test_pack_dim0_bf16_sources_and_odd_rows():
+    shp = shapes.tiny_ragged() + [("e", (1000,)), ("f", (9, 9)), ("g", (3, 1, 5)), ("h", (1,))]
+    params = _params(shp, seed=12, dtype=torch.bfloat16)
+    hp = [host(p) for p in params]
+    for world in (1, 2, 5, 9):
+        table = zs.Dim0Table(params, world)
+        for r in range(world):
+            master, _, _ = _pack(table, r)
+            want = odim0.shard_dim0([obf16.from_bf16_bits(x) for x in hp], world, r)
+            assert np.array_equal(bits32(master), bits32(want)), (world, r)
+
+
+def _copy_out_case(shape_list, seed, world):
+    dst = [torch.full(s, float("nan"), device="cuda", dtype=torch.bfloat16) for _, s in shape_list]
+    table = zs.Dim0Table(dst, world)
+    g = gen.device_generator(seed)
+    gathered = gen.device_normal(g, world * table.local_total, 1.0, torch.bfloat16)
+    zs.zs_copy_out_dim0(gathered, table)
+    torch.cuda.synchronize()
+    want = odim0.copy_out_dim0(host(gathered), [s for _, s in shape_list], world)
+    for i, (d, w) in enumerate(zip(dst, want)):
+        assert np.array_equal(host(d), w), (world, i)
+
+
+@pytest.mark.parametrize("name,world", [("tiny_ragged", 3), ("tiny_ragged", 4), ("tiny_ragged", 16),
+                                        ("tiny", 4), ("gpt2", 8), ("gpt2", 7)])
+def test_copy_out_dim0_matches_oracle(name, world):
+    _copy_out_case(shapes.WORKLOADS[name][0](), seed=21 + world, world=world)
+
+
+def test_copy_out_dim0_misaligned_chunks():
+    # odd row sizes and row counts put most rank pieces off the 16-byte grid
+    shp = [(f"p{i}", s) for i, s in enumerate([(1,), (3, 3), (5,), (7, 11), (9, 1), (4097,),
+                                               (13, 631), (2, 2), (16384,), (65537,), (1, 1)])]
+    for world in (3, 8, 64):
+        _copy_out_case(shp, seed=22, world=world)
+
+
+def test_copy_out_dim0_llama8b_block_full():
+    _copy_out_case(shapes.llama3_8b_block(), seed=23, world=8)
+
+
+def test_roundtrip_dim0_pack_cast_gather_copy_out():
+    # with lr = wd = 0 theta is unchanged, so the unsharded parameters come back
+    # as the bf16 rounding of the originals, bit for bit; every padding row
+    # gathers as +0
+    shp = shapes.gpt2_small()
+    world = 6
+    params = _params(shp, seed=31)
+    table = zs.Dim0Table(params, world)
+    lt = table.local_total
+    gather = torch.empty(world * lt, device="cuda", dtype=torch.bfloat16)
+    zero_g = torch.zeros(lt, device="cuda")
+    for r in range(world):
+        master = torch.empty(lt, device="cuda")
+        m = torch.empty_like(master)
+        v = torch.empty_like(master)
+        zs.zs_pack_shard_dim0(table, r, master, m, v)
+        zs.zs_adamw_step(master, m, v, zero_g, step=1, lr=0.0, beta1=0.9, beta2=0.999, eps=1e-8,
+                         weight_decay=0.0, bf16_out=gather[r * lt:(r + 1) * lt])
+    dst = [torch.empty(s, device="cuda", dtype=torch.bfloat16) for _, s in shp]
+    zs.zs_copy_out_dim0(gather, zs.Dim0Table(dst, world))
+    torch.cuda.synchronize()
+    for d, p in zip(dst, params):
+        assert np.array_equal(host(d).ravel(), obf16.to_bf16_bits(host(p).ravel()))
+    gh = host(gather)
+    for r in range(world):
+        for c, lo, p in zip(table.chunks, table.local_offsets, params):
+            val = odim0.valid(p.numel(), c, r)
+            assert not gh[r * lt + lo + val:r * lt + lo + c].any()
+
+
+def test_dim0_llama8b_full_pack_and_copy_out():
+    # the whole 8B list as bf16 parameters at N = 8 (every rank piece is whole
+    # rows): rank 7's shard against the oracle parameter by parameter on a
+    # sample, and the copy-out of a gathered buffer on the same sample
+    shp = shapes.llama3_8b()
+    world = 8
+    g = gen.device_generator(43)
+    params = [gen.device_normal(g, shapes.numel(s), gen.THETA_SIGMA, torch.bfloat16).reshape(s)
+              for _, s in shp]
+    table = zs.Dim0Table(params, world)
+    rng = np.random.default_rng(1)
+    sample = sorted({0, 1, 2, 9, len(shp) - 2, len(shp) - 1} |
+                    {int(x) for x in rng.integers(0, len(shp), size=8)})
+    master = torch.empty(table.local_total, device="cuda")
+    zs.zs_pack_shard_dim0(table, world - 1, master)
+    torch.cuda.synchronize()
+    for i in sample:
+        lo, c = table.local_offsets[i], table.chunks[i]
+        want = odim0.shard_dim0([obf16.from_bf16_bits(host(params[i]))], world, world - 1)
+        assert np.array_equal(bits32(host(master[lo:lo + c])), bits32(want)), i
+    del master
+    gathered = gen.device_normal(g, world * table.local_total, 1.0, torch.bfloat16)
+    for p in params:
+        p.fill_(float("nan"))
+    zs.zs_copy_out_dim0(gathered, table)
+    torch.cuda.synchronize()
+    lt = table.local_total
+    for i in sample:
+        lo, c = table.local_offsets[i], table.chunks[i]
+        pieces = np.concatenate([host(gathered[r * lt + lo:r * lt + lo + c]) for r in range(world)])
+        want = odim0.copy_out_dim0(pieces, [shp[i][1]], world)[0]
+        assert np.array_equal(host(params[i]), want), i
+    del gathered, params, table
+    torch.cuda.empty_cache()
