@@ -11,7 +11,7 @@ Reported value: shard elements updated per second (Gelem/s).
 
 Also measured (in "parts"): the same update as two launches (reduce, then AdamW
 with the fused cast), each kernel alone, the unshard copy-out of one Llama-3-8B
-decoder block, and the pack of the shard. The JSON line carries the roofline of
+decoder block (flat and dim-0 sharded), and the pack of the shard. The JSON line carries the roofline of
 the dominant kernel (HIP-event time on the launch stream) and the CPU oracle
 timed on a bounded sample of the same inputs.
 """
@@ -227,7 +227,16 @@ def main() -> int:
         gbs = 4 * sum(bn) / (t_co * 1e-3) / 1e9
         parts["copy_out_llama8b_block"] = dict(ms=round(t_co, 5), elems=sum(bn), bytes_per_elem=4,
                                                gb_s=round(gbs, 1), frac_of_peak=round(gbs / PEAK_HBM_GBS, 4))
-        del gathered_blk, dst, table
+        # the same block under per-parameter dim-0 sharding over 8 ranks (a scatter
+        # from 8 rank regions of the gather buffer)
+        dtable = zs.Dim0Table(dst, 8)
+        gathered_d0 = gen.device_normal(g0, 8 * dtable.local_total, 1.0, torch.bfloat16, dev)
+        t_cd = event_time_ms(lambda i: zs.zs_copy_out_dim0(gathered_d0, dtable), 10, stream)
+        gbs = 4 * sum(bn) / (t_cd * 1e-3) / 1e9
+        parts["copy_out_dim0_llama8b_block_n8"] = dict(
+            ms=round(t_cd, 5), elems=sum(bn), bytes_per_elem=4, gb_s=round(gbs, 1),
+            frac_of_peak=round(gbs / PEAK_HBM_GBS, 4))
+        del gathered_blk, gathered_d0, dst, table, dtable
 
         # pack of this shard from per-parameter fp32 tensors (one-time setup work);
         # a single 7.5e9-element parameter is represented by the rank's slice of it
