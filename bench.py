@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of one rank's sharded ZeRO/FSDP update on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload 7p5b|llama8b|gpt2|tiny]
+    python bench.py [--steps K] [--warmup W] [--workload 7p5b|llama8b|70b|gpt2|tiny]
 
 A step is the rank's shard update: the mean of N bf16 gradient contributions,
 fused AdamW on the fp32 master/m/v shard, and the bf16 copy into the rank's
@@ -9,9 +9,16 @@ slot of the all-gather buffer -- one launch of the single-pass kernel
 (zs_sharded_step). Inputs are synthetic and resident in HBM before timing.
 Reported value: shard elements updated per second (Gelem/s).
 
+The 70B shard (fp32 contributions, 64 x 4.4 GB of rows) does not fit in HBM
+whole: it is updated in 8 equal chunks, one launch each, with one chunk's worth
+of rows (35 GB) serving every chunk; a step is the 8 launches.
+
 Also measured (in "parts"): the same update as two launches (reduce, then AdamW
-with the fused cast), each kernel alone, the unshard copy-out of one Llama-3-8B
-decoder block (flat and dim-0 sharded), and the pack of the shard. The JSON line carries the roofline of
+with the fused cast), each kernel alone, the clipped update (reduce with its sum
+of squares, clip coefficient, AdamW with the gradient scale), fp32 gradient
+accumulation in the ZeRO-2 and ZeRO-1 orders, the unshard copy-out of one
+decoder block (flat and dim-0 sharded), the dim-0 pack of that block, and the
+pack of the shard. The JSON line carries the roofline of
 the dominant kernel (HIP-event time on the launch stream) and the CPU oracle
 timed on a bounded sample of the same inputs.
 """
@@ -38,6 +45,9 @@ WORKLOADS = {
                  desc="7.5B flat parameters, N=64 simulated ranks, rank 63's shard"),
     "llama8b": dict(shapes="llama3_8b", world=8, rank=7, wd=0.01,
                     desc="Llama-3-8B parameter list, N=8 simulated ranks, rank 7's shard"),
+    "70b": dict(shapes="llama_70b", world=64, rank=63, wd=0.01, rows="f32", chunks=8,
+                desc="70B parameter list (Llama-3 70B shapes), N=64 simulated ranks, rank 63's shard, "
+                     "fp32 contributions, 8 chunks"),
     "gpt2": dict(shapes="gpt2_small", world=8, rank=7, wd=0.01,
                  desc="GPT-2-small parameter list, N=8 simulated ranks, rank 7's shard"),
     "tiny": dict(shapes="tiny", world=4, rank=3, wd=0.01,
@@ -139,32 +149,47 @@ def main() -> int:
     hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=wl["wd"])
 
     # ---- inputs, resident in HBM before any timing
+    row_dtype = torch.float32 if wl.get("rows") == "f32" else torch.bfloat16
+    row_bytes = 4 if row_dtype == torch.float32 else 2
+    csize = -(-S // wl.get("chunks", 1))
+    ranges = [(a, min(S, a + csize)) for a in range(0, S, csize)]
     g0 = gen.device_generator(1000 + sorted(WORKLOADS).index(args.workload), dev)
-    rows = [gen.device_normal(g0, S, gen.GRAD_SIGMA, torch.bfloat16, dev) for _ in range(world)]
+    rows = [gen.device_normal(g0, csize, gen.GRAD_SIGMA, row_dtype, dev) for _ in range(world)]
     theta = gen.device_normal(g0, S, gen.THETA_SIGMA, None, dev)
     m = torch.zeros(S, device=dev)
     v = torch.zeros(S, device=dev)
-    gather = torch.empty(padded, device=dev, dtype=torch.bfloat16)
-    slot = gather[rank * S:(rank + 1) * S]
+    if len(ranges) == 1:
+        gather = torch.empty(padded, device=dev, dtype=torch.bfloat16)
+        slot = gather[rank * S:(rank + 1) * S]
+    else:  # the 70B gather buffer (141 GB) is not needed to time the rank's slot
+        slot = torch.empty(S, device=dev, dtype=torch.bfloat16)
     gbuf = torch.empty(S, device=dev)
     torch.cuda.synchronize()
 
+    def rows_for(a, b):
+        return rows if b - a == csize else [r[:b - a] for r in rows]
+
     # bit-identical host copies of the oracle's sample (taken before any update)
     win = 1 << 20
-    nwin = max(1, min(args.cpu_windows, S // win)) if not args.no_cpu_baseline else 0
+    nwin = max(1, min(args.cpu_windows, csize // win)) if not args.no_cpu_baseline else 0
     rng = np.random.default_rng(0)
-    starts = sorted(int(x) for x in rng.choice(max(1, S // win), size=nwin, replace=False)) if nwin else []
+    starts = sorted(int(x) for x in rng.choice(max(1, csize // win), size=nwin, replace=False)) if nwin else []
     cpu_inputs = []
     for s0 in starts:
-        a, b = s0 * win, min(S, s0 * win + win)
-        r_h = np.stack([r[a:b].view(torch.int16).cpu().numpy().view(np.uint16) for r in rows])
+        a, b = s0 * win, min(csize, s0 * win + win)
+        if row_dtype == torch.bfloat16:
+            r_h = np.stack([r[a:b].view(torch.int16).cpu().numpy().view(np.uint16) for r in rows])
+        else:
+            r_h = np.stack([r[a:b].cpu().numpy() for r in rows])
         cpu_inputs.append((r_h, theta[a:b].cpu().numpy(), m[a:b].cpu().numpy(), v[a:b].cpu().numpy()))
 
     step_no = [0]
 
     def fused_step(_i):
         step_no[0] += 1
-        zs.zs_sharded_step(rows, theta, m, v, step=step_no[0], bf16_out=slot, **hp)
+        for a, b in ranges:
+            zs.zs_sharded_step(rows_for(a, b), theta[a:b], m[a:b], v[a:b], step=step_no[0],
+                               bf16_out=slot[a:b], **hp)
 
     if args.calibrate_copy:
         src = torch.ones(1 << 28, device=dev)
@@ -173,21 +198,24 @@ def main() -> int:
         torch.cuda.synchronize()
         del src, dst
 
-    # ---- the step: warmup, then exactly K timed steps between synchronisations
+    # ---- the step: warmup, then exactly K timed steps between synchronisations;
+    # an event between steps gives the per-step spread
     for i in range(args.warmup):
         fused_step(i)
     torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    marks[0].record(stream)
     for i in range(args.steps):
         fused_step(i)
-    end.record(stream)
+        marks[i + 1].record(stream)
     torch.cuda.synchronize()
-    ms_step = start.elapsed_time(end) / args.steps
+    ms_step = marks[0].elapsed_time(marks[-1]) / args.steps
+    per_step = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
+    spread = dict(median=round(per_step[len(per_step) // 2], 5), min=round(per_step[0], 5),
+                  max=round(per_step[-1], 5)) if per_step else None
     gelem = S / (ms_step * 1e-3) / 1e9
 
-    n_rows_bytes = 2 * world
+    n_rows_bytes = row_bytes * world
     fused_bpe = n_rows_bytes + 26          # rows + read theta,m,v + write theta,m,v + bf16
     reduce_bpe = n_rows_bytes + 4          # rows + write g
     adamw_bpe = 30                         # read g,theta,m,v + write theta,m,v + bf16
@@ -198,13 +226,28 @@ def main() -> int:
     traffic = read_traffic(args.workload, kernel_name, src_hash)
 
     parts = {}
+    copy_gbs = None
+    if not args.no_parts and not args.calibrate_copy:
+        # a plain device copy (the runtime's copy kernel) of 2 GiB as a practical ceiling
+        src = torch.ones(1 << 29, device=dev)
+        dst = torch.empty_like(src)
+        t_copy = event_time_ms(lambda i: dst.copy_(src), 10, stream)
+        copy_gbs = 2 * src.numel() * 4 / (t_copy * 1e-3) / 1e9
+        del src, dst
     if not args.no_parts:
         iters = max(10, args.steps)
-        t_reduce = event_time_ms(lambda i: zs.zs_reduce_grads(rows, gbuf), iters, stream)
+
+        def reduce_call(i):
+            for a, b in ranges:
+                zs.zs_reduce_grads(rows_for(a, b), gbuf[a:b])
+
+        t_reduce = event_time_ms(reduce_call, iters, stream)
 
         def adamw_call(i):
             step_no[0] += 1
-            zs.zs_adamw_step(theta, m, v, gbuf, step=step_no[0], bf16_out=slot, **hp)
+            for a, b in ranges:
+                zs.zs_adamw_step(theta[a:b], m[a:b], v[a:b], gbuf[a:b], step=step_no[0],
+                                 bf16_out=slot[a:b], **hp)
 
         t_adamw = event_time_ms(adamw_call, iters, stream)
         t_cast = event_time_ms(lambda i: zs.zs_cast_for_gather(theta, slot), iters, stream)
@@ -215,32 +258,87 @@ def main() -> int:
             gbs = bpe * S / (t * 1e-3) / 1e9
             parts[name] = dict(ms=round(t, 5), bytes_per_elem=bpe, gb_s=round(gbs, 1),
                                frac_of_peak=round(gbs / PEAK_HBM_GBS, 4))
-        del gbuf
 
-        # unshard copy-out of one Llama-3-8B decoder block (218,112,000 elements)
-        blk = shapes.llama3_8b_block()
+        def put(name, t, bpe, elems=S):
+            gbs = bpe * elems / (t * 1e-3) / 1e9
+            parts[name] = dict(ms=round(t, 5), elems=elems, bytes_per_elem=bpe, gb_s=round(gbs, 1),
+                               frac_of_peak=round(gbs / PEAK_HBM_GBS, 4))
+
+        # global-norm clipping: the reduce also returns the fp64 sum of squares of its
+        # output, the clip coefficient combines the shards' partials (here the N
+        # simulated ranks' copies of this one), and AdamW takes it as a gradient scale
+        ws = torch.empty(zs.zs_workspace_bytes(csize), device=dev, dtype=torch.uint8)
+        partials = torch.zeros(world, device=dev, dtype=torch.float64)
+        coef = torch.empty(1, device=dev)
+
+        def reduce_sumsq_call(i):
+            for j, (a, b) in enumerate(ranges):
+                zs.zs_reduce_grads(rows_for(a, b), gbuf[a:b], sumsq_out=partials[j:j + 1], workspace=ws)
+
+        t_rs = event_time_ms(reduce_sumsq_call, iters, stream)
+        put("reduce_sumsq", t_rs, reduce_bpe)
+
+        def clipped_call(i):
+            step_no[0] += 1
+            reduce_sumsq_call(i)
+            zs.zs_clip_coefficient(partials, 1.0, coef)
+            for a, b in ranges:
+                zs.zs_adamw_step(theta[a:b], m[a:b], v[a:b], gbuf[a:b], step=step_no[0],
+                                 grad_scale=coef, bf16_out=slot[a:b], **hp)
+
+        put("clipped_step", event_time_ms(clipped_call, iters, stream), reduce_bpe + adamw_bpe)
+
+        # fp32 gradient accumulation over micro-batches. ZeRO-2 order: every
+        # micro-batch's N contributions are reduced and added into the fp32 shard
+        # (gbuf serves as the accumulator). ZeRO-1 order: each rank adds its whole
+        # local bf16 gradient into a full-size fp32 buffer; timed on S elements of it.
+        def accum_call(i):
+            for a, b in ranges:
+                zs.zs_accumulate_grads(rows_for(a, b), gbuf[a:b], scale=0.25)
+
+        put("accumulate_zero2", event_time_ms(accum_call, iters, stream), n_rows_bytes + 8)
+        local = rows[0][:min(csize, S)]
+        lacc = gbuf[:local.numel()]
+        put("accumulate_zero1_local", event_time_ms(lambda i: zs.zs_accumulate_local(local, lacc), iters,
+                                                    stream), row_bytes + 8, local.numel())
+        del gbuf, ws, partials, coef, lacc
+
+        # unshard copy-out of one decoder block: Llama-3-8B's (218,112,000 elements), or
+        # the 70B model's (855,654,400) for that workload
+        big = args.workload == "70b"
+        blk = shapes.llama_70b_block() if big else shapes.llama3_8b_block()
+        blk_name, blk_world = ("70b_block", 64) if big else ("llama8b_block", 8)
         bn = shapes.numels(blk)
         gathered_blk = gen.device_normal(g0, sum(bn), 1.0, torch.bfloat16, dev)
         dst = [torch.empty(s, device=dev, dtype=torch.bfloat16) for _, s in blk]
         table = zs.ParamTable(dst)
         t_co = event_time_ms(lambda i: zs.zs_copy_out(gathered_blk, table), 10, stream)
         gbs = 4 * sum(bn) / (t_co * 1e-3) / 1e9
-        parts["copy_out_llama8b_block"] = dict(ms=round(t_co, 5), elems=sum(bn), bytes_per_elem=4,
+        parts[f"copy_out_{blk_name}"] = dict(ms=round(t_co, 5), elems=sum(bn), bytes_per_elem=4,
                                                gb_s=round(gbs, 1), frac_of_peak=round(gbs / PEAK_HBM_GBS, 4))
-        # the same block under per-parameter dim-0 sharding over 8 ranks (a scatter
-        # from 8 rank regions of the gather buffer)
-        dtable = zs.Dim0Table(dst, 8)
-        gathered_d0 = gen.device_normal(g0, 8 * dtable.local_total, 1.0, torch.bfloat16, dev)
+        # the same block under per-parameter dim-0 sharding (a scatter from the N rank
+        # regions of the gather buffer)
+        dtable = zs.Dim0Table(dst, blk_world)
+        gathered_d0 = gen.device_normal(g0, blk_world * dtable.local_total, 1.0, torch.bfloat16, dev)
         t_cd = event_time_ms(lambda i: zs.zs_copy_out_dim0(gathered_d0, dtable), 10, stream)
         gbs = 4 * sum(bn) / (t_cd * 1e-3) / 1e9
-        parts["copy_out_dim0_llama8b_block_n8"] = dict(
+        parts[f"copy_out_dim0_{blk_name}_n{blk_world}"] = dict(
             ms=round(t_cd, 5), elems=sum(bn), bytes_per_elem=4, gb_s=round(gbs, 1),
             frac_of_peak=round(gbs / PEAK_HBM_GBS, 4))
         del gathered_blk, gathered_d0, dst, table, dtable
+        # dim-0 pack of the last rank's shard of the same block from fp32 parameters
+        src32 = [gen.device_normal(g0, shapes.numel(s), gen.THETA_SIGMA, None, dev).reshape(s) for _, s in blk]
+        ptab = zs.Dim0Table(src32, blk_world)
+        L = ptab.local_total
+        pm, pmm, pvv = (torch.empty(L, device=dev) for _ in range(3))
+        t_pd = event_time_ms(lambda i: zs.zs_pack_shard_dim0(ptab, blk_world - 1, pm, pmm, pvv), 10, stream)
+        put(f"pack_dim0_{blk_name}_n{blk_world}", t_pd, 16, L)
+        del src32, ptab, pm, pmm, pvv
 
         # pack of this shard from per-parameter fp32 tensors (one-time setup work);
-        # a single 7.5e9-element parameter is represented by the rank's slice of it
-        if args.workload == "7p5b":
+        # a single 7.5e9-element parameter, or the 70B list (282 GB of fp32
+        # parameters), is represented by the rank's slice of it
+        if args.workload in ("7p5b", "70b"):
             src = [gen.device_normal(g0, S, gen.THETA_SIGMA, None, dev)]
             ptable, pworld, prank = zs.ParamTable(src), 1, 0
         else:
@@ -269,7 +367,8 @@ def main() -> int:
         cpu_s = time.process_time() - c0
         cpu = {"value": round(done / wall / 1e9, 6), "unit": "Gelem/s",
                "cores": max(1, round(cpu_s / wall)), "kind": "oracle",
-               "sample": f"{len(cpu_inputs)} windows of {win} shard elements x {world} bf16 rows "
+               "sample": f"{len(cpu_inputs)} windows of {win} shard elements x {world} "
+                         f"{'fp32' if row_bytes == 4 else 'bf16'} rows "
                          f"(the GPU's own inputs), fp64 NumPy oracle: exact mean, AdamW, bf16 cast; "
                          f"{wall:.1f} s wall"}
 
@@ -281,6 +380,7 @@ def main() -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
+        "step_ms": spread,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -291,7 +391,8 @@ def main() -> int:
             "shard_elems": S,
             "world": world,
             "rank": rank,
-            "contributions": "bf16",
+            "contributions": "fp32" if row_bytes == 4 else "bf16",
+            "launches_per_step": len(ranges),
             "step": "mean of N contributions + AdamW (fp32 master/m/v) + bf16 cast, one pass",
             "adamw": hp,
         },
@@ -304,6 +405,8 @@ def main() -> int:
             "frac": round(achieved / PEAK_HBM_GBS, 4),
             "algorithmic_bytes_per_elem": fused_bpe,
             "traffic": traffic,
+            "copy_ceiling_gb_s": round(copy_gbs, 1) if copy_gbs else None,
+            "frac_of_copy_ceiling": round(achieved / copy_gbs, 4) if copy_gbs else None,
         },
         "cpu_baseline": cpu,
         "parts": parts,

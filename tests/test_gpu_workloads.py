@@ -167,3 +167,14 @@ def test_70b_fp32_contributions_chunk():
     _full_size_case((1 << 24) + 3, 64, "f32", step=2, moments=True, slot_offset=0, seed=7000,
                     windows=4, width=32768)
     torch.cuda.empty_cache()
+
+
+def test_70b_fp32_contributions_bench_chunk():
+    # one of the eight equal chunks the 70B shard is updated in (1,102,401,664 / 8
+    # = 137,800,208 elements; 64 fp32 rows of it are 35.3 GB)
+    lay = olayout.flat_layout(shapes.numels(shapes.llama_70b()), 64)
+    chunk = -(-lay.shard // 8)
+    assert chunk == 137_800_208
+    _full_size_case(chunk, 64, "f32", step=4, moments=True, slot_offset=0, seed=7100,
+                    windows=4, width=65536)
+    torch.cuda.empty_cache()
