@@ -91,12 +91,15 @@ def read_traffic(workload: str, kernel: str, src_hash: str):
         return None
 
 
-def event_time_ms(fn, iters: int, stream) -> float:
-    """Average ms per call of fn over `iters` calls, HIP events on `stream`."""
+def event_time_ms(fn, iters: int, stream, warmup: int = 2) -> float:
+    """Average ms per call of fn over `iters` calls after `warmup` untimed ones,
+    HIP events on `stream`."""
     import torch
 
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
+    for i in range(warmup):
+        fn(-1 - i)
     torch.cuda.synchronize()
     start.record(stream)
     for i in range(iters):

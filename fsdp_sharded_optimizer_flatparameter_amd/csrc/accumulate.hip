@@ -18,8 +18,6 @@
 namespace zs {
 namespace {
 
-constexpr int kAccumG = 4;  // groups per lane; their previous sums are loaded before the walk
-
 MeanDiv mean_div(int world) {
   MeanDiv d;
   d.n = (float)world;
@@ -28,39 +26,48 @@ MeanDiv mean_div(int world) {
   return d;
 }
 
-template <int NW, int CAP, typename In, bool SUMSQ, bool FIRST, bool SCALE>
+// G groups per lane (G*1024 consecutive elements per workgroup pass), in three
+// steps: the previous sums of all G groups are loaded into lane-private LDS
+// slots, the rank walk adds each group's scaled mean into its slot, and the G
+// results are written back as one burst of 16-byte stores. The row walk then
+// runs without a write stream beside it, and the LDS reservation caps the
+// workgroups resident per CU.
+template <int NW, int CAP, int G, typename In, bool SUMSQ, bool FIRST, bool SCALE>
 __global__ __launch_bounds__(kThreads) void k_accum(RowTable<CAP> rows, int world, MeanDiv div,
                                                     float scale, int64_t ngroups, int64_t n,
                                                     float* __restrict__ acc,
                                                     double* __restrict__ partials) {
   using L = Lanes<In>;
-  constexpr int G = kAccumG;
+  extern __shared__ f32x4 slot[];  // G * kThreads lane-private slots
   const int nw = NW > 0 ? NW : world;
   const int64_t span = (int64_t)kThreads * G;
   double ss = 0.0;
-  __shared__ f32x4 old[G * kThreads];  // each lane's previous sums (lane-private slots)
   for (int64_t base = (int64_t)blockIdx.x * span; base < ngroups; base += (int64_t)gridDim.x * span) {
     if (!FIRST) {
 #pragma unroll
       for (int k = 0; k < G; ++k) {
         const int64_t qq = base + (int64_t)k * kThreads + threadIdx.x;
         const int64_t q = qq < ngroups ? qq : ngroups - 1;
-        old[k * kThreads + threadIdx.x] = ld_nt(reinterpret_cast<const f32x4*>(acc) + q);
+        slot[k * kThreads + threadIdx.x] = ld_nt(reinterpret_cast<const f32x4*>(acc) + q);
       }
     }
     rank_sums_streamed<In, 8, G, CAP>(rows, nw, base, ngroups, [&](int k, const float* s) {
       const int64_t qq = base + (int64_t)k * kThreads + threadIdx.x;
-      if (qq >= ngroups) return;
       f32x4 o;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         float u = div(s[e]);
         if (SCALE) u *= scale;
-        o[e] = FIRST ? u : old[k * kThreads + threadIdx.x][e] + u;
-        if (SUMSQ) ss = fma((double)o[e], (double)o[e], ss);
+        o[e] = FIRST ? u : slot[k * kThreads + threadIdx.x][e] + u;
+        if (SUMSQ && qq < ngroups) ss = fma((double)o[e], (double)o[e], ss);
       }
-      st_nt(o, reinterpret_cast<f32x4*>(acc) + qq);
+      slot[k * kThreads + threadIdx.x] = o;
     });
+    for (int k = 0; k < G; ++k) {  // each lane writes back only its own slots
+      const int64_t qq = base + (int64_t)k * kThreads + threadIdx.x;
+      if (qq >= ngroups) break;
+      st_nt(slot[k * kThreads + threadIdx.x], reinterpret_cast<f32x4*>(acc) + qq);
+    }
   }
   if (blockIdx.x == 0) {  // ragged tail
     for (int64_t i = ngroups * 4 + threadIdx.x; i < n; i += kThreads) {
@@ -163,17 +170,25 @@ int64_t grid_for(int64_t units, int64_t per_block) {
   return gsz < 1 ? 1 : gsz;
 }
 
+// Measured on MI355X: 16 groups per lane (64 KiB of LDS, two workgroups per
+// CU) with many contributions, as for the reduce; 4 groups with few.
 template <int NW, int CAP, typename In, bool SUMSQ, bool FIRST, bool SCALE>
 void run_accum(const void* const* rows, int world, int64_t n, float* acc, float scale,
                double* partials, int64_t* grid_out, hipStream_t s) {
   RowTable<CAP> t;
   for (int i = 0; i < CAP; ++i) t.p[i] = i < world ? rows[i] : nullptr;
   const int64_t ngroups = n / 4;
-  int64_t grid = grid_for(ngroups, (int64_t)kThreads * kAccumG);
+  const int g = world >= 16 ? 16 : 4;
+  int64_t grid = grid_for(ngroups, (int64_t)kThreads * g);
   if (SUMSQ && grid > max_partials(n)) grid = max_partials(n);
   *grid_out = grid;
-  hipLaunchKernelGGL((k_accum<NW, CAP, In, SUMSQ, FIRST, SCALE>), dim3((unsigned)grid), dim3(kThreads),
-                     0, s, t, world, mean_div(world), scale, ngroups, n, acc, partials);
+  const size_t lds = (size_t)g * kThreads * sizeof(f32x4);
+  if (g == 16)
+    hipLaunchKernelGGL((k_accum<NW, CAP, 16, In, SUMSQ, FIRST, SCALE>), dim3((unsigned)grid),
+                       dim3(kThreads), lds, s, t, world, mean_div(world), scale, ngroups, n, acc, partials);
+  else
+    hipLaunchKernelGGL((k_accum<NW, CAP, 4, In, SUMSQ, FIRST, SCALE>), dim3((unsigned)grid),
+                       dim3(kThreads), lds, s, t, world, mean_div(world), scale, ngroups, n, acc, partials);
 }
 
 template <typename In, bool SUMSQ, bool FIRST, bool SCALE>

@@ -52,8 +52,8 @@ __global__ __launch_bounds__(kThreads) void k_fused(RowTable<CAP> rows, int worl
       for (int e = 0; e < 4; ++e) gv[e] = SCALE ? div(acc[e]) * sc : div(acc[e]);
       gl[k * kThreads + threadIdx.x] = gv;
     });
-    // phase 2, double-buffered: group k+1's state loads are in flight while
-    // group k is updated and stored
+    // phase 2: with bf16 contributions double-buffered (group k+1's state loads
+    // are in flight while group k is updated and stored)
     auto qidx = [&](int k) { return base + (int64_t)k * kThreads + threadIdx.x; };
     auto load = [&](int k, f32x4& T, f32x4& M, f32x4& W) {
       const int64_t q = qidx(k) < ngroups ? qidx(k) : ngroups - 1;
@@ -79,15 +79,25 @@ __global__ __launch_bounds__(kThreads) void k_fused(RowTable<CAP> rows, int worl
       if (CAST)
         st_nt(u32x2{pack_bf16x2(T[0], T[1]), pack_bf16x2(T[2], T[3])}, reinterpret_cast<u32x2*>(out) + qq);
     };
-    f32x4 T0, M0, W0, T1, M1, W1;
-    load(0, T0, M0, W0);
+    if constexpr (sizeof(In) == 4) {
+      // fp32 contributions: all G groups' state loads are issued before the
+      // first update (measured 2% faster than two in flight at N=64)
+      f32x4 T[G], M[G], W[G];
+#pragma unroll
+      for (int k = 0; k < G; ++k) load(k, T[k], M[k], W[k]);
+#pragma unroll
+      for (int k = 0; k < G; ++k) update(k, T[k], M[k], W[k]);
+    } else {
+      f32x4 T0, M0, W0, T1, M1, W1;
+      load(0, T0, M0, W0);
 #pragma unroll 1
-    for (int k = 0; k < G; k += 2) {
-      if (k + 1 < G) load(k + 1, T1, M1, W1);
-      update(k, T0, M0, W0);
-      if (k + 1 >= G) break;
-      if (k + 2 < G) load(k + 2, T0, M0, W0);
-      update(k + 1, T1, M1, W1);
+      for (int k = 0; k < G; k += 2) {
+        if (k + 1 < G) load(k + 1, T1, M1, W1);
+        update(k, T0, M0, W0);
+        if (k + 1 >= G) break;
+        if (k + 2 < G) load(k + 2, T0, M0, W0);
+        update(k + 1, T1, M1, W1);
+      }
     }
   }
   if (blockIdx.x == 0) {  // ragged tail (fewer than 4 elements)

@@ -165,11 +165,14 @@ hipError_t dispatch_world(const void* const* rows, int world, int64_t n, float* 
 }
 
 // Measured on MI355X: deep staging (16 groups, 64 KiB) pays off when the
-// rank walk is long; with few contributions direct stores are as fast.
+// rank walk is long; with few contributions direct stores are fastest, except
+// with the sum of squares, whose partials-per-workgroup bound then caps the grid
+// of one-group workgroups (4 staged groups measured 5% faster there).
 template <typename In>
 hipError_t dispatch_shape(const void* const* rows, int world, int64_t n, float* g,
                           double* partials, int64_t* grid, hipStream_t s) {
-  const int gsel = tuning().reduce_g > 0 ? tuning().reduce_g : (world >= 16 ? 16 : 1);
+  const int gsel = tuning().reduce_g > 0 ? tuning().reduce_g
+                                         : (world >= 16 ? 16 : (partials ? 4 : 1));
   const bool c4 = tuning().rank_chunk == 4;
   switch (gsel) {
     case 16:
