@@ -114,7 +114,7 @@ zs_status zs_check_layout(const zs_param_desc* host_desc, int32_t nparams, int64
 
 size_t zs_workspace_bytes(int64_t n) {
   if (n < 0) return 0;
-  return (size_t)zs::max_partials(n) * sizeof(double);
+  return (size_t)(zs::max_partials(n) + zs::kFinalizeBlocks) * sizeof(double);
 }
 
 zs_status zs_pack_shard(const zs_param_desc* d_desc, int32_t nparams, int64_t total_numel,

@@ -112,16 +112,6 @@ __global__ __launch_bounds__(kThreads) void k_accum_scalar(RowTable<ZS_MAX_WORLD
   }
 }
 
-__global__ __launch_bounds__(kThreads) void k_sumsq_finalize2(const double* __restrict__ partials,
-                                                              int64_t count,
-                                                              double* __restrict__ out) {
-  double s = 0.0;
-  for (int64_t i = threadIdx.x; i < count; i += kThreads) s += partials[i];
-  __shared__ double lds[kThreads / 64];
-  const double b = block_sum_fixed(s, lds);
-  if (threadIdx.x == 0) *out = b;
-}
-
 template <typename In, bool FIRST>
 __global__ __launch_bounds__(kThreads) void k_accum_local(const In* __restrict__ g, int64_t ngroups,
                                                           int64_t n, float* __restrict__ acc,
@@ -246,10 +236,7 @@ hipError_t launch_accumulate(const void* const* rows, int world, int dtype, int6
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (sumsq) {
-    hipLaunchKernelGGL(k_sumsq_finalize2, dim3(1), dim3(kThreads), 0, s, partials, grid, sumsq);
-    return hipGetLastError();
-  }
+  if (sumsq) return launch_sumsq_finalize(partials, grid, sumsq, s);
   return hipSuccess;
 }
 

@@ -115,15 +115,18 @@ __global__ __launch_bounds__(kThreads) void k_reduce_scalar(RowTable<ZS_MAX_WORL
   }
 }
 
-// Sum of the per-workgroup partials in a fixed order (deterministic).
+// Sum of partials[b*per, min((b+1)*per, count)) in a fixed order into
+// out[b] (deterministic for a given count).
 __global__ __launch_bounds__(kThreads) void k_sumsq_finalize(const double* __restrict__ partials,
-                                                             int64_t count,
+                                                             int64_t count, int64_t per,
                                                              double* __restrict__ out) {
+  const int64_t a = (int64_t)blockIdx.x * per;
+  const int64_t e = a + per < count ? a + per : count;
   double s = 0.0;
-  for (int64_t i = threadIdx.x; i < count; i += kThreads) s += partials[i];
+  for (int64_t i = a + threadIdx.x; i < e; i += kThreads) s += partials[i];
   __shared__ double lds[kThreads / 64];
   const double b = block_sum_fixed(s, lds);
-  if (threadIdx.x == 0) *out = b;
+  if (threadIdx.x == 0) out[blockIdx.x] = b;
 }
 
 template <int NW, int CAP, int G, int C, typename In>
@@ -165,14 +168,11 @@ hipError_t dispatch_world(const void* const* rows, int world, int64_t n, float* 
 }
 
 // Measured on MI355X: deep staging (16 groups, 64 KiB) pays off when the
-// rank walk is long; with few contributions direct stores are fastest, except
-// with the sum of squares, whose partials-per-workgroup bound then caps the grid
-// of one-group workgroups (4 staged groups measured 5% faster there).
+// rank walk is long; with few contributions direct stores are as fast.
 template <typename In>
 hipError_t dispatch_shape(const void* const* rows, int world, int64_t n, float* g,
                           double* partials, int64_t* grid, hipStream_t s) {
-  const int gsel = tuning().reduce_g > 0 ? tuning().reduce_g
-                                         : (world >= 16 ? 16 : (partials ? 4 : 1));
+  const int gsel = tuning().reduce_g > 0 ? tuning().reduce_g : (world >= 16 ? 16 : 1);
   const bool c4 = tuning().rank_chunk == 4;
   switch (gsel) {
     case 16:
@@ -221,11 +221,22 @@ hipError_t launch_reduce(const void* const* rows, int world, int dtype, int64_t 
     }
   }
   if (err != hipSuccess) return err;
-  if (sumsq) {
-    hipLaunchKernelGGL(k_sumsq_finalize, dim3(1), dim3(kThreads), 0, s, partials, grid, sumsq);
-    err = hipGetLastError();
-  }
+  if (sumsq) err = launch_sumsq_finalize(partials, grid, sumsq, s);
   return err;
+}
+
+hipError_t launch_sumsq_finalize(double* partials, int64_t count, double* out, hipStream_t s) {
+  if (count <= 16 * kThreads) {
+    hipLaunchKernelGGL(k_sumsq_finalize, dim3(1), dim3(kThreads), 0, s, partials, count, count, out);
+    return hipGetLastError();
+  }
+  const int64_t per = (count + kFinalizeBlocks - 1) / kFinalizeBlocks;
+  const int64_t blocks = (count + per - 1) / per;  // <= kFinalizeBlocks
+  double* second = partials + count;
+  hipLaunchKernelGGL(k_sumsq_finalize, dim3((unsigned)blocks), dim3(kThreads), 0, s, partials, count,
+                     per, second);
+  hipLaunchKernelGGL(k_sumsq_finalize, dim3(1), dim3(kThreads), 0, s, second, blocks, blocks, out);
+  return hipGetLastError();
 }
 
 }  // namespace zs

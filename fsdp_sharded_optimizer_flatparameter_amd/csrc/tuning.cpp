@@ -34,8 +34,9 @@ const Tuning& tuning() {
 
 int64_t max_partials(int64_t n) {
   // every sum-of-squares launch uses at most one workgroup per 1024 elements
+  // (one tile), up to the hard grid cap beyond which launches grid-stride
   const int64_t b = (n + 1023) / 1024;
-  const int64_t kMax = 65536;
+  const int64_t kMax = int64_t(1) << 22;
   return b < 1 ? 1 : (b > kMax ? kMax : b);
 }
 

@@ -29,6 +29,14 @@ const Tuning& tuning();
 // Largest number of per-workgroup partial sums a sum-of-squares launch over n
 // elements writes; the workspace holds that many doubles.
 int64_t max_partials(int64_t n);
+// Second-level partials the sum-of-squares finalize may use, stored after the
+// first-level ones in the caller's workspace.
+constexpr int64_t kFinalizeBlocks = 256;
+
+// Deterministic fp64 sum of partials[0, count) into *out: one workgroup for a
+// short list, else kFinalizeBlocks workgroups over fixed contiguous ranges
+// (their sums go to partials[count, count + kFinalizeBlocks)) and a second pass.
+hipError_t launch_sumsq_finalize(double* partials, int64_t count, double* out, hipStream_t s);
 
 AdamConsts adam_consts(const zs_adamw_hparams& hp);
 

@@ -182,7 +182,10 @@ zs_status zs_reduce_grads(const void* const* rows, int32_t world, int32_t dtype,
                           float* grad_out, double* sumsq_out, void* workspace,
                           size_t workspace_bytes, hipStream_t stream);
 
-/* Bytes of workspace zs_reduce_grads / zs_sharded_step need for a sum of squares over n elements. */
+/* Bytes of workspace zs_reduce_grads / zs_accumulate_grads need for a sum of
+ * squares over n elements: one fp64 partial per 1024-element tile (at most 2^22
+ * of them) plus 256 second-level partials; 0 for n < 0. The contents need no
+ * initialisation and are overwritten by every call that takes a sum of squares. */
 size_t zs_workspace_bytes(int64_t n);
 
 /*

@@ -110,10 +110,12 @@ def test_check_layout(lib):
 
 
 def test_workspace_bytes(lib):
-    assert lib.zs_workspace_bytes(0) == 8
-    assert lib.zs_workspace_bytes(1024) == 8
-    assert lib.zs_workspace_bytes(1025) == 16
-    assert lib.zs_workspace_bytes(117_187_500) == 8 * 65536
+    # one fp64 partial per 1024-element tile (at most 2^22), plus 256 second-level partials
+    assert lib.zs_workspace_bytes(0) == 8 * (1 + 256)
+    assert lib.zs_workspace_bytes(1024) == 8 * (1 + 256)
+    assert lib.zs_workspace_bytes(1025) == 8 * (2 + 256)
+    assert lib.zs_workspace_bytes(117_187_500) == 8 * (114_441 + 256)
+    assert lib.zs_workspace_bytes(1 << 40) == 8 * ((1 << 22) + 256)
     assert lib.zs_workspace_bytes(-1) == 0
 
 

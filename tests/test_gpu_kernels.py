@@ -92,12 +92,16 @@ def test_reduce_propagates_nonfinite_to_exactly_the_affected_elements():
     assert np.all(np.isnan(g[idx_nan])) and np.all(np.isposinf(g[idx_inf]))
 
 
-def test_reduce_is_deterministic():
-    n, world = 3_000_001, 16
+@pytest.mark.parametrize("n, world", [(3_000_001, 16), (8_388_611, 8)])
+def test_reduce_is_deterministic(n, world):
+    # the second case has one partial per 1024-element tile (8193 of them), which
+    # takes the two-level finalize
     rows = device_rows(11, world, n, "bf16")
     g1, s1 = _reduce(rows, n, sumsq=True)
     g2, s2 = _reduce(rows, n, sumsq=True)
     assert np.array_equal(bits32(g1), bits32(g2)) and s1 == s2
+    ref = oreduce.sumsq(g1)
+    assert abs(s1 - ref) <= 1e-12 * ref
 
 
 def _adamw(n, step, hp, seed, cast=True, scale=None, offset=0, out_offset=0):
