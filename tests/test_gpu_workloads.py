@@ -178,3 +178,33 @@ def test_70b_fp32_contributions_bench_chunk():
     _full_size_case(chunk, 64, "f32", step=4, moments=True, slot_offset=0, seed=7100,
                     windows=4, width=65536)
     torch.cuda.empty_cache()
+
+
+def test_resume_from_saved_state_is_bitwise_the_straight_run():
+    # the rank's resumable state is {master, m, v, step}: 5 steps, save to host
+    # bytes, reload into fresh device buffers, 5 more steps == 10 straight steps
+    import io
+
+    n, world = 262144 + 7, 8
+    hp = hparams()
+    g0 = gen.device_generator(4242)
+    th0 = gen.device_normal(g0, n, gen.THETA_SIGMA)
+    grads = [device_rows(4300 + t, world, n, "bf16") for t in range(10)]
+    straight = (th0.clone(), torch.zeros(n, device="cuda"), torch.zeros(n, device="cuda"))
+    slot = torch.empty(n, device="cuda", dtype=torch.bfloat16)
+    for t in range(10):
+        zs.zs_sharded_step(grads[t], *straight, step=t + 1, bf16_out=slot, **hp)
+    part = (th0.clone(), torch.zeros(n, device="cuda"), torch.zeros(n, device="cuda"))
+    for t in range(5):
+        zs.zs_sharded_step(grads[t], *part, step=t + 1, bf16_out=slot, **hp)
+    buf = io.BytesIO()
+    torch.save({"master": part[0].cpu(), "exp_avg": part[1].cpu(), "exp_avg_sq": part[2].cpu(), "step": 5}, buf)
+    del part
+    buf.seek(0)
+    ck = torch.load(buf, weights_only=True)
+    resumed = tuple(ck[k].cuda() for k in ("master", "exp_avg", "exp_avg_sq"))
+    for t in range(ck["step"], 10):
+        zs.zs_sharded_step(grads[t], *resumed, step=t + 1, bf16_out=slot, **hp)
+    torch.cuda.synchronize()
+    for x, y in zip(straight, resumed):
+        assert torch.equal(x.view(torch.int32), y.view(torch.int32))
