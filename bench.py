@@ -17,8 +17,9 @@ Also measured (in "parts"): the same update as two launches (reduce, then AdamW
 with the fused cast), each kernel alone, the clipped update (reduce with its sum
 of squares, clip coefficient, AdamW with the gradient scale), fp32 gradient
 accumulation in the ZeRO-2 and ZeRO-1 orders, the unshard copy-out of one
-decoder block (flat and dim-0 sharded), the dim-0 pack of that block, and the
-pack of the shard. The JSON line carries the roofline of
+decoder block (flat and dim-0 sharded), the dim-0 pack of that block, the
+pack of the shard, and the same update composed from PyTorch's own ops (rank
+adds, fused AdamW, copy-cast) as a library reference. The JSON line carries the roofline of
 the dominant kernel (HIP-event time on the launch stream) and the CPU oracle
 timed on a bounded sample of the same inputs.
 """
@@ -268,6 +269,30 @@ def main() -> int:
             gbs = bpe * elems / (t * 1e-3) / 1e9
             parts[name] = dict(ms=round(t, 5), elems=elems, bytes_per_elem=bpe, gb_s=round(gbs, 1),
                                frac_of_peak=round(gbs / PEAK_HBM_GBS, 4))
+
+        # the same update composed from PyTorch's own ops, as a library reference:
+        # in-place fp32 adds of the N contributions in rank order, one division,
+        # PyTorch's fused AdamW, and a copy-cast into the slot
+        if len(ranges) == 1:
+            p = torch.nn.Parameter(theta.clone())
+            p.grad = torch.empty_like(p)
+            opt = torch.optim.AdamW([p], lr=hp["lr"], betas=(hp["beta1"], hp["beta2"]), eps=hp["eps"],
+                                    weight_decay=hp["weight_decay"], fused=True)
+
+            def torch_step(i):
+                gg = p.grad
+                gg.copy_(rows[0])
+                for r in rows[1:]:
+                    gg.add_(r)
+                gg.div_(world)
+                opt.step()
+                slot.copy_(p.detach())
+
+            t_torch = event_time_ms(torch_step, max(5, iters // 4), stream)
+            parts["torch_composed_step"] = dict(
+                ms=round(t_torch, 5), gelem_s=round(S / (t_torch * 1e-3) / 1e9, 3),
+                fused_step_speedup=round(t_torch / ms_step, 3))
+            del p, opt
 
         # global-norm clipping: the reduce also returns the fp64 sum of squares of its
         # output, the clip coefficient combines the shards' partials (here the N
