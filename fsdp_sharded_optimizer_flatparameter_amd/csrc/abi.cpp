@@ -44,6 +44,27 @@ zs_status check_rows(const void* const* rows, int32_t world, int32_t dtype, int6
 
 inline zs_status hip_status(hipError_t e) { return e == hipSuccess ? ZS_OK : ZS_ERR_HIP; }
 
+// The sum of squares' workspace and result are written while the rows are read
+// and `out` (n fp32) is written: none of them may share bytes.
+zs_status check_sumsq_buffers(const void* const* rows, int32_t world, int32_t dtype, int64_t n,
+                              const void* out, const void* sumsq, const void* ws, size_t ws_bytes) {
+  const int64_t wb = (int64_t)ws_bytes;
+  if (overlaps(sumsq, 8, ws, wb) || overlaps(sumsq, 8, out, n * 4) || overlaps(ws, wb, out, n * 4))
+    return ZS_ERR_OVERLAP;
+  for (int32_t q = 0; q < world && n > 0; ++q) {
+    const int64_t rb = n * elem_size(dtype);
+    if (overlaps(rows[q], rb, sumsq, 8) || overlaps(rows[q], rb, ws, wb)) return ZS_ERR_OVERLAP;
+  }
+  return ZS_OK;
+}
+
+// The gradient scale is read by every workgroup while the state is written.
+bool scale_overlaps(const float* scale, const void* a, const void* b, const void* c, int64_t n,
+                    const void* bf16_out) {
+  return scale && (overlaps(scale, 4, a, n * 4) || overlaps(scale, 4, b, n * 4) ||
+                   overlaps(scale, 4, c, n * 4) || (bf16_out && overlaps(scale, 4, bf16_out, n * 2)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -153,6 +174,8 @@ zs_status zs_reduce_grads(const void* const* rows, int32_t world, int32_t dtype,
     if (!aligned(sumsq_out, 8)) return ZS_ERR_ALIGN;
     if (!workspace || workspace_bytes < zs_workspace_bytes(n)) return ZS_ERR_WORKSPACE;
     if (!aligned(workspace, 8)) return ZS_ERR_ALIGN;
+    st = check_sumsq_buffers(rows, world, dtype, n, grad_out, sumsq_out, workspace, workspace_bytes);
+    if (st != ZS_OK) return st;
   }
   if (n == 0) {
     if (!sumsq_out) return ZS_OK;
@@ -186,6 +209,7 @@ zs_status zs_adamw_step(float* master, float* exp_avg, float* exp_avg_sq, const 
   if (bf16_out && (overlaps(bf16_out, n * 2, master, b) || overlaps(bf16_out, n * 2, exp_avg, b) ||
                    overlaps(bf16_out, n * 2, exp_avg_sq, b) || overlaps(bf16_out, n * 2, grad, b)))
     return ZS_ERR_OVERLAP;
+  if (scale_overlaps(grad_scale, master, exp_avg, exp_avg_sq, n, bf16_out)) return ZS_ERR_OVERLAP;
   return hip_status(
       zs::launch_adamw(master, exp_avg, exp_avg_sq, grad, n, *hp, grad_scale, bf16_out, stream));
 }
@@ -316,6 +340,7 @@ zs_status zs_sharded_step(const void* const* rows, int32_t world, int32_t dtype,
   if (bf16_out && (overlaps(bf16_out, n * 2, master, b) || overlaps(bf16_out, n * 2, exp_avg, b) ||
                    overlaps(bf16_out, n * 2, exp_avg_sq, b)))
     return ZS_ERR_OVERLAP;
+  if (scale_overlaps(grad_scale, master, exp_avg, exp_avg_sq, n, bf16_out)) return ZS_ERR_OVERLAP;
   return hip_status(zs::launch_fused(rows, world, dtype, n, master, exp_avg, exp_avg_sq, *hp,
                                      grad_scale, bf16_out, stream));
 }
@@ -332,6 +357,8 @@ zs_status zs_accumulate_grads(const void* const* rows, int32_t world, int32_t dt
     if (!aligned(sumsq_out, 8)) return ZS_ERR_ALIGN;
     if (!workspace || workspace_bytes < zs_workspace_bytes(n)) return ZS_ERR_WORKSPACE;
     if (!aligned(workspace, 8)) return ZS_ERR_ALIGN;
+    st = check_sumsq_buffers(rows, world, dtype, n, acc, sumsq_out, workspace, workspace_bytes);
+    if (st != ZS_OK) return st;
   }
   if (n == 0 && !sumsq_out) return ZS_OK;
   for (int32_t q = 0; q < world && n > 0; ++q)

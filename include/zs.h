@@ -174,7 +174,8 @@ zs_status zs_pack_shard(const zs_param_desc* d_desc, int32_t nparams, int64_t to
  *                 accumulated in fp64 in a fixed order (deterministic)
  *   workspace     DEVICE scratch of at least zs_workspace_bytes(n) bytes,
  *                 required only when sumsq_out != NULL
- * grad_out may not overlap any row (ZS_ERR_OVERLAP). Errors: ZS_ERR_NULL,
+ * grad_out may not overlap any row; sumsq_out and workspace may not overlap
+ * each other, grad_out or a row (ZS_ERR_OVERLAP). Errors: ZS_ERR_NULL,
  * ZS_ERR_SIZE, ZS_ERR_WORLD, ZS_ERR_DTYPE, ZS_ERR_WORKSPACE, ZS_ERR_ALIGN,
  * ZS_ERR_OVERLAP, ZS_ERR_HIP.
  */
@@ -204,8 +205,11 @@ size_t zs_workspace_bytes(int64_t n);
  *                 coefficient computed on the device from sums of squares)
  *   bf16_out[n]   optional DEVICE bf16 output (NULL = skip): bf16(theta'),
  *                 typically the rank's slot of the all-gather buffer
+ * No two of master, exp_avg, exp_avg_sq, grad and bf16_out may share bytes, and
+ * grad_scale may not overlap an output (ZS_ERR_OVERLAP).
  * Errors: ZS_ERR_NULL, ZS_ERR_SIZE, ZS_ERR_HPARAM (non-finite values, lr, eps
- * or wd < 0, betas outside [0, 1), step < 1), ZS_ERR_ALIGN, ZS_ERR_HIP.
+ * or wd < 0, betas outside [0, 1), step < 1), ZS_ERR_ALIGN, ZS_ERR_OVERLAP,
+ * ZS_ERR_HIP.
  */
 zs_status zs_adamw_step(float* master, float* exp_avg, float* exp_avg_sq, const float* grad,
                         int64_t n, const zs_adamw_hparams* hp, const float* grad_scale,

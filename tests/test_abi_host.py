@@ -152,6 +152,13 @@ def test_reduce_argument_errors(lib):
     assert f(_rows(4), 4, 1, 4096, g, s, C.c_void_p(FAKE + (1 << 42)), 31, None) == -8
     # output overlapping a contribution
     assert f(_rows(4), 4, 1, 100, C.c_void_p(FAKE + 16), None, None, 0, None) == -11
+    # the sum of squares' result and workspace may not overlap each other, the output or a row
+    ws = C.c_void_p(FAKE + (1 << 42))
+    wsb = lib.zs_workspace_bytes(4096)
+    assert f(_rows(4), 4, 1, 4096, g, C.c_void_p(FAKE + (1 << 42) + 8), ws, wsb, None) == -11
+    assert f(_rows(4), 4, 1, 4096, g, s, C.c_void_p(FAKE + (1 << 40) + 64), wsb, None) == -11
+    assert f(_rows(4), 4, 1, 4096, g, C.c_void_p(FAKE + (1 << 30) + 8), ws, wsb, None) == -11
+    assert f(_rows(4), 4, 1, 4096, g, s, C.c_void_p(FAKE + 64), wsb, None) == -11
 
 
 def test_adamw_argument_errors(lib):
@@ -167,6 +174,10 @@ def test_adamw_argument_errors(lib):
     assert f(a, C.c_void_p(FAKE + 8), c, g, 10, C.byref(_hp()), None, None, None) == -11
     assert f(a, b, c, g, 10, C.byref(_hp()), None, C.c_void_p(FAKE + 1), None) == -10
     assert f(a, b, c, g, 10, C.byref(_hp()), None, C.c_void_p(FAKE + 4), None) == -11
+    # the gradient scale is read while the state is written
+    assert f(a, b, c, g, 10, C.byref(_hp()), C.c_void_p(FAKE + (1 << 32) + 8), None, None) == -11
+    assert f(a, b, c, g, 10, C.byref(_hp()), C.c_void_p(FAKE + 4 * (1 << 32) + 4),
+             C.c_void_p(FAKE + 4 * (1 << 32)), None) == -11
     # n == 0 is a valid no-op even with NULL buffers (nothing is enqueued)
     assert f(None, None, None, None, 0, C.byref(_hp()), None, None, None) == 0
 
@@ -207,6 +218,9 @@ def test_sharded_step_argument_errors(lib):
     assert f(_rows(8), 8, 1, 10, None, b, c, C.byref(_hp()), None, None, None) == -1
     assert f(_rows(8), 8, 1, 10, C.c_void_p(FAKE + 4), b, c, C.byref(_hp()), None, None, None) == -11
     assert f(_rows(8), 8, 1, 10, a, b, c, C.byref(_hp()), None, C.c_void_p(FAKE + 2), None) == -11
+    # a gradient scale inside the state it scales
+    assert f(_rows(8), 8, 1, 10, a, b, c, C.byref(_hp()), C.c_void_p(FAKE + (1 << 44) + 12), None,
+             None) == -11
 
 
 def test_accumulate_and_clip_argument_errors(lib):
@@ -218,6 +232,9 @@ def test_accumulate_and_clip_argument_errors(lib):
     assert f(_rows(4), 4, 1, 100, None, C.c_float(1.0), 0, None, None, 0, None) == -1
     assert f(_rows(4), 4, 1, 4096, a, C.c_float(1.0), 0, C.c_void_p(FAKE + (1 << 41)), None, 0, None) == -8
     assert f(_rows(4), 4, 1, 100, C.c_void_p(FAKE + 8), C.c_float(1.0), 1, None, None, 0, None) == -11
+    wsb = lib.zs_workspace_bytes(4096)
+    assert f(_rows(4), 4, 1, 4096, a, C.c_float(1.0), 0, C.c_void_p(FAKE + (1 << 41)),
+             C.c_void_p(FAKE + (1 << 40) + 8), wsb, None) == -11  # workspace inside acc
     g = lib.zs_accumulate_local
     assert g(a, 2, 10, a, 0, None) == -5
     assert g(a, 1, -1, a, 0, None) == -2
