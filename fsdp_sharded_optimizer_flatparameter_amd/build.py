@@ -3,7 +3,8 @@
     python -m fsdp_sharded_optimizer_flatparameter_amd.build [-v]
 
 Each source is compiled by hipcc in parallel; the objects are linked into
-fsdp_sharded_optimizer_flatparameter_amd/libzs.so, replaced atomically.
+fsdp_sharded_optimizer_flatparameter_amd/libzs.so, replaced atomically. The
+standalone C-ABI test driver (tests/c/zs_driver) is linked against it.
 """
 from __future__ import annotations
 
@@ -70,7 +71,25 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
     os.replace(tmp, LIB)
+    build_driver()
     return LIB
+
+
+DRIVER_SRC = os.path.join(ROOT, "tests", "c", "zs_driver.cpp")
+DRIVER = os.path.join(ROOT, "tests", "c", "zs_driver")
+
+
+def build_driver() -> str:
+    """The standalone C-ABI test driver (host code only), linked against the
+    in-tree libzs.so through a path relative to the binary."""
+    tmp = DRIVER + ".tmp"
+    cmd = [hipcc(), "-O2", "-std=c++17", "-Wall", f"-I{INCLUDE}", DRIVER_SRC, f"-L{PKG}", "-lzs",
+           "-Wl,-rpath,$ORIGIN/../../fsdp_sharded_optimizer_flatparameter_amd", "-o", tmp]
+    res = subprocess.run(cmd, capture_output=True, text=True, cwd=os.path.dirname(DRIVER))
+    if res.returncode != 0:
+        raise RuntimeError(f"driver build failed:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+    os.replace(tmp, DRIVER)
+    return DRIVER
 
 
 if __name__ == "__main__":

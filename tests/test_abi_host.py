@@ -345,3 +345,19 @@ def test_dim0_pack_copy_out_errors(lib):
     assert c(g, 40, None, 2, 4, 30, 10, None) == -1
     assert c(C.c_void_p(FAKE + 1), 40, d, 2, 4, 30, 10, None) == -10
     assert c(g, 40, d, 0, 4, 0, 0, None) == 0
+
+
+def test_c_driver_is_built_and_rejects_bad_usage(tmp_path):
+    # the standalone C-ABI driver links libzs.so; argument and I/O errors end it
+    # with status 2 before any GPU call
+    import subprocess
+
+    drv = os.path.join(os.path.dirname(os.path.abspath(__file__)), "c", "zs_driver")
+    assert os.access(drv, os.X_OK), "tests/c/zs_driver is built with the library"
+    assert subprocess.run([drv], capture_output=True, timeout=60).returncode == 2
+    assert subprocess.run([drv, str(tmp_path / "missing.bin"), str(tmp_path / "o.bin")],
+                          capture_output=True, timeout=60).returncode == 2
+    bad = tmp_path / "short.bin"
+    bad.write_bytes(b"\x01\x00\x00\x00")
+    assert subprocess.run([drv, str(bad), str(tmp_path / "o.bin")], capture_output=True,
+                          timeout=60).returncode == 2
