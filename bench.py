@@ -57,18 +57,22 @@ WORKLOADS = {
 
 
 # Sources that define each timed kernel and its launch shape; counter-derived
-# traffic is reported only while these are unchanged since the counters were taken.
+# traffic is reported only while these, and the device compile flags, are
+# unchanged since the counters were taken.
 KERNEL_SOURCES = {
-    "k_fused": ("csrc/fused.hip", "csrc/zs_device.hpp", "csrc/zs_launch.hpp", "csrc/tuning.cpp",
-                "build.py"),
+    "k_fused": ("csrc/fused.hip", "csrc/zs_device.hpp", "csrc/zs_launch.hpp", "csrc/tuning.cpp"),
 }
 
 
 def source_hash(kernel: str) -> str:
+    from fsdp_sharded_optimizer_flatparameter_amd import build as zsbuild
+
     h = hashlib.sha256()
     for name in KERNEL_SOURCES[kernel]:
         with open(os.path.join(os.path.dirname(CSRC), name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
+    flags = [f for f in (*zsbuild.COMMON, *zsbuild.DEVICE) if not f.startswith("-I")]  # no paths
+    h.update(" ".join([zsbuild.ARCH, *flags]).encode())
     return h.hexdigest()[:16]
 
 
