@@ -18,8 +18,9 @@ with the fused cast), each kernel alone, the clipped update (reduce with its sum
 of squares, clip coefficient, AdamW with the gradient scale), fp32 gradient
 accumulation in the ZeRO-2 and ZeRO-1 orders, the unshard copy-out of one
 decoder block (flat and dim-0 sharded), the dim-0 pack of that block, the
-pack of the shard, and the same update composed from PyTorch's own ops (rank
-adds, fused AdamW, copy-cast) as a library reference. The JSON line carries the roofline of
+pack of the shard, the step replayed from a captured HIP graph, and the same
+update composed from PyTorch's own ops (rank adds, fused AdamW, copy-cast) as a
+library reference. The JSON line carries the roofline of
 the dominant kernel (HIP-event time on the launch stream) and the CPU oracle
 timed on a bounded sample of the same inputs.
 """
@@ -273,6 +274,21 @@ def main() -> int:
             gbs = bpe * elems / (t * 1e-3) / 1e9
             parts[name] = dict(ms=round(t, 5), elems=elems, bytes_per_elem=bpe, gb_s=round(gbs, 1),
                                frac_of_peak=round(gbs / PEAK_HBM_GBS, 4))
+
+        # the step captured once in a HIP graph and replayed: no host launch work
+        # per step (what decides the launch-bound Tiny shard)
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            fused_step(0)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            fused_step(0)
+        t_graph = event_time_ms(lambda i: graph.replay(), iters, stream)
+        parts["graph_replayed_step"] = dict(ms=round(t_graph, 5), gelem_s=round(S / (t_graph * 1e-3) / 1e9, 3))
+        del graph
 
         # the same update composed from PyTorch's own ops, as a library reference:
         # in-place fp32 adds of the N contributions in rank order, one division,
