@@ -8,6 +8,7 @@ not been built.
 from .api import (  # noqa: F401
     Dim0Table,
     ParamTable,
+    ShardedStep,
     ZsArgumentError,
     ZsError,
     zs_accumulate_grads,

@@ -305,6 +305,37 @@ def zs_sharded_step(rows, master, exp_avg, exp_avg_sq, *, lr, beta1, beta2, eps,
         _ptr(grad_scale), _ptr(bf16_out), _stream(stream, master.device)))
 
 
+class ShardedStep:
+    """zs_sharded_step with its arguments checked and marshalled once.
+
+    Calling the object with a step number issues one C call with the prepared
+    arguments: the per-step host cost is a single ctypes call, which is what a
+    small (launch-bound) shard needs. The tensors are kept referenced. The
+    stream is fixed when the object is made (default: the current stream of
+    the master's device at that moment), so an object used under HIP graph
+    capture must be made inside the capture. The library still validates
+    every call.
+    """
+
+    def __init__(self, rows, master, exp_avg, exp_avg_sq, *, lr, beta1, beta2, eps, weight_decay,
+                 grad_scale=None, bf16_out=None, stream=None):
+        n = _state(master, exp_avg, exp_avg_sq)
+        self._rows, self._world, self._dtype = _rows(rows, n)
+        _opt_out(bf16_out, grad_scale, n)
+        self._keep = (list(rows), master, exp_avg, exp_avg_sq, grad_scale, bf16_out)
+        self._hp = _hparams(lr, beta1, beta2, eps, weight_decay, 1)
+        self._fn = _lib().zs_sharded_step
+        self._args = (self._rows, self._world, self._dtype, n, _ptr(master), _ptr(exp_avg),
+                      _ptr(exp_avg_sq), C.byref(self._hp), _ptr(grad_scale), _ptr(bf16_out),
+                      _stream(stream, master.device))
+
+    def __call__(self, step: int) -> None:
+        self._hp.step = int(step)
+        st = self._fn(*self._args)
+        if st != 0:
+            L.check("zs_sharded_step", st)
+
+
 def zs_accumulate_grads(rows, acc, *, scale=1.0, first=False, sumsq_out=None, workspace=None,
                         stream=None):
     _dev(acc, "acc", torch.float32)

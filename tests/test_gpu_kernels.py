@@ -254,3 +254,25 @@ def test_binding_rejects_bad_tensors():
         zs.zs_reduce_grads([x.cpu().bfloat16()], torch.zeros(8, device="cuda"))
     with pytest.raises(zs.ZsArgumentError):
         zs.zs_adamw_step(x, x.clone(), x.clone(), x.clone(), step=0, **hparams())
+
+
+def test_prepared_step_is_the_plain_call():
+    n, world = 262144 + 7, 8
+    rows = device_rows(880, world, n, "bf16")
+    a = device_state(881, n)
+    b = tuple(t.clone() for t in a)
+    oa = torch.empty(n, device="cuda", dtype=torch.bfloat16)
+    ob = torch.empty_like(oa)
+    hp = hparams()
+    plan = zs.ShardedStep(rows, *b, bf16_out=ob, **hp)
+    for step in (1, 2, 3):
+        zs.zs_sharded_step(rows, *a, step=step, bf16_out=oa, **hp)
+        plan(step)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert np.array_equal(bits32(host(x)), bits32(host(y)))
+    assert np.array_equal(host(oa), host(ob))
+    with pytest.raises(ValueError):
+        zs.ShardedStep(rows, a[0], a[1][:-1], a[2], **hp)
+    with pytest.raises(zs.ZsArgumentError):
+        plan(0)  # the library rejects step 0
