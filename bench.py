@@ -50,8 +50,9 @@ WORKLOADS = {
     "70b": dict(shapes="llama_70b", world=64, rank=63, wd=0.01, rows="f32", chunks=8,
                 desc="70B parameter list (Llama-3 70B shapes), N=64 simulated ranks, rank 63's shard, "
                      "fp32 contributions, 8 chunks"),
-    "gpt2": dict(shapes="gpt2_small", world=8, rank=7, wd=0.01,
-                 desc="GPT-2-small parameter list, N=8 simulated ranks, rank 7's shard"),
+    "gpt2": dict(shapes="gpt2_small", world=8, rank=7, wd=0.01, rotate=3,
+                 desc="GPT-2-small parameter list, N=8 simulated ranks, rank 7's shard "
+                      "(3 input sets in rotation)"),
     "tiny": dict(shapes="tiny", world=4, rank=3, wd=0.01,
                  desc="4 x 512x512 parameters, N=4 simulated ranks, rank 3's shard"),
 }
@@ -203,10 +204,20 @@ def main() -> int:
                 for a, b in ranges]
 
     plans = make_plans()
+    # A shard whose working set is near the 256 MB Infinity Cache (GPT-2: 0.65 GB)
+    # steps round-robin over independent copies of its inputs, so that no step
+    # finds the previous step's bytes still cached.
+    rotation = [plans]
+    for k in range(1, wl.get("rotate", 1)):
+        rk = [gen.device_normal(g0, csize, gen.GRAD_SIGMA, row_dtype, dev) for _ in range(world)]
+        tk = gen.device_normal(g0, S, gen.THETA_SIGMA, None, dev)
+        mk, vk = torch.zeros(S, device=dev), torch.zeros(S, device=dev)
+        sk = torch.empty(S, device=dev, dtype=torch.bfloat16)
+        rotation.append([zs.ShardedStep(rk, tk, mk, vk, bf16_out=sk, **hp)])
 
     def fused_step(_i):
         step_no[0] += 1
-        for plan in plans:
+        for plan in rotation[step_no[0] % len(rotation)]:
             plan(step_no[0])
 
     if args.calibrate_copy:

@@ -101,6 +101,11 @@ def test_copy_out_dim0_llama8b_block_full():
     _copy_out_case(shapes.llama3_8b_block(), seed=23, world=8)
 
 
+def test_copy_out_dim0_70b_block_full():
+    # one 70B decoder block split on dim 0 over 64 ranks, as the benchmark times it
+    _copy_out_case(shapes.llama_70b_block(), seed=24, world=64)
+
+
 def test_roundtrip_dim0_pack_cast_gather_copy_out():
     # with lr = wd = 0 theta is unchanged, so the unsharded parameters come back
     # as the bf16 rounding of the originals, bit for bit; every padding row
