@@ -276,3 +276,32 @@ def test_prepared_step_is_the_plain_call():
         zs.ShardedStep(rows, a[0], a[1][:-1], a[2], **hp)
     with pytest.raises(zs.ZsArgumentError):
         plan(0)  # the library rejects step 0
+
+
+def test_concurrent_updates_on_two_streams_match_sequential():
+    # the library keeps no state: two shards updated at once on two streams give
+    # the same bits as one after the other
+    n, world, hp = 1_000_003, 8, hparams()
+    shards = []
+    for k in range(2):
+        rows = device_rows(890 + k, world, n, "bf16")
+        st = device_state(895 + k, n)
+        shards.append((rows, st, tuple(t.clone() for t in st),
+                       torch.empty(n, device="cuda", dtype=torch.bfloat16),
+                       torch.empty(n, device="cuda", dtype=torch.bfloat16)))
+    torch.cuda.synchronize()
+    for rows, _, seq, _, out in shards:  # sequential reference on the current stream
+        for step in (1, 2):
+            zs.zs_sharded_step(rows, *seq, step=step, bf16_out=out, **hp)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for s_ in streams:
+        s_.wait_stream(torch.cuda.current_stream())
+    for step in (1, 2):
+        for (rows, st, _, out, _), s_ in zip(shards, streams):
+            zs.zs_sharded_step(rows, *st, step=step, bf16_out=out, stream=s_, **hp)
+    torch.cuda.synchronize()
+    for rows, st, seq, out_c, out_s in shards:
+        for x, y in zip(st, seq):
+            assert torch.equal(x.view(torch.int32), y.view(torch.int32))
+        assert torch.equal(out_c.view(torch.int16), out_s.view(torch.int16))
