@@ -256,13 +256,18 @@ def main() -> int:
 
     parts = {}
     copy_gbs = None
+    runtime_copy_gbs = None
     if not args.no_parts and not args.calibrate_copy:
-        # a plain device copy (the runtime's copy kernel) of 2 GiB as a practical ceiling
-        src = torch.ones(1 << 29, device=dev)
+        # practical copy ceilings, 2 GiB each way: the library's own streaming copy
+        # (zs_copy_out of a one-parameter unit) and the HIP runtime's copy kernel
+        src = torch.ones(1 << 30, device=dev, dtype=torch.bfloat16)
         dst = torch.empty_like(src)
+        one = zs.ParamTable([dst])
+        t_copy = event_time_ms(lambda i: zs.zs_copy_out(src, one), 10, stream)
+        copy_gbs = 2 * src.numel() * 2 / (t_copy * 1e-3) / 1e9
         t_copy = event_time_ms(lambda i: dst.copy_(src), 10, stream)
-        copy_gbs = 2 * src.numel() * 4 / (t_copy * 1e-3) / 1e9
-        del src, dst
+        runtime_copy_gbs = 2 * src.numel() * 2 / (t_copy * 1e-3) / 1e9
+        del src, dst, one
     if not args.no_parts:
         iters = max(10, args.steps)
 
@@ -501,6 +506,7 @@ def main() -> int:
             "traffic": traffic,
             "copy_ceiling_gb_s": round(copy_gbs, 1) if copy_gbs else None,
             "frac_of_copy_ceiling": round(achieved / copy_gbs, 4) if copy_gbs else None,
+            "runtime_copy_gb_s": round(runtime_copy_gbs, 1) if runtime_copy_gbs else None,
         },
         "cpu_baseline": cpu,
         "parts": parts,
