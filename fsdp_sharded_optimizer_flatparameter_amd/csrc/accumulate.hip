@@ -18,14 +18,6 @@
 namespace zs {
 namespace {
 
-MeanDiv mean_div(int world) {
-  MeanDiv d;
-  d.n = (float)world;
-  d.pow2 = (world & (world - 1)) == 0;
-  d.inv = 1.0f / (float)world;
-  return d;
-}
-
 // G groups per lane (G*1024 consecutive elements per workgroup pass), in three
 // steps: the previous sums of all G groups are loaded into lane-private LDS
 // slots, the rank walk adds each group's scaled mean into its slot, and the G
@@ -154,11 +146,6 @@ __global__ void k_clip(const double* __restrict__ partials, int count, double ma
   if (norm_out) *norm_out = norm;
 }
 
-int64_t grid_for(int64_t units, int64_t per_block) {
-  int64_t gsz = (units + per_block - 1) / per_block;
-  if (gsz > tuning().grid_cap) gsz = tuning().grid_cap;
-  return gsz < 1 ? 1 : gsz;
-}
 
 // Measured on MI355X: 16 groups per lane (64 KiB of LDS, two workgroups per
 // CU) with many contributions, as for the reduce; 4 groups with few.
@@ -214,7 +201,6 @@ void dispatch_flags(bool first, bool scaled, bool vec, const void* const* rows, 
   else dispatch_world<In, SUMSQ, false, false>(rows, world, n, acc, scale, partials, grid, s);
 }
 
-bool al(const void* p, unsigned a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 }  // namespace
 
@@ -223,8 +209,8 @@ hipError_t launch_accumulate(const void* const* rows, int world, int dtype, int6
                              hipStream_t s) {
   int64_t grid = 0;
   if (n > 0) {
-    bool vec = al(acc, 16);
-    for (int i = 0; i < world; ++i) vec = vec && al(rows[i], dtype == ZS_BF16 ? 8 : 16);
+    bool vec = aligned_to(acc, 16);
+    for (int i = 0; i < world; ++i) vec = vec && aligned_to(rows[i], dtype == ZS_BF16 ? 8 : 16);
     const bool scaled = scale != 1.0f;
     if (dtype == ZS_BF16) {
       if (sumsq) dispatch_flags<uint16_t, true>(first, scaled, vec, rows, world, n, acc, scale, partials, &grid, s);
@@ -243,7 +229,7 @@ hipError_t launch_accumulate(const void* const* rows, int world, int dtype, int6
 hipError_t launch_accumulate_local(const void* g, int dtype, int64_t n, float* acc, bool first,
                                    hipStream_t s) {
   if (n == 0) return hipSuccess;
-  const bool vec = al(acc, 16) && al(g, dtype == ZS_BF16 ? 8 : 16);
+  const bool vec = aligned_to(acc, 16) && aligned_to(g, dtype == ZS_BF16 ? 8 : 16);
   const int64_t ngroups = n / 4;
   const dim3 gd((unsigned)grid_for(vec ? ngroups : n, kThreads)), bd(kThreads);
   if (dtype == ZS_BF16) {

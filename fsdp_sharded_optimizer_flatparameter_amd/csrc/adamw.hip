@@ -148,14 +148,6 @@ __global__ __launch_bounds__(kThreads) void k_cast_scalar(const float* __restric
     out[i] = (uint16_t)f32_to_bf16(src[i]);
 }
 
-bool al(const void* p, unsigned a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
-
-int64_t grid_for(int64_t units, int64_t per_block) {
-  int64_t gsz = (units + per_block - 1) / per_block;
-  if (gsz > tuning().grid_cap) gsz = tuning().grid_cap;
-  return gsz < 1 ? 1 : gsz;
-}
-
 template <int V, bool CAST, bool SCALE>
 void run_adamw(float* th, float* m, float* v, const float* g, int64_t n, const AdamConsts& c,
                const float* scale, uint16_t* out, hipStream_t s) {
@@ -182,7 +174,7 @@ hipError_t launch_adamw(float* th, float* m, float* v, const float* g, int64_t n
                         hipStream_t s) {
   if (n == 0) return hipSuccess;
   const AdamConsts c = adam_consts(hp);
-  const bool vec = al(th, 16) && al(m, 16) && al(v, 16) && al(g, 16) && (!out || al(out, 8));
+  const bool vec = aligned_to(th, 16) && aligned_to(m, 16) && aligned_to(v, 16) && aligned_to(g, 16) && (!out || aligned_to(out, 8));
   if (vec) {
     if (out && scale) pick_v<true, true>(th, m, v, g, n, c, scale, out, s);
     else if (out) pick_v<true, false>(th, m, v, g, n, c, scale, out, s);
@@ -200,7 +192,7 @@ hipError_t launch_adamw(float* th, float* m, float* v, const float* g, int64_t n
 
 hipError_t launch_cast(const float* src, int64_t n, uint16_t* out, hipStream_t s) {
   if (n == 0) return hipSuccess;
-  if (al(src, 16) && al(out, 8)) {
+  if (aligned_to(src, 16) && aligned_to(out, 8)) {
     const int64_t ngroups = n / 4;
     const dim3 gd((unsigned)grid_for(ngroups, 2 * kThreads));
     hipLaunchKernelGGL((k_cast<2>), gd, dim3(kThreads), 0, s, src, ngroups, n, out);

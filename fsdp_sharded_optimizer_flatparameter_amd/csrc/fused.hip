@@ -16,14 +16,6 @@
 namespace zs {
 namespace {
 
-MeanDiv mean_div(int world) {
-  MeanDiv d;
-  d.n = (float)world;
-  d.pow2 = (world & (world - 1)) == 0;
-  d.inv = 1.0f / (float)world;
-  return d;
-}
-
 // Two phases per workgroup over G groups per lane (G*1024 consecutive elements):
 //   1. the rank walk only -- the mean gradient of each group is parked in LDS;
 //   2. AdamW over the fp32 state of the same groups, each lane reading back its
@@ -141,11 +133,6 @@ __global__ __launch_bounds__(kThreads) void k_fused_scalar(RowTable<ZS_MAX_WORLD
   }
 }
 
-int64_t grid_for(int64_t units, int64_t per_block) {
-  int64_t gsz = (units + per_block - 1) / per_block;
-  if (gsz > tuning().grid_cap) gsz = tuning().grid_cap;
-  return gsz < 1 ? 1 : gsz;
-}
 
 
 struct Shape {
@@ -220,7 +207,6 @@ void dispatch(const void* const* rows, int world, int64_t n, float* th, float* m
   else dispatch_g<In, 8>(sh.g, rows, world, n, th, m, v, c, scale, out, sh.lds, s);
 }
 
-bool al(const void* p, unsigned a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 }  // namespace
 
@@ -229,8 +215,8 @@ hipError_t launch_fused(const void* const* rows, int world, int dtype, int64_t n
                         uint16_t* out, hipStream_t s) {
   if (n == 0) return hipSuccess;
   const AdamConsts c = adam_consts(hp);
-  bool vec = al(th, 16) && al(m, 16) && al(v, 16) && (!out || al(out, 8));
-  for (int i = 0; i < world; ++i) vec = vec && al(rows[i], dtype == ZS_BF16 ? 8 : 16);
+  bool vec = aligned_to(th, 16) && aligned_to(m, 16) && aligned_to(v, 16) && (!out || aligned_to(out, 8));
+  for (int i = 0; i < world; ++i) vec = vec && aligned_to(rows[i], dtype == ZS_BF16 ? 8 : 16);
   if (vec) {
     if (dtype == ZS_BF16) dispatch<uint16_t>(rows, world, n, th, m, v, c, scale, out, s);
     else dispatch<float>(rows, world, n, th, m, v, c, scale, out, s);

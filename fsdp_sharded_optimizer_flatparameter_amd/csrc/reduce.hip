@@ -27,14 +27,6 @@ namespace zs {
 
 namespace {
 
-MeanDiv mean_div(int world) {
-  MeanDiv d;
-  d.n = (float)world;
-  d.pow2 = (world & (world - 1)) == 0;
-  d.inv = 1.0f / (float)world;  // exact when pow2
-  return d;
-}
-
 // G groups per lane: with G > 1 the lane's mean-gradient groups are parked in
 // LDS during the rank walk and written out afterwards as one burst of
 // nontemporal 16-byte stores (the LDS reservation also caps the workgroups
@@ -187,7 +179,6 @@ hipError_t dispatch_shape(const void* const* rows, int world, int64_t n, float* 
   }
 }
 
-bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 }  // namespace
 
@@ -196,7 +187,7 @@ hipError_t launch_reduce(const void* const* rows, int world, int dtype, int64_t 
   int64_t grid = 0;
   hipError_t err = hipSuccess;
   if (n > 0) {
-    bool vec = aligned16(g);
+    bool vec = aligned_to(g, 16);
     const uintptr_t ra = dtype == ZS_BF16 ? 7u : 15u;  // one lane group: 8 B of bf16, 16 B of fp32
     for (int i = 0; i < world; ++i) vec = vec && (reinterpret_cast<uintptr_t>(rows[i]) & ra) == 0;
     double* parts = sumsq ? partials : nullptr;

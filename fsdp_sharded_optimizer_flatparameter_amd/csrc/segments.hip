@@ -270,11 +270,7 @@ __global__ __launch_bounds__(kThreads) void k_copy_out_dim0(const uint16_t* __re
   }
 }
 
-int64_t grid_for(int64_t elems) {
-  int64_t gsz = (elems + kChunk - 1) / kChunk;
-  if (gsz > tuning().grid_cap) gsz = tuning().grid_cap;
-  return gsz < 1 ? 1 : gsz;
-}
+int64_t chunk_grid(int64_t elems) { return grid_for(elems, kChunk); }
 
 }  // namespace
 
@@ -282,7 +278,7 @@ hipError_t launch_pack(const zs_param_desc* d_desc, int nparams, int64_t total, 
                        int64_t flat_begin, int64_t shard, float* master, float* m, float* v,
                        hipStream_t s) {
   if (shard == 0) return hipSuccess;
-  const dim3 gd((unsigned)grid_for(shard)), bd(kThreads);
+  const dim3 gd((unsigned)chunk_grid(shard)), bd(kThreads);
   if (src_dtype == ZS_BF16)
     hipLaunchKernelGGL((k_pack<uint16_t>), gd, bd, 0, s, d_desc, nparams, total, flat_begin, shard,
                        master, m, v);
@@ -295,7 +291,7 @@ hipError_t launch_pack(const zs_param_desc* d_desc, int nparams, int64_t total, 
 hipError_t launch_pack_dim0(const zs_dim0_desc* d_desc, int nparams, int src_dtype, int rank,
                             int64_t local_total, float* master, float* m, float* v, hipStream_t s) {
   if (local_total == 0) return hipSuccess;
-  const dim3 gd((unsigned)grid_for(local_total)), bd(kThreads);
+  const dim3 gd((unsigned)chunk_grid(local_total)), bd(kThreads);
   if (src_dtype == ZS_BF16)
     hipLaunchKernelGGL((k_pack_dim0<uint16_t>), gd, bd, 0, s, d_desc, nparams, rank, local_total, master, m, v);
   else
@@ -306,7 +302,7 @@ hipError_t launch_pack_dim0(const zs_dim0_desc* d_desc, int nparams, int src_dty
 hipError_t launch_copy_out_dim0(const uint16_t* gathered, const zs_dim0_desc* d_desc, int nparams,
                                 int64_t total, int64_t local_total, hipStream_t s) {
   if (total == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_copy_out_dim0, dim3((unsigned)grid_for(total)), dim3(kThreads), 0, s, gathered,
+  hipLaunchKernelGGL(k_copy_out_dim0, dim3((unsigned)chunk_grid(total)), dim3(kThreads), 0, s, gathered,
                      d_desc, nparams, total, local_total);
   return hipGetLastError();
 }
@@ -314,7 +310,7 @@ hipError_t launch_copy_out_dim0(const uint16_t* gathered, const zs_dim0_desc* d_
 hipError_t launch_copy_out(const uint16_t* gathered, const zs_param_desc* d_desc, int nparams,
                            int64_t total, hipStream_t s) {
   if (total == 0 || nparams == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_copy_out, dim3((unsigned)grid_for(total)), dim3(kThreads), 0, s, gathered,
+  hipLaunchKernelGGL(k_copy_out, dim3((unsigned)chunk_grid(total)), dim3(kThreads), 0, s, gathered,
                      d_desc, nparams, total);
   return hipGetLastError();
 }

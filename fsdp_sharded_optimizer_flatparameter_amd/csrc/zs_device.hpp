@@ -105,62 +105,15 @@ struct Lanes<float> {
   }
 };
 
-// Rank sums of V groups per lane, double-buffered: the loads of the next chunk
-// of C ranks are in flight while the current chunk is added, so a lane keeps
-// C*V to 2*C*V independent loads outstanding through the whole walk. Each sum
-// starts from -0.0, the additive identity of IEEE addition (-0 + x == x for
-// every x, signed zeros included), so it equals c_0 + c_1 + ... + c_{N-1}
-// evaluated left to right in fp32.
-template <typename In, int C, int V, int CAP>
-__device__ __forceinline__ void rank_sum(const RowTable<CAP>& rows, int nw, const int64_t* q,
-                                         float (*acc)[4]) {
-  using L = Lanes<In>;
-  using Vec = typename L::Vec;
-#pragma unroll
-  for (int j = 0; j < V; ++j)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) acc[j][e] = -0.0f;
-  Vec a[C][V], b[C][V];
-#pragma unroll
-  for (int u = 0; u < C; ++u)
-    if (u < nw)
-#pragma unroll
-      for (int j = 0; j < V; ++j) a[u][j] = ld_nt(static_cast<const Vec*>(rows.p[u]) + q[j]);
-#pragma unroll 1
-  for (int r0 = 0; r0 < nw; r0 += 2 * C) {
-#pragma unroll
-    for (int u = 0; u < C; ++u)
-      if (r0 + C + u < nw)
-#pragma unroll
-        for (int j = 0; j < V; ++j)
-          b[u][j] = ld_nt(static_cast<const Vec*>(rows.p[r0 + C + u]) + q[j]);
-#pragma unroll
-    for (int u = 0; u < C; ++u)
-      if (r0 + u < nw)
-#pragma unroll
-        for (int j = 0; j < V; ++j) L::add(a[u][j], acc[j]);
-    if (r0 + C >= nw) break;
-#pragma unroll
-    for (int u = 0; u < C; ++u)
-      if (r0 + 2 * C + u < nw)
-#pragma unroll
-        for (int j = 0; j < V; ++j)
-          a[u][j] = ld_nt(static_cast<const Vec*>(rows.p[r0 + 2 * C + u]) + q[j]);
-#pragma unroll
-    for (int u = 0; u < C; ++u)
-      if (r0 + C + u < nw)
-#pragma unroll
-        for (int j = 0; j < V; ++j) L::add(b[u][j], acc[j]);
-  }
-}
-
 // Rank sums of G groups per lane -- group k at index base + k*kThreads + lane --
 // streamed as one double-buffered sequence of rank chunks that runs across
 // group boundaries: while chunk i is added, chunk i+1 (the next ranks of the
 // same group, or the first ranks of the next group) is already in flight, so a
 // lane never waits a full memory round trip between two groups. Each group's
-// sum starts from -0.0 and adds ranks in ascending order (the same fp32 result
-// as rank_sum). sink(k, acc) receives group k's finished sums.
+// sum starts from -0.0, the additive identity of IEEE addition (-0 + x == x for
+// every x, signed zeros included), and adds ranks in ascending order, so it
+// equals c_0 + c_1 + ... + c_{N-1} evaluated left to right in fp32.
+// sink(k, acc) receives group k's finished sums.
 template <typename In, int C, int G, int CAP, typename Sink>
 __device__ __forceinline__ void rank_sums_streamed(const RowTable<CAP>& rows, int nw, int64_t base,
                                                    int64_t ngroups, Sink&& sink) {
@@ -211,6 +164,15 @@ struct MeanDiv {
   int pow2;
   __device__ __forceinline__ float operator()(float s) const { return pow2 ? s * inv : s / n; }
 };
+
+// Host: the divisor of a launch over `world` contributions.
+inline MeanDiv mean_div(int world) {
+  MeanDiv d;
+  d.n = (float)world;
+  d.pow2 = (world & (world - 1)) == 0;
+  d.inv = 1.0f / (float)world;  // exact when world is a power of two
+  return d;
+}
 
 // ---- AdamW ---------------------------------------------------------------------
 

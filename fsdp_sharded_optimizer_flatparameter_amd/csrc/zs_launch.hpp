@@ -26,8 +26,21 @@ struct Tuning {
 };
 const Tuning& tuning();
 
-// Largest number of per-workgroup partial sums a sum-of-squares launch over n
-// elements writes; the workspace holds that many doubles.
+// Workgroups of a streaming launch over `units` work items, `per_block` per
+// workgroup, capped by the grid cap (the kernels grid-stride past it).
+inline int64_t grid_for(int64_t units, int64_t per_block) {
+  int64_t g = (units + per_block - 1) / per_block;
+  if (g > tuning().grid_cap) g = tuning().grid_cap;
+  return g < 1 ? 1 : g;
+}
+
+inline bool aligned_to(const void* p, unsigned a) {
+  return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
+}
+
+// Largest number of first-level partial sums a sum-of-squares launch over n
+// elements writes (one per 1024-element tile, capped with the grid); the
+// workspace holds that many doubles plus kFinalizeBlocks.
 int64_t max_partials(int64_t n);
 // Second-level partials the sum-of-squares finalize may use, stored after the
 // first-level ones in the caller's workspace.
