@@ -16,7 +16,7 @@
 namespace zs {
 namespace {
 
-// Two phases per workgroup over G groups per lane (G*1024 consecutive elements):
+// Two phases per workgroup over G groups per lane (G*BS*4 consecutive elements):
 //   1. the rank walk only -- the mean gradient of each group is parked in LDS;
 //   2. AdamW over the fp32 state of the same groups, each lane reading back its
 //      own LDS entries (no barrier), the state read and written as 16-byte
@@ -24,29 +24,29 @@ namespace {
 // Keeping the row streams and the state read-modify-write apart in time, and
 // the LDS reservation (which caps the workgroups resident per CU), keeps fewer
 // DRAM pages open at once; both were measured to raise HBM throughput.
-template <int NW, int CAP, int G, int C, typename In, bool CAST, bool SCALE>
-__global__ __launch_bounds__(kThreads) void k_fused(RowTable<CAP> rows, int world, MeanDiv div,
+template <int NW, int CAP, int G, int C, int BS, typename In, bool CAST, bool SCALE>
+__global__ __launch_bounds__(BS) void k_fused(RowTable<CAP> rows, int world, MeanDiv div,
                                                     int64_t ngroups, int64_t n,
                                                     float* __restrict__ th, float* __restrict__ m,
                                                     float* __restrict__ v, AdamConsts c,
                                                     const float* __restrict__ scale,
                                                     uint16_t* __restrict__ out) {
-  extern __shared__ f32x4 gl[];  // G * kThreads mean-gradient groups (plus any occupancy pad)
+  extern __shared__ f32x4 gl[];  // G * BS mean-gradient groups (plus any occupancy pad)
   using L = Lanes<In>;
   const int nw = NW > 0 ? NW : world;
   const float sc = SCALE ? *scale : 1.0f;
-  const int64_t span = (int64_t)kThreads * G;
+  const int64_t span = (int64_t)BS * G;
 
   for (int64_t base = (int64_t)blockIdx.x * span; base < ngroups; base += (int64_t)gridDim.x * span) {
-    rank_sums_streamed<In, C, G, CAP>(rows, nw, base, ngroups, [&](int k, const float* acc) {
+    rank_sums_streamed<In, C, G, CAP, BS>(rows, nw, base, ngroups, [&](int k, const float* acc) {
       f32x4 gv;
 #pragma unroll
       for (int e = 0; e < 4; ++e) gv[e] = SCALE ? div(acc[e]) * sc : div(acc[e]);
-      gl[k * kThreads + threadIdx.x] = gv;
+      gl[k * BS + threadIdx.x] = gv;
     });
     // phase 2: with bf16 contributions double-buffered (group k+1's state loads
     // are in flight while group k is updated and stored)
-    auto qidx = [&](int k) { return base + (int64_t)k * kThreads + threadIdx.x; };
+    auto qidx = [&](int k) { return base + (int64_t)k * BS + threadIdx.x; };
     auto load = [&](int k, f32x4& T, f32x4& M, f32x4& W) {
       const int64_t q = qidx(k) < ngroups ? qidx(k) : ngroups - 1;
       T = ld_nt(reinterpret_cast<const f32x4*>(th) + q);
@@ -56,7 +56,7 @@ __global__ __launch_bounds__(kThreads) void k_fused(RowTable<CAP> rows, int worl
     auto update = [&](int k, f32x4& T, f32x4& M, f32x4& W) {
       const int64_t qq = qidx(k);
       if (qq >= ngroups) return;
-      const f32x4 gv = gl[k * kThreads + threadIdx.x];
+      const f32x4 gv = gl[k * BS + threadIdx.x];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         float tt = T[e], mm = M[e], vv = W[e];
@@ -93,7 +93,7 @@ __global__ __launch_bounds__(kThreads) void k_fused(RowTable<CAP> rows, int worl
     }
   }
   if (blockIdx.x == 0) {  // ragged tail (fewer than 4 elements)
-    for (int64_t i = ngroups * 4 + threadIdx.x; i < n; i += kThreads) {
+    for (int64_t i = ngroups * 4 + threadIdx.x; i < n; i += BS) {
       float s = -0.0f;
       for (int r = 0; r < nw; ++r) s += L::scalar(rows.p[r], i);
       float gg = div(s);
@@ -136,66 +136,81 @@ __global__ __launch_bounds__(kThreads) void k_fused_scalar(RowTable<ZS_MAX_WORLD
 
 
 struct Shape {
+  int bs;      // workgroup size: 256 (4 waves) or 64 (one wave)
   int g;       // groups per lane staged in LDS
-  size_t lds;  // dynamic LDS bytes per workgroup (>= g * kThreads * 16)
+  size_t lds;  // dynamic LDS bytes per workgroup (>= g * bs * 16)
 };
 
-// Measured on MI355X: with many contributions the row walk dominates and deep
-// staging (16 groups in 64 KiB) is best; with few contributions the state
-// read-modify-write dominates and shallow staging (2 groups) under the same
-// 64 KiB reservation (2 workgroups per CU) is best.
+// Measured on MI355X. With many contributions the row walk dominates: 4-wave
+// workgroups with deep staging (16 groups in 64 KiB, 2 workgroups per CU) are
+// best. With few contributions the state read-modify-write dominates:
+// one-wave workgroups of a single group each, with a 16 KiB reservation (10
+// waves per CU), ran the Llama-3-8B shard at N=8 11% faster than 4-wave
+// workgroups (which were best with 2 groups and 64 KiB); residency matters
+// sharply there (5 waves per CU ran 35% slower, 20 waves 8% slower).
 Shape fused_shape(int world) {
   Shape sh;
-  sh.g = tuning().fused_g > 0 ? tuning().fused_g : (world >= 16 ? 16 : 2);
-  const size_t need = (size_t)sh.g * kThreads * 16;
-  sh.lds = tuning().fused_lds > 0 ? (size_t)tuning().fused_lds : 65536;
+  const bool many = world >= 16;
+  sh.bs = tuning().fused_bs > 0 ? tuning().fused_bs : (many ? 256 : 64);
+  sh.g = tuning().fused_g > 0 ? tuning().fused_g : (many ? 16 : 1);
+  if (sh.bs == 64 && sh.g > 4) sh.g = 4;  // one-wave workgroups are built for 1, 2 or 4 groups
+  const size_t need = (size_t)sh.g * sh.bs * 16;
+  sh.lds = tuning().fused_lds > 0 ? (size_t)tuning().fused_lds : (sh.bs == 64 ? 16384 : 65536);
   if (sh.lds < need) sh.lds = need;
   return sh;
 }
 
-template <int NW, int CAP, int G, int C, typename In>
+template <int NW, int CAP, int G, int C, int BS, typename In>
 void run_fused(const void* const* rows, int world, int64_t n, float* th, float* m, float* v,
                const AdamConsts& c, const float* scale, uint16_t* out, size_t lds, hipStream_t s) {
   RowTable<CAP> t;
   for (int i = 0; i < CAP; ++i) t.p[i] = i < world ? rows[i] : nullptr;
   const int64_t ngroups = n / 4;
-  const dim3 gd((unsigned)grid_for(ngroups, (int64_t)kThreads * G)), bd(kThreads);
+  const dim3 gd((unsigned)grid_for(ngroups, (int64_t)BS * G, BS)), bd(BS);
   const MeanDiv d = mean_div(world);
   if (out && scale)
-    hipLaunchKernelGGL((k_fused<NW, CAP, G, C, In, true, true>), gd, bd, lds, s, t, world, d, ngroups, n, th, m, v, c, scale, out);
+    hipLaunchKernelGGL((k_fused<NW, CAP, G, C, BS, In, true, true>), gd, bd, lds, s, t, world, d, ngroups, n, th, m, v, c, scale, out);
   else if (out)
-    hipLaunchKernelGGL((k_fused<NW, CAP, G, C, In, true, false>), gd, bd, lds, s, t, world, d, ngroups, n, th, m, v, c, scale, out);
+    hipLaunchKernelGGL((k_fused<NW, CAP, G, C, BS, In, true, false>), gd, bd, lds, s, t, world, d, ngroups, n, th, m, v, c, scale, out);
   else if (scale)
-    hipLaunchKernelGGL((k_fused<NW, CAP, G, C, In, false, true>), gd, bd, lds, s, t, world, d, ngroups, n, th, m, v, c, scale, out);
+    hipLaunchKernelGGL((k_fused<NW, CAP, G, C, BS, In, false, true>), gd, bd, lds, s, t, world, d, ngroups, n, th, m, v, c, scale, out);
   else
-    hipLaunchKernelGGL((k_fused<NW, CAP, G, C, In, false, false>), gd, bd, lds, s, t, world, d, ngroups, n, th, m, v, c, scale, out);
+    hipLaunchKernelGGL((k_fused<NW, CAP, G, C, BS, In, false, false>), gd, bd, lds, s, t, world, d, ngroups, n, th, m, v, c, scale, out);
 }
 
-template <typename In, int G, int C>
+template <typename In, int G, int C, int BS>
 void dispatch_world(const void* const* rows, int world, int64_t n, float* th, float* m, float* v,
                     const AdamConsts& c, const float* scale, uint16_t* out, size_t lds, hipStream_t s) {
   switch (world) {
-    case 2: run_fused<2, 2, G, C, In>(rows, world, n, th, m, v, c, scale, out, lds, s); break;
-    case 4: run_fused<4, 4, G, C, In>(rows, world, n, th, m, v, c, scale, out, lds, s); break;
-    case 8: run_fused<8, 8, G, C, In>(rows, world, n, th, m, v, c, scale, out, lds, s); break;
-    case 16: run_fused<16, 16, G, C, In>(rows, world, n, th, m, v, c, scale, out, lds, s); break;
-    case 32: run_fused<32, 32, G, C, In>(rows, world, n, th, m, v, c, scale, out, lds, s); break;
-    case 64: run_fused<64, 64, G, C, In>(rows, world, n, th, m, v, c, scale, out, lds, s); break;
+    case 2: run_fused<2, 2, G, C, BS, In>(rows, world, n, th, m, v, c, scale, out, lds, s); break;
+    case 4: run_fused<4, 4, G, C, BS, In>(rows, world, n, th, m, v, c, scale, out, lds, s); break;
+    case 8: run_fused<8, 8, G, C, BS, In>(rows, world, n, th, m, v, c, scale, out, lds, s); break;
+    case 16: run_fused<16, 16, G, C, BS, In>(rows, world, n, th, m, v, c, scale, out, lds, s); break;
+    case 32: run_fused<32, 32, G, C, BS, In>(rows, world, n, th, m, v, c, scale, out, lds, s); break;
+    case 64: run_fused<64, 64, G, C, BS, In>(rows, world, n, th, m, v, c, scale, out, lds, s); break;
     default:
-      if (world <= 64) run_fused<0, 64, G, C, In>(rows, world, n, th, m, v, c, scale, out, lds, s);
-      else run_fused<0, ZS_MAX_WORLD, G, C, In>(rows, world, n, th, m, v, c, scale, out, lds, s);
+      if (world <= 64) run_fused<0, 64, G, C, BS, In>(rows, world, n, th, m, v, c, scale, out, lds, s);
+      else run_fused<0, ZS_MAX_WORLD, G, C, BS, In>(rows, world, n, th, m, v, c, scale, out, lds, s);
   }
 }
 
 template <typename In, int C>
-void dispatch_g(int g, const void* const* rows, int world, int64_t n, float* th, float* m, float* v,
-                const AdamConsts& c, const float* scale, uint16_t* out, size_t lds, hipStream_t s) {
-  switch (g) {
-    case 1: dispatch_world<In, 1, C>(rows, world, n, th, m, v, c, scale, out, lds, s); break;
-    case 2: dispatch_world<In, 2, C>(rows, world, n, th, m, v, c, scale, out, lds, s); break;
-    case 8: dispatch_world<In, 8, C>(rows, world, n, th, m, v, c, scale, out, lds, s); break;
-    case 16: dispatch_world<In, 16, C>(rows, world, n, th, m, v, c, scale, out, lds, s); break;
-    default: dispatch_world<In, 4, C>(rows, world, n, th, m, v, c, scale, out, lds, s); break;
+void dispatch_g(const Shape& sh, const void* const* rows, int world, int64_t n, float* th, float* m,
+                float* v, const AdamConsts& c, const float* scale, uint16_t* out, hipStream_t s) {
+  if (sh.bs == 64) {
+    switch (sh.g) {
+      case 2: dispatch_world<In, 2, C, 64>(rows, world, n, th, m, v, c, scale, out, sh.lds, s); break;
+      case 4: dispatch_world<In, 4, C, 64>(rows, world, n, th, m, v, c, scale, out, sh.lds, s); break;
+      default: dispatch_world<In, 1, C, 64>(rows, world, n, th, m, v, c, scale, out, sh.lds, s); break;
+    }
+    return;
+  }
+  switch (sh.g) {
+    case 1: dispatch_world<In, 1, C, 256>(rows, world, n, th, m, v, c, scale, out, sh.lds, s); break;
+    case 2: dispatch_world<In, 2, C, 256>(rows, world, n, th, m, v, c, scale, out, sh.lds, s); break;
+    case 8: dispatch_world<In, 8, C, 256>(rows, world, n, th, m, v, c, scale, out, sh.lds, s); break;
+    case 16: dispatch_world<In, 16, C, 256>(rows, world, n, th, m, v, c, scale, out, sh.lds, s); break;
+    default: dispatch_world<In, 4, C, 256>(rows, world, n, th, m, v, c, scale, out, sh.lds, s); break;
   }
 }
 
@@ -203,8 +218,8 @@ template <typename In>
 void dispatch(const void* const* rows, int world, int64_t n, float* th, float* m, float* v,
               const AdamConsts& c, const float* scale, uint16_t* out, hipStream_t s) {
   const Shape sh = fused_shape(world);
-  if (tuning().rank_chunk == 4) dispatch_g<In, 4>(sh.g, rows, world, n, th, m, v, c, scale, out, sh.lds, s);
-  else dispatch_g<In, 8>(sh.g, rows, world, n, th, m, v, c, scale, out, sh.lds, s);
+  if (tuning().rank_chunk == 4) dispatch_g<In, 4>(sh, rows, world, n, th, m, v, c, scale, out, s);
+  else dispatch_g<In, 8>(sh, rows, world, n, th, m, v, c, scale, out, s);
 }
 
 

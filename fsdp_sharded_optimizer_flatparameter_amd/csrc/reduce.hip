@@ -128,10 +128,8 @@ hipError_t run_vec(const void* const* rows, int world, int64_t n, float* g, doub
   for (int i = 0; i < CAP; ++i) t.p[i] = i < world ? rows[i] : nullptr;
   const int64_t ngroups = n / 4;
   const int64_t span = (int64_t)kThreads * G;
-  int64_t grid = (ngroups + span - 1) / span;
-  if (grid > tuning().grid_cap) grid = tuning().grid_cap;
+  int64_t grid = grid_for(ngroups, span);
   if (partials && grid > max_partials(n)) grid = max_partials(n);
-  if (grid < 1) grid = 1;
   *grid_out = grid;
   const size_t lds = G > 1 ? (size_t)G * kThreads * 16 : 0;
   if (partials)

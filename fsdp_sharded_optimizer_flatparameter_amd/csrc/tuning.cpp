@@ -1,5 +1,6 @@
 // Launch-shape knobs of the streaming kernels and the sum-of-squares workspace
 // bound. Host code only.
+#include <cstdint>
 #include <cstdlib>
 
 #include "zs_launch.hpp"
@@ -8,7 +9,7 @@ namespace zs {
 
 const Tuning& tuning() {
   static const Tuning t = [] {
-    Tuning x{0, 0, 0, 0, 0, 0, 0};
+    Tuning x{0, 0, 0, 0, 0, 0, 0, 0};
     const char* e;
     x.adamw_v = (e = std::getenv("ZS_ADAMW_V")) ? std::atoi(e) : 1;
     if (x.adamw_v != 1 && x.adamw_v != 2 && x.adamw_v != 4) x.adamw_v = 1;
@@ -21,12 +22,14 @@ const Tuning& tuning() {
     if (x.fused_g != 1 && x.fused_g != 2 && x.fused_g != 4 && x.fused_g != 8 && x.fused_g != 16) x.fused_g = 0;
     x.fused_lds = (e = std::getenv("ZS_FUSED_LDS")) ? std::atoll(e) : 0;
     if (x.fused_lds < 0 || x.fused_lds > 65536) x.fused_lds = 0;
+    x.fused_bs = (e = std::getenv("ZS_FUSED_BS")) ? std::atoi(e) : 0;
+    if (x.fused_bs != 64 && x.fused_bs != 256) x.fused_bs = 0;
     x.reduce_g = (e = std::getenv("ZS_REDUCE_G")) ? std::atoi(e) : 0;
     if (x.reduce_g != 1 && x.reduce_g != 4 && x.reduce_g != 16) x.reduce_g = 0;
+    // an optional cap on workgroups per launch (grid-stride loops cover the
+    // rest); launches also stay within the 32-bit work-item count of a dispatch
     x.grid_cap = (e = std::getenv("ZS_GRID_CAP")) ? std::atoll(e) : 0;
-    // gridDim.x * blockDim.x must stay below 2^32; grid-stride loops cover the rest
-    const int64_t kHardCap = int64_t(1) << 22;
-    if (x.grid_cap <= 0 || x.grid_cap > kHardCap) x.grid_cap = kHardCap;
+    if (x.grid_cap <= 0) x.grid_cap = INT64_MAX;
     return x;
   }();
   return t;

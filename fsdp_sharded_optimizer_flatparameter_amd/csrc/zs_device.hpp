@@ -105,7 +105,8 @@ struct Lanes<float> {
   }
 };
 
-// Rank sums of G groups per lane -- group k at index base + k*kThreads + lane --
+// Rank sums of G groups per lane -- group k at index base + k*BS + lane, BS the
+// workgroup size --
 // streamed as one double-buffered sequence of rank chunks that runs across
 // group boundaries: while chunk i is added, chunk i+1 (the next ranks of the
 // same group, or the first ranks of the next group) is already in flight, so a
@@ -114,7 +115,7 @@ struct Lanes<float> {
 // every x, signed zeros included), and adds ranks in ascending order, so it
 // equals c_0 + c_1 + ... + c_{N-1} evaluated left to right in fp32.
 // sink(k, acc) receives group k's finished sums.
-template <typename In, int C, int G, int CAP, typename Sink>
+template <typename In, int C, int G, int CAP, int BS = kThreads, typename Sink>
 __device__ __forceinline__ void rank_sums_streamed(const RowTable<CAP>& rows, int nw, int64_t base,
                                                    int64_t ngroups, Sink&& sink) {
   using L = Lanes<In>;
@@ -124,7 +125,7 @@ __device__ __forceinline__ void rank_sums_streamed(const RowTable<CAP>& rows, in
   auto load = [&](int idx, Vec* buf) {
     const int k = idx / nch;
     const int r0 = (idx - k * nch) * C;
-    const int64_t qq = base + (int64_t)k * kThreads + threadIdx.x;
+    const int64_t qq = base + (int64_t)k * BS + threadIdx.x;
     const int64_t q = qq < ngroups ? qq : ngroups - 1;  // clamped: loads stay in bounds
 #pragma unroll
     for (int u = 0; u < C; ++u)

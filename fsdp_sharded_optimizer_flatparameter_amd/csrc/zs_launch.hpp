@@ -14,22 +14,26 @@ struct AdamConsts;
 // Launch-shape knobs. Defaults are the measured best on MI355X; each can be
 // overridden once per process through the environment (ZS_ADAMW_V,
 // ZS_ADAMW_LDS, ZS_RANK_CHUNK, ZS_FUSED_G,
-// ZS_FUSED_LDS, ZS_REDUCE_G, ZS_GRID_CAP) for sweeps. None of them changes any result.
+// ZS_FUSED_LDS, ZS_FUSED_BS, ZS_REDUCE_G, ZS_GRID_CAP) for sweeps. None of them changes any result.
 struct Tuning {
   int adamw_v;     // 16-byte groups per lane per tile in AdamW (1, 2 or 4)
   int64_t adamw_lds;  // LDS bytes reserved per AdamW workgroup (caps residency)
   int rank_chunk;  // ranks per load chunk of the double-buffered rank walk (4 or 8)
   int fused_g;     // groups per lane staged in LDS by the single-pass kernel (0 = by world size)
   int64_t fused_lds;  // LDS bytes reserved per workgroup of the single-pass kernel (0 = default)
+  int fused_bs;    // workgroup size of the single-pass kernel (64 or 256; 0 = by world size)
   int reduce_g;    // groups per lane staged in LDS by the reduce kernel (0 = by world size)
   int64_t grid_cap;  // upper bound on workgroups of the streaming kernels
 };
 const Tuning& tuning();
 
 // Workgroups of a streaming launch over `units` work items, `per_block` per
-// workgroup, capped by the grid cap (the kernels grid-stride past it).
-inline int64_t grid_for(int64_t units, int64_t per_block) {
+// workgroup of `threads` lanes, capped by the grid cap and by the 32-bit
+// work-item count of a dispatch (the kernels grid-stride past the cap).
+inline int64_t grid_for(int64_t units, int64_t per_block, int64_t threads = 256) {
   int64_t g = (units + per_block - 1) / per_block;
+  const int64_t hard = (int64_t)0xffffffff / threads;
+  if (g > hard) g = hard;
   if (g > tuning().grid_cap) g = tuning().grid_cap;
   return g < 1 ? 1 : g;
 }
