@@ -37,22 +37,22 @@ AdamConsts adam_consts(const zs_adamw_hparams& hp) {
 
 namespace {
 
-template <int V, bool CAST, bool SCALE>
-__global__ __launch_bounds__(kThreads) void k_adamw(float* __restrict__ th, float* __restrict__ m,
+template <int V, int BS, bool CAST, bool SCALE>
+__global__ __launch_bounds__(BS) void k_adamw(float* __restrict__ th, float* __restrict__ m,
                                                     float* __restrict__ v,
                                                     const float* __restrict__ g, int64_t ngroups,
                                                     int64_t n, AdamConsts c,
                                                     const float* __restrict__ scale,
                                                     uint16_t* __restrict__ out) {
   const float sc = SCALE ? *scale : 1.0f;
-  const int64_t tile = (int64_t)kThreads * V;
+  const int64_t tile = (int64_t)BS * V;
   for (int64_t base = (int64_t)blockIdx.x * tile; base < ngroups;
        base += (int64_t)gridDim.x * tile) {
     int64_t q[V];
     f32x4 G[V], T[V], M[V], W[V];
 #pragma unroll
     for (int j = 0; j < V; ++j) {
-      const int64_t qq = base + threadIdx.x + (int64_t)j * kThreads;
+      const int64_t qq = base + threadIdx.x + (int64_t)j * BS;
       q[j] = qq < ngroups ? qq : ngroups - 1;
       G[j] = ld_nt(reinterpret_cast<const f32x4*>(g) + q[j]);
       T[j] = ld_nt(reinterpret_cast<const f32x4*>(th) + q[j]);
@@ -61,7 +61,7 @@ __global__ __launch_bounds__(kThreads) void k_adamw(float* __restrict__ th, floa
     }
 #pragma unroll
     for (int j = 0; j < V; ++j) {
-      if (base + threadIdx.x + (int64_t)j * kThreads >= ngroups) continue;
+      if (base + threadIdx.x + (int64_t)j * BS >= ngroups) continue;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         float tt = T[j][e], mm = M[j][e], vv = W[j][e];
@@ -81,7 +81,7 @@ __global__ __launch_bounds__(kThreads) void k_adamw(float* __restrict__ th, floa
     }
   }
   if (blockIdx.x == 0) {  // ragged tail
-    for (int64_t i = ngroups * 4 + threadIdx.x; i < n; i += kThreads) {
+    for (int64_t i = ngroups * 4 + threadIdx.x; i < n; i += BS) {
       float tt = th[i], mm = m[i], vv = v[i];
       const float gg = SCALE ? g[i] * sc : g[i];
       adamw_elem(tt, mm, vv, gg, c);
@@ -115,29 +115,29 @@ __global__ __launch_bounds__(kThreads) void k_adamw_scalar(float* __restrict__ t
   }
 }
 
-template <int V>
-__global__ __launch_bounds__(kThreads) void k_cast(const float* __restrict__ src, int64_t ngroups,
+template <int V, int BS>
+__global__ __launch_bounds__(BS) void k_cast(const float* __restrict__ src, int64_t ngroups,
                                                    int64_t n, uint16_t* __restrict__ out) {
-  const int64_t tile = (int64_t)kThreads * V;
+  const int64_t tile = (int64_t)BS * V;
   for (int64_t base = (int64_t)blockIdx.x * tile; base < ngroups;
        base += (int64_t)gridDim.x * tile) {
     f32x4 x[V];
     int64_t q[V];
 #pragma unroll
     for (int j = 0; j < V; ++j) {
-      const int64_t qq = base + threadIdx.x + (int64_t)j * kThreads;
+      const int64_t qq = base + threadIdx.x + (int64_t)j * BS;
       q[j] = qq < ngroups ? qq : ngroups - 1;
       x[j] = ld_nt(reinterpret_cast<const f32x4*>(src) + q[j]);
     }
 #pragma unroll
     for (int j = 0; j < V; ++j) {
-      if (base + threadIdx.x + (int64_t)j * kThreads >= ngroups) continue;
+      if (base + threadIdx.x + (int64_t)j * BS >= ngroups) continue;
       const u32x2 b{pack_bf16x2(x[j][0], x[j][1]), pack_bf16x2(x[j][2], x[j][3])};
       st_nt(b, reinterpret_cast<u32x2*>(out) + q[j]);
     }
   }
   if (blockIdx.x == 0)
-    for (int64_t i = ngroups * 4 + threadIdx.x; i < n; i += kThreads)
+    for (int64_t i = ngroups * 4 + threadIdx.x; i < n; i += BS)
       out[i] = (uint16_t)f32_to_bf16(src[i]);
 }
 
@@ -148,12 +148,16 @@ __global__ __launch_bounds__(kThreads) void k_cast_scalar(const float* __restric
     out[i] = (uint16_t)f32_to_bf16(src[i]);
 }
 
+// One-wave workgroups under a 16 KiB reservation (10 waves per CU) measured
+// 7% faster than 4-wave workgroups under 32 KiB.
+constexpr int kAdamBS = 64;
+
 template <int V, bool CAST, bool SCALE>
 void run_adamw(float* th, float* m, float* v, const float* g, int64_t n, const AdamConsts& c,
                const float* scale, uint16_t* out, hipStream_t s) {
   const int64_t ngroups = n / 4;
-  const int64_t grid = grid_for(ngroups, (int64_t)kThreads * V);
-  hipLaunchKernelGGL((k_adamw<V, CAST, SCALE>), dim3((unsigned)grid), dim3(kThreads),
+  const int64_t grid = grid_for(ngroups, (int64_t)kAdamBS * V, kAdamBS);
+  hipLaunchKernelGGL((k_adamw<V, kAdamBS, CAST, SCALE>), dim3((unsigned)grid), dim3(kAdamBS),
                      (size_t)tuning().adamw_lds, s, th, m, v, g, ngroups, n, c, scale, out);
 }
 
@@ -194,8 +198,8 @@ hipError_t launch_cast(const float* src, int64_t n, uint16_t* out, hipStream_t s
   if (n == 0) return hipSuccess;
   if (aligned_to(src, 16) && aligned_to(out, 8)) {
     const int64_t ngroups = n / 4;
-    const dim3 gd((unsigned)grid_for(ngroups, 2 * kThreads));
-    hipLaunchKernelGGL((k_cast<2>), gd, dim3(kThreads), 0, s, src, ngroups, n, out);
+    const dim3 gd((unsigned)grid_for(ngroups, 2 * kAdamBS, kAdamBS));
+    hipLaunchKernelGGL((k_cast<2, kAdamBS>), gd, dim3(kAdamBS), 0, s, src, ngroups, n, out);
   } else {
     const dim3 gd((unsigned)grid_for(n, 4 * kThreads));
     hipLaunchKernelGGL(k_cast_scalar, gd, dim3(kThreads), 0, s, src, n, out);

@@ -13,9 +13,9 @@ const Tuning& tuning() {
     const char* e;
     x.adamw_v = (e = std::getenv("ZS_ADAMW_V")) ? std::atoi(e) : 1;
     if (x.adamw_v != 1 && x.adamw_v != 2 && x.adamw_v != 4) x.adamw_v = 1;
-    // a 32 KiB reservation (4 workgroups per CU) measured best for AdamW and the cast
-    x.adamw_lds = (e = std::getenv("ZS_ADAMW_LDS")) ? std::atoll(e) : 32768;
-    if (x.adamw_lds < 0 || x.adamw_lds > 65536) x.adamw_lds = 32768;
+    // a 16 KiB reservation (10 one-wave workgroups per CU) measured best for AdamW
+    x.adamw_lds = (e = std::getenv("ZS_ADAMW_LDS")) ? std::atoll(e) : 16384;
+    if (x.adamw_lds < 0 || x.adamw_lds > 65536) x.adamw_lds = 16384;
     x.rank_chunk = (e = std::getenv("ZS_RANK_CHUNK")) ? std::atoi(e) : 8;
     if (x.rank_chunk != 4 && x.rank_chunk != 8) x.rank_chunk = 8;
     x.fused_g = (e = std::getenv("ZS_FUSED_G")) ? std::atoi(e) : 0;
@@ -36,10 +36,11 @@ const Tuning& tuning() {
 }
 
 int64_t max_partials(int64_t n) {
-  // every sum-of-squares launch uses at most one workgroup per 1024 elements
-  // (one tile), up to the hard grid cap beyond which launches grid-stride
-  const int64_t b = (n + 1023) / 1024;
-  const int64_t kMax = int64_t(1) << 22;
+  // every sum-of-squares launch uses at most one workgroup per 256 elements
+  // (the smallest tile: one wave, one group per lane), up to a cap beyond
+  // which launches grid-stride
+  const int64_t b = (n + 255) / 256;
+  const int64_t kMax = (int64_t(1) << 24) - 1;  // x 256 lanes stays a 32-bit dispatch
   return b < 1 ? 1 : (b > kMax ? kMax : b);
 }
 

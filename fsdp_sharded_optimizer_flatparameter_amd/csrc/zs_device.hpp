@@ -200,14 +200,15 @@ __device__ __forceinline__ void adamw_elem(float& th, float& m, float& v, float 
 
 // ---- block reduction of per-thread fp64 partials (fixed order) ------------------
 
-__device__ __forceinline__ double block_sum_fixed(double x, double* lds /* >= kThreads/64 */) {
+template <int BS = kThreads>
+__device__ __forceinline__ double block_sum_fixed(double x, double* lds /* >= BS/64 */) {
   for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
   const int wave = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) lds[wave] = x;
   __syncthreads();
   double s = 0.0;
   if (threadIdx.x == 0) {
-    for (int w = 0; w < kThreads / 64; ++w) s += lds[w];
+    for (int w = 0; w < BS / 64; ++w) s += lds[w];
   }
   return s;  // valid in thread 0
 }

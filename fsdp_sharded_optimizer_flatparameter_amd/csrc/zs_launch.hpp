@@ -43,7 +43,7 @@ inline bool aligned_to(const void* p, unsigned a) {
 }
 
 // Largest number of first-level partial sums a sum-of-squares launch over n
-// elements writes (one per 1024-element tile, capped with the grid); the
+// elements writes (one per tile of at least 256 elements, capped); the
 // workspace holds that many doubles plus kFinalizeBlocks.
 int64_t max_partials(int64_t n);
 // Second-level partials the sum-of-squares finalize may use, stored after the

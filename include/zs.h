@@ -184,9 +184,10 @@ zs_status zs_reduce_grads(const void* const* rows, int32_t world, int32_t dtype,
                           size_t workspace_bytes, hipStream_t stream);
 
 /* Bytes of workspace zs_reduce_grads / zs_accumulate_grads need for a sum of
- * squares over n elements: one fp64 partial per 1024-element tile (at most 2^22
- * of them) plus 256 second-level partials; 0 for n < 0. The contents need no
- * initialisation and are overwritten by every call that takes a sum of squares. */
+ * squares over n elements: one fp64 partial per 256-element tile (at most
+ * 2^24 - 1 of them) plus 256 second-level partials; 0 for n < 0. The contents
+ * need no initialisation and are overwritten by every call that takes a sum of
+ * squares. */
 size_t zs_workspace_bytes(int64_t n);
 
 /*

@@ -110,12 +110,12 @@ def test_check_layout(lib):
 
 
 def test_workspace_bytes(lib):
-    # one fp64 partial per 1024-element tile (at most 2^22), plus 256 second-level partials
+    # one fp64 partial per 256-element tile (at most 2^24 - 1), plus 256 second-level partials
     assert lib.zs_workspace_bytes(0) == 8 * (1 + 256)
-    assert lib.zs_workspace_bytes(1024) == 8 * (1 + 256)
-    assert lib.zs_workspace_bytes(1025) == 8 * (2 + 256)
-    assert lib.zs_workspace_bytes(117_187_500) == 8 * (114_441 + 256)
-    assert lib.zs_workspace_bytes(1 << 40) == 8 * ((1 << 22) + 256)
+    assert lib.zs_workspace_bytes(256) == 8 * (1 + 256)
+    assert lib.zs_workspace_bytes(257) == 8 * (2 + 256)
+    assert lib.zs_workspace_bytes(117_187_500) == 8 * (457_764 + 256)
+    assert lib.zs_workspace_bytes(1 << 40) == 8 * ((1 << 24) - 1 + 256)
     assert lib.zs_workspace_bytes(-1) == 0
 
 

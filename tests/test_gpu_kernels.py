@@ -94,7 +94,7 @@ def test_reduce_propagates_nonfinite_to_exactly_the_affected_elements():
 
 @pytest.mark.parametrize("n, world", [(3_000_001, 16), (8_388_611, 8)])
 def test_reduce_is_deterministic(n, world):
-    # the second case has one partial per 1024-element tile (8193 of them), which
+    # the second case has one partial per 256-element tile (32,768 of them), which
     # takes the two-level finalize
     rows = device_rows(11, world, n, "bf16")
     g1, s1 = _reduce(rows, n, sumsq=True)
