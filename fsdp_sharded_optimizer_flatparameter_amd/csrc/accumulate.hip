@@ -18,51 +18,51 @@
 namespace zs {
 namespace {
 
-// G groups per lane (G*1024 consecutive elements per workgroup pass), in three
+// G groups per lane (G*BS*4 consecutive elements per workgroup pass), in three
 // steps: the previous sums of all G groups are loaded into lane-private LDS
 // slots, the rank walk adds each group's scaled mean into its slot, and the G
 // results are written back as one burst of 16-byte stores. The row walk then
 // runs without a write stream beside it, and the LDS reservation caps the
 // workgroups resident per CU.
-template <int NW, int CAP, int G, typename In, bool SUMSQ, bool FIRST, bool SCALE>
-__global__ __launch_bounds__(kThreads) void k_accum(RowTable<CAP> rows, int world, MeanDiv div,
+template <int NW, int CAP, int G, int BS, typename In, bool SUMSQ, bool FIRST, bool SCALE>
+__global__ __launch_bounds__(BS) void k_accum(RowTable<CAP> rows, int world, MeanDiv div,
                                                     float scale, int64_t ngroups, int64_t n,
                                                     float* __restrict__ acc,
                                                     double* __restrict__ partials) {
   using L = Lanes<In>;
-  extern __shared__ f32x4 slot[];  // G * kThreads lane-private slots
+  extern __shared__ f32x4 slot[];  // G * BS lane-private slots
   const int nw = NW > 0 ? NW : world;
-  const int64_t span = (int64_t)kThreads * G;
+  const int64_t span = (int64_t)BS * G;
   double ss = 0.0;
   for (int64_t base = (int64_t)blockIdx.x * span; base < ngroups; base += (int64_t)gridDim.x * span) {
     if (!FIRST) {
 #pragma unroll
       for (int k = 0; k < G; ++k) {
-        const int64_t qq = base + (int64_t)k * kThreads + threadIdx.x;
+        const int64_t qq = base + (int64_t)k * BS + threadIdx.x;
         const int64_t q = qq < ngroups ? qq : ngroups - 1;
-        slot[k * kThreads + threadIdx.x] = ld_nt(reinterpret_cast<const f32x4*>(acc) + q);
+        slot[k * BS + threadIdx.x] = ld_nt(reinterpret_cast<const f32x4*>(acc) + q);
       }
     }
-    rank_sums_streamed<In, 8, G, CAP>(rows, nw, base, ngroups, [&](int k, const float* s) {
-      const int64_t qq = base + (int64_t)k * kThreads + threadIdx.x;
+    rank_sums_streamed<In, 8, G, CAP, BS>(rows, nw, base, ngroups, [&](int k, const float* s) {
+      const int64_t qq = base + (int64_t)k * BS + threadIdx.x;
       f32x4 o;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         float u = div(s[e]);
         if (SCALE) u *= scale;
-        o[e] = FIRST ? u : slot[k * kThreads + threadIdx.x][e] + u;
+        o[e] = FIRST ? u : slot[k * BS + threadIdx.x][e] + u;
         if (SUMSQ && qq < ngroups) ss = fma((double)o[e], (double)o[e], ss);
       }
-      slot[k * kThreads + threadIdx.x] = o;
+      slot[k * BS + threadIdx.x] = o;
     });
     for (int k = 0; k < G; ++k) {  // each lane writes back only its own slots
-      const int64_t qq = base + (int64_t)k * kThreads + threadIdx.x;
+      const int64_t qq = base + (int64_t)k * BS + threadIdx.x;
       if (qq >= ngroups) break;
-      st_nt(slot[k * kThreads + threadIdx.x], reinterpret_cast<f32x4*>(acc) + qq);
+      st_nt(slot[k * BS + threadIdx.x], reinterpret_cast<f32x4*>(acc) + qq);
     }
   }
   if (blockIdx.x == 0) {  // ragged tail
-    for (int64_t i = ngroups * 4 + threadIdx.x; i < n; i += kThreads) {
+    for (int64_t i = ngroups * 4 + threadIdx.x; i < n; i += BS) {
       float s = -0.0f;
       for (int r = 0; r < nw; ++r) s += L::scalar(rows.p[r], i);
       float u = div(s);
@@ -73,8 +73,8 @@ __global__ __launch_bounds__(kThreads) void k_accum(RowTable<CAP> rows, int worl
     }
   }
   if (SUMSQ) {
-    __shared__ double lds[kThreads / 64];
-    const double b = block_sum_fixed(ss, lds);
+    __shared__ double lds[BS / 64];
+    const double b = block_sum_fixed<BS>(ss, lds);
     if (threadIdx.x == 0) partials[blockIdx.x] = b;
   }
 }
@@ -147,25 +147,33 @@ __global__ void k_clip(const double* __restrict__ partials, int count, double ma
 }
 
 
-// Measured on MI355X: 16 groups per lane (64 KiB of LDS, two workgroups per
-// CU) with many contributions, as for the reduce; 4 groups with few.
+// Measured on MI355X: with many contributions 16 groups per lane in 4-wave
+// workgroups (64 KiB of LDS, two workgroups per CU), as for the reduce; with
+// few, the shape of the single pass (ZS_ACCUM_SHAPE=1 selects the earlier
+// 4 groups per lane in 4-wave workgroups for comparison).
+template <int G, int BS, int NW, int CAP, typename In, bool SUMSQ, bool FIRST, bool SCALE>
+void launch_accum_shape(const RowTable<CAP>& t, int world, int64_t n, float* acc, float scale,
+                        double* partials, int64_t* grid_out, size_t lds, hipStream_t s) {
+  const int64_t ngroups = n / 4;
+  int64_t grid = grid_for(ngroups, (int64_t)BS * G, BS);
+  if (SUMSQ && grid > max_partials(n)) grid = max_partials(n);
+  *grid_out = grid;
+  if (lds < (size_t)G * BS * sizeof(f32x4)) lds = (size_t)G * BS * sizeof(f32x4);
+  hipLaunchKernelGGL((k_accum<NW, CAP, G, BS, In, SUMSQ, FIRST, SCALE>), dim3((unsigned)grid),
+                     dim3(BS), lds, s, t, world, mean_div(world), scale, ngroups, n, acc, partials);
+}
+
 template <int NW, int CAP, typename In, bool SUMSQ, bool FIRST, bool SCALE>
 void run_accum(const void* const* rows, int world, int64_t n, float* acc, float scale,
                double* partials, int64_t* grid_out, hipStream_t s) {
   RowTable<CAP> t;
   for (int i = 0; i < CAP; ++i) t.p[i] = i < world ? rows[i] : nullptr;
-  const int64_t ngroups = n / 4;
-  const int g = world >= 16 ? 16 : 4;
-  int64_t grid = grid_for(ngroups, (int64_t)kThreads * g);
-  if (SUMSQ && grid > max_partials(n)) grid = max_partials(n);
-  *grid_out = grid;
-  const size_t lds = (size_t)g * kThreads * sizeof(f32x4);
-  if (g == 16)
-    hipLaunchKernelGGL((k_accum<NW, CAP, 16, In, SUMSQ, FIRST, SCALE>), dim3((unsigned)grid),
-                       dim3(kThreads), lds, s, t, world, mean_div(world), scale, ngroups, n, acc, partials);
+  if (world >= 16)
+    launch_accum_shape<16, 256, NW, CAP, In, SUMSQ, FIRST, SCALE>(t, world, n, acc, scale, partials, grid_out, 0, s);
+  else if (tuning().accum_shape == 1)
+    launch_accum_shape<4, 256, NW, CAP, In, SUMSQ, FIRST, SCALE>(t, world, n, acc, scale, partials, grid_out, 0, s);
   else
-    hipLaunchKernelGGL((k_accum<NW, CAP, 4, In, SUMSQ, FIRST, SCALE>), dim3((unsigned)grid),
-                       dim3(kThreads), lds, s, t, world, mean_div(world), scale, ngroups, n, acc, partials);
+    launch_accum_shape<1, 64, NW, CAP, In, SUMSQ, FIRST, SCALE>(t, world, n, acc, scale, partials, grid_out, 16384, s);
 }
 
 template <typename In, bool SUMSQ, bool FIRST, bool SCALE>

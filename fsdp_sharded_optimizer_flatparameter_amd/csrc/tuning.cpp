@@ -9,7 +9,7 @@ namespace zs {
 
 const Tuning& tuning() {
   static const Tuning t = [] {
-    Tuning x{0, 0, 0, 0, 0, 0, 0, 0};
+    Tuning x{0, 0, 0, 0, 0, 0, 0, 0, 0};
     const char* e;
     x.adamw_v = (e = std::getenv("ZS_ADAMW_V")) ? std::atoi(e) : 1;
     if (x.adamw_v != 1 && x.adamw_v != 2 && x.adamw_v != 4) x.adamw_v = 1;
@@ -24,6 +24,8 @@ const Tuning& tuning() {
     if (x.fused_lds < 0 || x.fused_lds > 65536) x.fused_lds = 0;
     x.fused_bs = (e = std::getenv("ZS_FUSED_BS")) ? std::atoi(e) : 0;
     if (x.fused_bs != 64 && x.fused_bs != 256) x.fused_bs = 0;
+    x.accum_shape = (e = std::getenv("ZS_ACCUM_SHAPE")) ? std::atoi(e) : 0;
+    if (x.accum_shape != 1) x.accum_shape = 0;
     x.reduce_g = (e = std::getenv("ZS_REDUCE_G")) ? std::atoi(e) : 0;
     if (x.reduce_g != 1 && x.reduce_g != 4 && x.reduce_g != 16) x.reduce_g = 0;
     // an optional cap on workgroups per launch (grid-stride loops cover the

@@ -14,7 +14,7 @@ struct AdamConsts;
 // Launch-shape knobs. Defaults are the measured best on MI355X; each can be
 // overridden once per process through the environment (ZS_ADAMW_V,
 // ZS_ADAMW_LDS, ZS_RANK_CHUNK, ZS_FUSED_G,
-// ZS_FUSED_LDS, ZS_FUSED_BS, ZS_REDUCE_G, ZS_GRID_CAP) for sweeps. None of them changes any result.
+// ZS_FUSED_LDS, ZS_FUSED_BS, ZS_ACCUM_SHAPE, ZS_REDUCE_G, ZS_GRID_CAP) for sweeps. None of them changes any result.
 struct Tuning {
   int adamw_v;     // 16-byte groups per lane per tile in AdamW (1, 2 or 4)
   int64_t adamw_lds;  // LDS bytes reserved per AdamW workgroup (caps residency)
@@ -22,6 +22,7 @@ struct Tuning {
   int fused_g;     // groups per lane staged in LDS by the single-pass kernel (0 = by world size)
   int64_t fused_lds;  // LDS bytes reserved per workgroup of the single-pass kernel (0 = default)
   int fused_bs;    // workgroup size of the single-pass kernel (64 or 256; 0 = by world size)
+  int accum_shape;  // ZeRO-2 accumulation with few contributions: 0 one-wave, 1 four-wave
   int reduce_g;    // groups per lane staged in LDS by the reduce kernel (0 = by world size)
   int64_t grid_cap;  // upper bound on workgroups of the streaming kernels
 };
