@@ -11,8 +11,9 @@
 // Design (HBM-bound, 2N+4 bytes per element for bf16 contributions):
 //   * each lane owns groups of 4 consecutive elements, lane-contiguous in
 //     every stream (8-byte bf16 / 16-byte fp32 row loads, 16-byte g stores);
-//   * with many contributions, a workgroup parks 16 groups per lane in LDS and
-//     writes them as one burst after the rank walk;
+//   * with many contributions, a 4-wave workgroup parks 16 groups per lane in
+//     LDS and writes them as one burst after the rank walk; with few, one-wave
+//     workgroups store each group as soon as it is summed;
 //   * row pointers sit in the kernel-argument segment (SGPR bases);
 //   * ranks are walked in double-buffered chunks of C: a chunk's loads are in
 //     flight while the previous chunk is added, and the fp32 sum still runs
