@@ -391,6 +391,10 @@ def main() -> int:
         gbs = 4 * sum(bn) / (t_co * 1e-3) / 1e9
         parts[f"copy_out_{blk_name}"] = dict(ms=round(t_co, 5), elems=sum(bn), bytes_per_elem=4,
                                                gb_s=round(gbs, 1), frac_of_peak=round(gbs / PEAK_HBM_GBS, 4))
+        if big:
+            # with reshard_after_forward every one of the 80 blocks is unsharded
+            # twice per step (forward and backward): the step's copy-out time
+            parts["copy_out_70b_per_step_ms"] = round(t_co * 160, 3)
         # the same block under per-parameter dim-0 sharding (a scatter from the N rank
         # regions of the gather buffer)
         dtable = zs.Dim0Table(dst, blk_world)
