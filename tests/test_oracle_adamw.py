@@ -121,6 +121,49 @@ def test_worked_example_from_the_page():
     assert [round(float(x), 6) for x in th_b] == want_th
 
 
+def test_composed_step_matches_torch_over_steps():
+    # The rank's step -- mean of N bf16 contributions, AdamW on its fp32 slice,
+    # bf16 of the new master -- against torch: the mean of the decoded rows in
+    # fp64, torch.optim.AdamW in fp64 started each step from the oracle's fp32
+    # state, and torch's own fp32 -> bf16 cast.
+    world, n = 4, 2048
+    theta = gen.host_normal(31, n, 0.02)
+    m = np.zeros(n, np.float32)
+    v = np.zeros(n, np.float32)
+    p = torch.nn.Parameter(torch.zeros(n, dtype=torch.float64))
+    opt = torch.optim.AdamW([p], lr=HP.lr, betas=(HP.beta1, HP.beta2), eps=HP.eps,
+                            weight_decay=HP.weight_decay, foreach=False, fused=False)
+    for t in range(1, 6):
+        rows = gen.host_grad_rows(40 + t, world, n, "bf16")
+        with torch.no_grad():
+            p.copy_(torch.from_numpy(theta.astype(np.float64)))
+            if t > 1:
+                opt.state[p]["exp_avg"].copy_(torch.from_numpy(m.astype(np.float64)))
+                opt.state[p]["exp_avg_sq"].copy_(torch.from_numpy(v.astype(np.float64)))
+        g, theta, m, v, out = step.sharded_step(rows, theta, m, v, t, HP)
+        rows_t = torch.from_numpy(rows.astype(np.int16)).view(torch.bfloat16).to(torch.float64)
+        want_g = rows_t.mean(dim=0).to(torch.float32)
+        assert np.array_equal(g, want_g.numpy())
+        p.grad = want_g.to(torch.float64)
+        opt.step()
+        want = p.detach().numpy()
+        # the oracle rounds m and v to fp32 before it forms the update, torch
+        # does not: half an ulp of theta plus 2^-22 of the update's size
+        r = (np.abs(m.astype(np.float64)) / (1 - HP.beta1 ** t)
+             / (np.sqrt(v.astype(np.float64) / (1 - HP.beta2 ** t)) + HP.eps))
+        bound = 0.5 * np.spacing(np.abs(theta)).astype(np.float64) + 2.0 ** -22 * HP.lr * r
+        assert np.all(np.abs(theta.astype(np.float64) - want) <= bound)
+        # moments: one rounding of the same fp64 value up to the order of its two
+        # terms (torch forms m + (1 - beta1)(g - m)); bf16-short gradients put
+        # some of them on an exact fp32 tie, which that order may decide
+        for mine, key in ((m, "exp_avg"), (v, "exp_avg_sq")):
+            ref = opt.state[p][key].numpy()
+            tie = (0.5 + 2.0 ** -20) * np.spacing(np.abs(mine)).astype(np.float64)
+            assert np.all(np.abs(mine.astype(np.float64) - ref) <= tie)
+        want_b = torch.from_numpy(theta).to(torch.bfloat16).view(torch.int16).numpy().astype(np.uint16)
+        assert np.array_equal(out, want_b)
+
+
 def test_error_scales_bound_a_perturbed_update():
     # an fp32 re-evaluation of the same formula (a different rounding sequence)
     # stays well inside 1e-6 of the scales -- the tolerance is not vacuous and

@@ -7,6 +7,7 @@ import itertools
 
 import numpy as np
 import pytest
+import torch
 
 from oracle import layout
 from synth import shapes
@@ -118,6 +119,37 @@ def test_pack_bf16_source_is_exact_upcast():
     bits = np.array([0x3F80, 0xBF80, 0x0001, 0x7F7F, 0x8000], dtype=np.uint16)
     master, _, _ = layout.pack_shard([bits], 1, 0)
     assert master.view(np.uint32).tolist() == [int(b) << 16 for b in bits]
+
+
+def test_multidim_params_flatten_row_major():
+    # A tensor of shape (a, b, c) enters the flat buffer with its last index
+    # varying fastest: element [i, j, k] sits at off + (i*b + j)*c + k. Written
+    # with explicit index arithmetic, and checked against torch's flatten of a
+    # contiguous tensor.
+    rng = np.random.default_rng(11)
+    shp = [(2, 3), (4,), (1, 2, 5), (3, 1), ()]
+    params = [rng.standard_normal(s).astype(np.float32) for s in shp]
+    world = 4
+    flat = layout.flatten(params, world, dtype=np.float32)
+    lay = layout.flat_layout([p.size for p in params], world)
+    p0, p2, p3 = params[0], params[2], params[3]
+    for i in range(2):
+        for j in range(3):
+            assert flat[lay.offsets[0] + i * 3 + j] == p0[i, j]
+    for j in range(2):
+        for k in range(5):
+            assert flat[lay.offsets[2] + j * 5 + k] == p2[0, j, k]
+    for i in range(3):
+        assert flat[lay.offsets[3] + i] == p3[i, 0]
+    assert flat[lay.offsets[4]] == params[4]
+    want = torch.cat([torch.from_numpy(p).reshape(-1) for p in params]).numpy()
+    assert np.array_equal(flat[:lay.total], want)
+    assert not flat[lay.total:].any()
+    outs = layout.copy_out(flat, shp)
+    for o, p in zip(outs, params):
+        assert o.shape == p.shape and np.array_equal(o, p)
+    master, _, _ = layout.pack_shard(params, world, 1)
+    assert np.array_equal(master, want[lay.shard:2 * lay.shard])
 
 
 def test_copy_out_shapes_and_pad_dropped():
