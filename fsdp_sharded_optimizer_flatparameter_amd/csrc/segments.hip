@@ -73,7 +73,10 @@ __device__ void seg_to_f32(const Src* __restrict__ src, float* __restrict__ dst,
   for (int64_t i = head + 4 * nv + threadIdx.x; i < len; i += kThreads) dst[i] = widen(src[i]);
 }
 
-// Workgroup-cooperative copy of len bf16 elements.
+// Workgroup-cooperative copy of len bf16 elements. Each lane issues two
+// 16-byte loads before their stores (32 bytes in flight per lane instead of
+// 16: measured 2.5% faster for both copy-outs; four or more were no better,
+// and the fp32-widening copy above is fastest one vector at a time).
 __device__ void seg_bf16(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst,
                          int64_t len) {
   const uintptr_t da = reinterpret_cast<uintptr_t>(dst);
@@ -88,7 +91,13 @@ __device__ void seg_bf16(const uint16_t* __restrict__ src, uint16_t* __restrict_
   const int64_t nv = (len - head) / 8;
   const u32x4* s = reinterpret_cast<const u32x4*>(src + head);
   u32x4* d = reinterpret_cast<u32x4*>(dst + head);
-  for (int64_t i = threadIdx.x; i < nv; i += kThreads) st_nt(ld_nt(s + i), d + i);
+  int64_t i = threadIdx.x;
+  for (; i + kThreads < nv; i += 2 * kThreads) {
+    const u32x4 a = ld_nt(s + i), b = ld_nt(s + i + kThreads);
+    st_nt(a, d + i);
+    st_nt(b, d + i + kThreads);
+  }
+  if (i < nv) st_nt(ld_nt(s + i), d + i);
   for (int64_t i = head + 8 * nv + threadIdx.x; i < len; i += kThreads) dst[i] = src[i];
 }
 
