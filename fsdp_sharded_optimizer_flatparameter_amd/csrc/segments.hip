@@ -27,6 +27,10 @@ namespace {
 
 constexpr int64_t kChunk = 8192;   // elements per workgroup iteration
 constexpr int kLdsParams = 1024;   // offsets cached in LDS up to this many parameters
+// LDS reserved (beyond the offset table) by each pack workgroup: it holds the
+// write-heavy pack to 4 workgroups per CU, measured 3-11% faster than the 8
+// that fit otherwise. The copy-outs keep full residency (capping them was slower).
+constexpr unsigned kPackLds = 32768;
 
 // Largest p with off[p] <= f (off ascending, off[0] == 0 <= f).
 __device__ __forceinline__ int find_param(const int64_t* off_lds, const zs_param_desc* desc,
@@ -289,11 +293,11 @@ hipError_t launch_pack(const zs_param_desc* d_desc, int nparams, int64_t total, 
   if (shard == 0) return hipSuccess;
   const dim3 gd((unsigned)chunk_grid(shard)), bd(kThreads);
   if (src_dtype == ZS_BF16)
-    hipLaunchKernelGGL((k_pack<uint16_t>), gd, bd, 0, s, d_desc, nparams, total, flat_begin, shard,
-                       master, m, v);
+    hipLaunchKernelGGL((k_pack<uint16_t>), gd, bd, kPackLds, s, d_desc, nparams, total, flat_begin,
+                       shard, master, m, v);
   else
-    hipLaunchKernelGGL((k_pack<float>), gd, bd, 0, s, d_desc, nparams, total, flat_begin, shard,
-                       master, m, v);
+    hipLaunchKernelGGL((k_pack<float>), gd, bd, kPackLds, s, d_desc, nparams, total, flat_begin,
+                       shard, master, m, v);
   return hipGetLastError();
 }
 
