@@ -45,8 +45,10 @@ def _adamw_variant(mistake):
             gg = gg + hp.weight_decay * th
         m1 = (b1 * m0 + (1.0 - b1) * gg).astype(state_dtype)
         v1 = (b2 * v0 + (1.0 - b2) * gg * gg).astype(state_dtype)
-        bc1 = 1.0 if mistake == "no_bias_correction" else 1.0 - b1 ** t
-        bc2 = 1.0 if mistake == "no_bias_correction" else 1.0 - b2 ** t
+        bc1 = 1.0 if mistake in ("no_bias_correction", "bias_correction_v_only") else 1.0 - b1 ** t
+        bc2 = 1.0 if mistake in ("no_bias_correction", "bias_correction_m_only") else 1.0 - b2 ** t
+        if mistake == "step_off_by_one":
+            bc1, bc2 = 1.0 - b1 ** (t + 1), 1.0 - b2 ** (t + 1)
         m_hat = m1.astype(np.float64) / bc1
         v_hat = v1.astype(np.float64) / bc2
         if mistake == "eps_inside_root":
@@ -59,12 +61,16 @@ def _adamw_variant(mistake):
             decay = 1.0 + hp.lr * hp.weight_decay
         else:
             decay = 1.0 - hp.lr * hp.weight_decay
+        if mistake == "decay_after_update":
+            return ((th - upd) * decay).astype(state_dtype), m1, v1
         return (th * decay - upd).astype(state_dtype), m1, v1
     return step
 
 
-@pytest.mark.parametrize("mistake", ["no_bias_correction", "l2_decay", "eps_inside_root",
-                                     "decay_sign", "swapped_betas"])
+@pytest.mark.parametrize("mistake", ["no_bias_correction", "bias_correction_m_only",
+                                     "bias_correction_v_only", "step_off_by_one", "l2_decay",
+                                     "eps_inside_root", "decay_sign", "decay_after_update",
+                                     "swapped_betas"])
 def test_adamw_pins_catch(monkeypatch, mistake):
     monkeypatch.setattr(adamw, "adamw_step", _adamw_variant(mistake))
     assert _fails([pins_adamw.test_matches_torch_adamw_fp64_over_ten_steps,
@@ -98,6 +104,23 @@ def _seq32_descending(rows):  # the fp32 running sum in the other order
     return (s / np.float32(c.shape[0])).astype(np.float32)
 
 
+def _seq32_divide_first(rows):  # each contribution divided by N before the fp32 sum
+    c = reduce.decode_rows(rows)
+    n = np.float32(c.shape[0])
+    s = (c[0] / n).astype(np.float32)
+    for r in range(1, c.shape[0]):
+        s = (s + (c[r] / n).astype(np.float32)).astype(np.float32)
+    return s
+
+
+def _seq32_sum_in_fp64(rows):  # the running sum kept in fp64, rounded once
+    c = reduce.decode_rows(rows).astype(np.float64)
+    s = c[0].copy()
+    for r in range(1, c.shape[0]):
+        s = s + c[r]
+    return (s / c.shape[0]).astype(np.float32)
+
+
 REDUCE_PINS = [lambda: pins_reduce.test_mean_exact_is_rounded_once("bf16"),
                lambda: pins_reduce.test_mean_exact_is_rounded_once("f32"),
                pins_reduce.test_mean_seq32_order_is_ascending_from_rank0,
@@ -108,7 +131,9 @@ REDUCE_PINS = [lambda: pins_reduce.test_mean_exact_is_rounded_once("bf16"),
 
 
 @pytest.mark.parametrize("name,fn", [("mean_exact", _mean_exact_sum), ("mean_exact", _mean_exact_drops_last),
-                                     ("mean_seq32", _seq32_descending)])
+                                     ("mean_seq32", _seq32_descending),
+                                     ("mean_seq32", _seq32_divide_first),
+                                     ("mean_seq32", _seq32_sum_in_fp64)])
 def test_reduce_pins_catch(monkeypatch, name, fn):
     monkeypatch.setattr(reduce, name, fn)
     assert _fails(REDUCE_PINS), fn.__name__
@@ -191,11 +216,28 @@ def _bf16_ties_away(x):
     return np.where(nan, (u >> np.uint64(16)) | np.uint64(0x40), r).astype(np.uint16)
 
 
+def _bf16_ties_down(x):  # ties always round down (toward zero in magnitude)
+    u = bf16.f32_bits(x).astype(np.uint64)
+    hi, lo = u >> np.uint64(16), u & np.uint64(0xFFFF)
+    r = hi + (lo > np.uint64(0x8000)).astype(np.uint64)
+    nan = ((u & np.uint64(0x7F800000)) == np.uint64(0x7F800000)) & ((u & np.uint64(0x7FFFFF)) != 0)
+    return np.where(nan, hi | np.uint64(0x40), r).astype(np.uint16)
+
+
+def _bf16_nan_unquieted(x):  # NaN payload truncated without forcing the quiet bit
+    u = bf16.f32_bits(x).astype(np.uint64)
+    hi, lo = u >> np.uint64(16), u & np.uint64(0xFFFF)
+    up = (lo > np.uint64(0x8000)) | ((lo == np.uint64(0x8000)) & ((hi & np.uint64(1)) == np.uint64(1)))
+    r = hi + up.astype(np.uint64)
+    nan = ((u & np.uint64(0x7F800000)) == np.uint64(0x7F800000)) & ((u & np.uint64(0x7FFFFF)) != 0)
+    return np.where(nan, hi, r).astype(np.uint16)
+
+
 BF16_PINS = [pins_bf16.test_hand_worked_patterns, pins_bf16.test_against_torch_on_many_patterns,
              pins_bf16.test_nan_stays_quiet_nan]
 
 
-@pytest.mark.parametrize("fn", [_bf16_truncate, _bf16_ties_away])
+@pytest.mark.parametrize("fn", [_bf16_truncate, _bf16_ties_away, _bf16_ties_down, _bf16_nan_unquieted])
 def test_bf16_pins_catch(monkeypatch, fn):
     monkeypatch.setattr(bf16, "to_bf16_bits", fn)
     assert _fails(BF16_PINS), fn.__name__

@@ -69,9 +69,11 @@ def test_single_rank_and_identical_contributions():
     rows = gen.host_grad_rows(3, 1, 1000, "bf16")
     assert np.array_equal(reduce.mean_exact(rows).view(np.uint32), rows[0].astype(np.uint32) << 16)
     assert np.array_equal(reduce.mean_seq32(rows).view(np.uint32), rows[0].astype(np.uint32) << 16)
-    for world in (2, 3, 8, 64):
+    for world in (2, 3, 5, 7, 8, 13, 63, 64):
         same = np.repeat(rows, world, axis=0)
-        # k*c is exact in fp32 for k <= 64 and bf16 c, so the mean returns c
+        # k*c is exact in fp32 for k <= 64 and bf16 c, and the one correctly
+        # rounded division of k*c by k returns c (dividing each term by k first
+        # would not, for k other than a power of two)
         assert np.array_equal(reduce.mean_seq32(same), bf16.from_bf16_bits(rows[0]))
         assert np.array_equal(reduce.mean_exact(same), bf16.from_bf16_bits(rows[0]))
 
