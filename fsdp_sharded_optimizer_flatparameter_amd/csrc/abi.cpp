@@ -311,7 +311,7 @@ zs_status zs_copy_out_dim0(const uint16_t* gathered, int64_t gathered_numel,
   if (!gathered || !d_desc) return ZS_ERR_NULL;
   if (!aligned(gathered, 2) || !aligned(d_desc, 8)) return ZS_ERR_ALIGN;
   return hip_status(
-      zs::launch_copy_out_dim0(gathered, d_desc, nparams, total, local_total, stream));
+      zs::launch_copy_out_dim0(gathered, d_desc, nparams, world, total, local_total, stream));
 }
 
 zs_status zs_sharded_step(const void* const* rows, int32_t world, int32_t dtype, int64_t n,

@@ -77,18 +77,76 @@ __device__ void seg_to_f32(const Src* __restrict__ src, float* __restrict__ dst,
   for (int64_t i = head + 4 * nv + threadIdx.x; i < len; i += kThreads) dst[i] = widen(src[i]);
 }
 
-// Workgroup-cooperative copy of len bf16 elements. Each lane issues two
-// 16-byte loads before their stores (32 bytes in flight per lane instead of
-// 16: measured 2.5% faster for both copy-outs; four or more were no better,
-// and the fp32-widening copy above is fastest one vector at a time).
+// Destination vectors [k_begin, k_end) of a bf16 copy whose source runs SH
+// elements (1..7) past a 16-byte boundary when the destination sits on one:
+// destination vector k takes elements SH + 8k .. SH + 8k + 7 of the aligned
+// source vectors sa[k] and sa[k + 1]. Each lane loads its own sa[k] and gets
+// sa[k + 1] from the next lane by a wave shuffle (the last active lane of a
+// wave loads it itself), then funnel-shifts the pair into one aligned store.
+// The caller keeps every loaded vector inside the copied range: k_begin >= 1
+// and k_end <= nv - 1 for nv destination vectors, so sa[k_begin] starts after
+// the range's first element and sa[k_end] ends before its last.
+template <int SH>
+__device__ void realign_bf16(const u32x4* __restrict__ sa, u32x4* __restrict__ da, int64_t k_begin,
+                             int64_t k_end) {
+  constexpr int q = SH / 2;          // whole 32-bit words to skip
+  constexpr bool half = (SH & 1) != 0;  // plus one bf16
+  const int lane = threadIdx.x & 63;
+  for (int64_t kb = k_begin; kb < k_end; kb += kThreads) {  // uniform across the workgroup
+    const int64_t k = kb + threadIdx.x;
+    const bool act = k < k_end;
+    const u32x4 lo = act ? ld_nt(sa + k) : u32x4{0u, 0u, 0u, 0u};
+    u32x4 hi;
+    hi.x = __shfl_down(lo.x, 1, 64);
+    hi.y = __shfl_down(lo.y, 1, 64);
+    hi.z = __shfl_down(lo.z, 1, 64);
+    hi.w = __shfl_down(lo.w, 1, 64);
+    if (!act) continue;
+    if (lane == 63 || k + 1 >= k_end) hi = ld_nt(sa + k + 1);
+    const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    u32x4 o;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      o[t] = half ? (w[q + t] >> 16) | (w[q + t + 1] << 16) : w[q + t];
+    st_nt(o, da + k);
+  }
+}
+
+// Workgroup-cooperative copy of len bf16 elements. When source and destination
+// reach the 16-byte grid at the same element, each lane issues two 16-byte
+// loads before their stores (32 bytes in flight per lane instead of 16:
+// measured 2.5% faster for both copy-outs; four or more were no better, and
+// the fp32-widening copy above is fastest one vector at a time). Otherwise the
+// middle of the range goes through realign_bf16 and only the ends are copied
+// element by element.
 __device__ void seg_bf16(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst,
                          int64_t len) {
   const uintptr_t da = reinterpret_cast<uintptr_t>(dst);
   int64_t head = (int64_t)(((16u - (da & 15u)) & 15u) / 2u);
   if (head > len) head = len;
-  const bool vec = (reinterpret_cast<uintptr_t>(src + head) & 15u) == 0;
-  if (!vec) {
-    for (int64_t i = threadIdx.x; i < len; i += kThreads) dst[i] = src[i];
+  const int sh = (int)((reinterpret_cast<uintptr_t>(src + head) & 15u) / 2u);
+  if (sh != 0) {
+    const int64_t nv = (len - head) / 8;  // destination vectors
+    if (nv < 3) {
+      for (int64_t i = threadIdx.x; i < len; i += kThreads) dst[i] = src[i];
+      return;
+    }
+    // element by element: the head and destination vector 0, then the last
+    // destination vector and the tail
+    const int64_t e0 = head + 8, e1 = head + 8 * (nv - 1);
+    for (int64_t i = threadIdx.x; i < e0; i += kThreads) dst[i] = src[i];
+    for (int64_t i = e1 + threadIdx.x; i < len; i += kThreads) dst[i] = src[i];
+    const u32x4* sa = reinterpret_cast<const u32x4*>(src + head - sh);
+    u32x4* dv = reinterpret_cast<u32x4*>(dst + head);
+    switch (sh) {
+      case 1: realign_bf16<1>(sa, dv, 1, nv - 1); break;
+      case 2: realign_bf16<2>(sa, dv, 1, nv - 1); break;
+      case 3: realign_bf16<3>(sa, dv, 1, nv - 1); break;
+      case 4: realign_bf16<4>(sa, dv, 1, nv - 1); break;
+      case 5: realign_bf16<5>(sa, dv, 1, nv - 1); break;
+      case 6: realign_bf16<6>(sa, dv, 1, nv - 1); break;
+      default: realign_bf16<7>(sa, dv, 1, nv - 1); break;
+    }
     return;
   }
   for (int64_t i = threadIdx.x; i < head; i += kThreads) dst[i] = src[i];
@@ -246,39 +304,48 @@ __global__ __launch_bounds__(kThreads) void k_pack_dim0(const zs_dim0_desc* __re
   }
 }
 
-// Full parameters from the rank-major gathered buffer [N * L].
+// Full parameters from the rank-major gathered buffer [N * L]. The workgroups
+// walk the gathered buffer in order (one compact read window; walking the
+// parameters in order instead reads N windows at once and measured 2-9%
+// slower) and scatter each piece -- rank r's part of one parameter's chunk --
+// to that parameter's rows [r*c, r*c + valid). Padding rows are not copied.
 __global__ __launch_bounds__(kThreads) void k_copy_out_dim0(const uint16_t* __restrict__ gathered,
                                                             const zs_dim0_desc* __restrict__ desc,
-                                                            int nparams, int64_t total,
+                                                            int nparams, int world,
                                                             int64_t local_total) {
   __shared__ int64_t key[kLdsParams];
   __shared__ int s_lo, s_hi;
   const bool use_lds = nparams <= kLdsParams;
   if (use_lds)
-    for (int i = threadIdx.x; i < nparams; i += kThreads) key[i] = desc[i].flat_offset;
+    for (int i = threadIdx.x; i < nparams; i += kThreads) key[i] = desc[i].local_offset;
   __syncthreads();
-  auto fkey = [&](int i) { return desc[i].flat_offset; };
-  for (int64_t f0 = (int64_t)blockIdx.x * kChunk; f0 < total; f0 += (int64_t)gridDim.x * kChunk) {
-    const int64_t fe = f0 + kChunk < total ? f0 + kChunk : total;
-    if (threadIdx.x == 0) s_lo = find_by(key, use_lds, nparams, f0, fkey);
-    if (threadIdx.x == 64) s_hi = find_by(key, use_lds, nparams, fe - 1, fkey);
-    __syncthreads();
-    const int lo = __builtin_amdgcn_readfirstlane(s_lo), hi = __builtin_amdgcn_readfirstlane(s_hi);
-    __syncthreads();
-    for (int p = lo; p <= hi; ++p) {
-      const zs_dim0_desc d = desc[p];
-      const int64_t a = f0 > d.flat_offset ? f0 : d.flat_offset;
-      const int64_t b = fe < d.flat_offset + d.numel ? fe : d.flat_offset + d.numel;
-      if (a >= b) continue;
-      int64_t e = a - d.flat_offset;
-      const int64_t e1 = b - d.flat_offset;
-      while (e < e1) {  // split at rank boundaries: each piece is contiguous on both sides
-        const int64_t r = e / d.chunk;
-        const int64_t end = (r + 1) * d.chunk < e1 ? (r + 1) * d.chunk : e1;
-        seg_bf16(gathered + r * local_total + d.local_offset + (e - r * d.chunk),
-                 static_cast<uint16_t*>(d.ptr) + e, end - e);
-        e = end;
+  auto lkey = [&](int i) { return desc[i].local_offset; };
+  const int64_t src_total = (int64_t)world * local_total;
+  for (int64_t g0 = (int64_t)blockIdx.x * kChunk; g0 < src_total; g0 += (int64_t)gridDim.x * kChunk) {
+    const int64_t ge = g0 + kChunk < src_total ? g0 + kChunk : src_total;
+    int64_t gp = g0;
+    while (gp < ge) {  // the chunk's pieces inside one rank's shard (uniform loop)
+      const int64_t r = gp / local_total;
+      const int64_t rend = (r + 1) * local_total < ge ? (r + 1) * local_total : ge;
+      const int64_t j0 = gp - r * local_total, j1 = rend - r * local_total;
+      if (threadIdx.x == 0) s_lo = find_by(key, use_lds, nparams, j0, lkey);
+      if (threadIdx.x == 64) s_hi = find_by(key, use_lds, nparams, j1 - 1, lkey);
+      __syncthreads();
+      const int lo = __builtin_amdgcn_readfirstlane(s_lo), hi = __builtin_amdgcn_readfirstlane(s_hi);
+      __syncthreads();
+      for (int p = lo; p <= hi; ++p) {
+        const zs_dim0_desc d = desc[p];
+        const int64_t a = j0 > d.local_offset ? j0 : d.local_offset;
+        const int64_t b = j1 < d.local_offset + d.chunk ? j1 : d.local_offset + d.chunk;
+        if (a >= b) continue;
+        const int64_t ja = a - d.local_offset, jb = b - d.local_offset;  // within the chunk
+        const int64_t val = valid_part(d, (int)r);
+        const int64_t je = jb < val ? jb : val;  // real rows end
+        if (ja < je)
+          seg_bf16(gathered + r * local_total + a, static_cast<uint16_t*>(d.ptr) + r * d.chunk + ja,
+                   je - ja);
       }
+      gp = rend;
     }
   }
 }
@@ -313,10 +380,10 @@ hipError_t launch_pack_dim0(const zs_dim0_desc* d_desc, int nparams, int src_dty
 }
 
 hipError_t launch_copy_out_dim0(const uint16_t* gathered, const zs_dim0_desc* d_desc, int nparams,
-                                int64_t total, int64_t local_total, hipStream_t s) {
+                                int world, int64_t total, int64_t local_total, hipStream_t s) {
   if (total == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_copy_out_dim0, dim3((unsigned)chunk_grid(total)), dim3(kThreads), 0, s, gathered,
-                     d_desc, nparams, total, local_total);
+  hipLaunchKernelGGL(k_copy_out_dim0, dim3((unsigned)chunk_grid((int64_t)world * local_total)),
+                     dim3(kThreads), 0, s, gathered, d_desc, nparams, world, local_total);
   return hipGetLastError();
 }
 

@@ -89,7 +89,7 @@ hipError_t launch_pack_dim0(const zs_dim0_desc* d_desc, int nparams, int src_dty
                             int64_t local_total, float* master, float* m, float* v, hipStream_t s);
 
 hipError_t launch_copy_out_dim0(const uint16_t* gathered, const zs_dim0_desc* d_desc, int nparams,
-                                int64_t total, int64_t local_total, hipStream_t s);
+                                int world, int64_t total, int64_t local_total, hipStream_t s);
 
 hipError_t launch_copy_out(const uint16_t* gathered, const zs_param_desc* d_desc, int nparams,
                            int64_t total, hipStream_t s);
