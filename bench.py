@@ -17,7 +17,8 @@ Also measured (in "parts"): the same update as two launches (reduce, then AdamW
 with the fused cast), each kernel alone, the clipped update (reduce with its sum
 of squares, clip coefficient, AdamW with the gradient scale), fp32 gradient
 accumulation in the ZeRO-2 and ZeRO-1 orders, the unshard copy-out of one
-decoder block (flat and dim-0 sharded), the dim-0 pack of that block, the
+decoder block (flat and dim-0 sharded), GPT-2's dim-0 copy-out at N=5 (most
+pieces off the 16-byte grid), the dim-0 pack of that block, the
 pack of the shard, the step replayed from a captured HIP graph, and the same
 update composed from PyTorch's own ops (rank adds, fused AdamW, copy-cast) as a
 library reference. The JSON line carries the roofline of
@@ -405,6 +406,19 @@ def main() -> int:
             ms=round(t_cd, 5), elems=sum(bn), bytes_per_elem=4, gb_s=round(gbs, 1),
             frac_of_peak=round(gbs / PEAK_HBM_GBS, 4))
         del gathered_blk, gathered_d0, dst, table, dtable
+        # GPT-2's list under dim-0 sharding at N=5: odd-sized bias and norm chunks
+        # put most pieces off the 16-byte grid (the realigning copy path)
+        g2 = shapes.gpt2_small()
+        g2n = shapes.numels(g2)
+        dst2 = [torch.empty(s, device=dev, dtype=torch.bfloat16) for _, s in g2]
+        dtab2 = zs.Dim0Table(dst2, 5)
+        gathered_g2 = gen.device_normal(g0, 5 * dtab2.local_total, 1.0, torch.bfloat16, dev)
+        t_g2 = event_time_ms(lambda i: zs.zs_copy_out_dim0(gathered_g2, dtab2), 10, stream)
+        gbs = 4 * sum(g2n) / (t_g2 * 1e-3) / 1e9
+        parts["copy_out_dim0_gpt2_n5_misaligned"] = dict(
+            ms=round(t_g2, 5), elems=sum(g2n), bytes_per_elem=4, gb_s=round(gbs, 1),
+            frac_of_peak=round(gbs / PEAK_HBM_GBS, 4))
+        del dst2, dtab2, gathered_g2
         # dim-0 pack of the last rank's shard of the same block from fp32 parameters
         src32 = [gen.device_normal(g0, shapes.numel(s), gen.THETA_SIGMA, None, dev).reshape(s) for _, s in blk]
         ptab = zs.Dim0Table(src32, blk_world)
