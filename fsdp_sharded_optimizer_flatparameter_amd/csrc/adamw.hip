@@ -43,7 +43,7 @@ __global__ __launch_bounds__(BS) void k_adamw(float* __restrict__ th, float* __r
                                                     const float* __restrict__ g, int64_t ngroups,
                                                     int64_t n, AdamConsts c,
                                                     const float* __restrict__ scale,
-                                                    uint16_t* __restrict__ out) {
+                                                    uint16_t* __restrict__ out, int om) {
   const float sc = SCALE ? *scale : 1.0f;
   const int64_t tile = (int64_t)BS * V;
   for (int64_t base = (int64_t)blockIdx.x * tile; base < ngroups;
@@ -74,10 +74,7 @@ __global__ __launch_bounds__(BS) void k_adamw(float* __restrict__ th, float* __r
       st_nt(T[j], reinterpret_cast<f32x4*>(th) + q[j]);
       st_nt(M[j], reinterpret_cast<f32x4*>(m) + q[j]);
       st_nt(W[j], reinterpret_cast<f32x4*>(v) + q[j]);
-      if (CAST) {
-        const u32x2 b{pack_bf16x2(T[j][0], T[j][1]), pack_bf16x2(T[j][2], T[j][3])};
-        st_nt(b, reinterpret_cast<u32x2*>(out) + q[j]);
-      }
+      if (CAST) store_bf16x4(out, q[j], T[j], om);
     }
   }
   if (blockIdx.x == 0) {  // ragged tail
@@ -117,7 +114,7 @@ __global__ __launch_bounds__(kThreads) void k_adamw_scalar(float* __restrict__ t
 
 template <int V, int BS>
 __global__ __launch_bounds__(BS) void k_cast(const float* __restrict__ src, int64_t ngroups,
-                                                   int64_t n, uint16_t* __restrict__ out) {
+                                                   int64_t n, uint16_t* __restrict__ out, int om) {
   const int64_t tile = (int64_t)BS * V;
   for (int64_t base = (int64_t)blockIdx.x * tile; base < ngroups;
        base += (int64_t)gridDim.x * tile) {
@@ -132,8 +129,7 @@ __global__ __launch_bounds__(BS) void k_cast(const float* __restrict__ src, int6
 #pragma unroll
     for (int j = 0; j < V; ++j) {
       if (base + threadIdx.x + (int64_t)j * BS >= ngroups) continue;
-      const u32x2 b{pack_bf16x2(x[j][0], x[j][1]), pack_bf16x2(x[j][2], x[j][3])};
-      st_nt(b, reinterpret_cast<u32x2*>(out) + q[j]);
+      store_bf16x4(out, q[j], x[j], om);
     }
   }
   if (blockIdx.x == 0)
@@ -157,8 +153,9 @@ void run_adamw(float* th, float* m, float* v, const float* g, int64_t n, const A
                const float* scale, uint16_t* out, hipStream_t s) {
   const int64_t ngroups = n / 4;
   const int64_t grid = grid_for(ngroups, (int64_t)kAdamBS * V, kAdamBS);
+  const int om = out ? bf16_out_mode(out) : 0;
   hipLaunchKernelGGL((k_adamw<V, kAdamBS, CAST, SCALE>), dim3((unsigned)grid), dim3(kAdamBS),
-                     (size_t)tuning().adamw_lds, s, th, m, v, g, ngroups, n, c, scale, out);
+                     (size_t)tuning().adamw_lds, s, th, m, v, g, ngroups, n, c, scale, out, om);
 }
 
 template <bool CAST, bool SCALE>
@@ -178,7 +175,7 @@ hipError_t launch_adamw(float* th, float* m, float* v, const float* g, int64_t n
                         hipStream_t s) {
   if (n == 0) return hipSuccess;
   const AdamConsts c = adam_consts(hp);
-  const bool vec = aligned_to(th, 16) && aligned_to(m, 16) && aligned_to(v, 16) && aligned_to(g, 16) && (!out || aligned_to(out, 8));
+  const bool vec = aligned_to(th, 16) && aligned_to(m, 16) && aligned_to(v, 16) && aligned_to(g, 16) && (!out || aligned_to(out, 2));
   if (vec) {
     if (out && scale) pick_v<true, true>(th, m, v, g, n, c, scale, out, s);
     else if (out) pick_v<true, false>(th, m, v, g, n, c, scale, out, s);
@@ -196,10 +193,11 @@ hipError_t launch_adamw(float* th, float* m, float* v, const float* g, int64_t n
 
 hipError_t launch_cast(const float* src, int64_t n, uint16_t* out, hipStream_t s) {
   if (n == 0) return hipSuccess;
-  if (aligned_to(src, 16) && aligned_to(out, 8)) {
+  if (aligned_to(src, 16) && aligned_to(out, 2)) {
     const int64_t ngroups = n / 4;
     const dim3 gd((unsigned)grid_for(ngroups, 2 * kAdamBS, kAdamBS));
-    hipLaunchKernelGGL((k_cast<2, kAdamBS>), gd, dim3(kAdamBS), 0, s, src, ngroups, n, out);
+    hipLaunchKernelGGL((k_cast<2, kAdamBS>), gd, dim3(kAdamBS), 0, s, src, ngroups, n, out,
+                       bf16_out_mode(out));
   } else {
     const dim3 gd((unsigned)grid_for(n, 4 * kThreads));
     hipLaunchKernelGGL(k_cast_scalar, gd, dim3(kThreads), 0, s, src, n, out);

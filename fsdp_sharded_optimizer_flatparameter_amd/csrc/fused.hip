@@ -30,7 +30,7 @@ __global__ __launch_bounds__(BS) void k_fused(RowTable<CAP> rows, int world, Mea
                                                     float* __restrict__ th, float* __restrict__ m,
                                                     float* __restrict__ v, AdamConsts c,
                                                     const float* __restrict__ scale,
-                                                    uint16_t* __restrict__ out) {
+                                                    uint16_t* __restrict__ out, int om) {
   extern __shared__ f32x4 gl[];  // G * BS mean-gradient groups (plus any occupancy pad)
   using L = Lanes<In>;
   const int nw = NW > 0 ? NW : world;
@@ -68,8 +68,7 @@ __global__ __launch_bounds__(BS) void k_fused(RowTable<CAP> rows, int world, Mea
       st_nt(T, reinterpret_cast<f32x4*>(th) + qq);
       st_nt(M, reinterpret_cast<f32x4*>(m) + qq);
       st_nt(W, reinterpret_cast<f32x4*>(v) + qq);
-      if (CAST)
-        st_nt(u32x2{pack_bf16x2(T[0], T[1]), pack_bf16x2(T[2], T[3])}, reinterpret_cast<u32x2*>(out) + qq);
+      if (CAST) store_bf16x4(out, qq, T, om);
     };
     if constexpr (sizeof(In) == 4) {
       // fp32 contributions: all G groups' state loads are issued before the
@@ -168,14 +167,15 @@ void run_fused(const void* const* rows, int world, int64_t n, float* th, float* 
   const int64_t ngroups = n / 4;
   const dim3 gd((unsigned)grid_for(ngroups, (int64_t)BS * G, BS)), bd(BS);
   const MeanDiv d = mean_div(world);
+  const int om = out ? bf16_out_mode(out) : 0;
   if (out && scale)
-    hipLaunchKernelGGL((k_fused<NW, CAP, G, C, BS, In, true, true>), gd, bd, lds, s, t, world, d, ngroups, n, th, m, v, c, scale, out);
+    hipLaunchKernelGGL((k_fused<NW, CAP, G, C, BS, In, true, true>), gd, bd, lds, s, t, world, d, ngroups, n, th, m, v, c, scale, out, om);
   else if (out)
-    hipLaunchKernelGGL((k_fused<NW, CAP, G, C, BS, In, true, false>), gd, bd, lds, s, t, world, d, ngroups, n, th, m, v, c, scale, out);
+    hipLaunchKernelGGL((k_fused<NW, CAP, G, C, BS, In, true, false>), gd, bd, lds, s, t, world, d, ngroups, n, th, m, v, c, scale, out, om);
   else if (scale)
-    hipLaunchKernelGGL((k_fused<NW, CAP, G, C, BS, In, false, true>), gd, bd, lds, s, t, world, d, ngroups, n, th, m, v, c, scale, out);
+    hipLaunchKernelGGL((k_fused<NW, CAP, G, C, BS, In, false, true>), gd, bd, lds, s, t, world, d, ngroups, n, th, m, v, c, scale, out, om);
   else
-    hipLaunchKernelGGL((k_fused<NW, CAP, G, C, BS, In, false, false>), gd, bd, lds, s, t, world, d, ngroups, n, th, m, v, c, scale, out);
+    hipLaunchKernelGGL((k_fused<NW, CAP, G, C, BS, In, false, false>), gd, bd, lds, s, t, world, d, ngroups, n, th, m, v, c, scale, out, om);
 }
 
 template <typename In, int G, int C, int BS>
@@ -230,7 +230,7 @@ hipError_t launch_fused(const void* const* rows, int world, int dtype, int64_t n
                         uint16_t* out, hipStream_t s) {
   if (n == 0) return hipSuccess;
   const AdamConsts c = adam_consts(hp);
-  bool vec = aligned_to(th, 16) && aligned_to(m, 16) && aligned_to(v, 16) && (!out || aligned_to(out, 8));
+  bool vec = aligned_to(th, 16) && aligned_to(m, 16) && aligned_to(v, 16) && (!out || aligned_to(out, 2));
   for (int i = 0; i < world; ++i) vec = vec && aligned_to(rows[i], dtype == ZS_BF16 ? 8 : 16);
   if (vec) {
     if (dtype == ZS_BF16) dispatch<uint16_t>(rows, world, n, th, m, v, c, scale, out, s);

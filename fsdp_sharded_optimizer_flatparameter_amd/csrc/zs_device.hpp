@@ -66,6 +66,33 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
 }
 
+// bf16 store of one 4-element group into out[4q .. 4q + 3]. The group's 8
+// bytes go out as one 8-byte store when out is 8-byte aligned, as two 4-byte
+// stores when it is 4-byte aligned and as four 2-byte stores otherwise (a
+// rank's slot of the all-gather buffer starts at element r*S, so its alignment
+// follows S). `om` is uniform across the launch: 0, 1 or 2 for those cases.
+__device__ __forceinline__ void store_bf16x4(uint16_t* out, int64_t q, const f32x4& x, int om) {
+  const uint32_t lo = pack_bf16x2(x[0], x[1]), hi = pack_bf16x2(x[2], x[3]);
+  uint16_t* p = out + 4 * q;
+  if (om == 0) {
+    st_nt(u32x2{lo, hi}, reinterpret_cast<u32x2*>(p));
+  } else if (om == 1) {
+    st_nt(lo, reinterpret_cast<uint32_t*>(p));
+    st_nt(hi, reinterpret_cast<uint32_t*>(p) + 1);
+  } else {
+    st_nt((uint16_t)lo, p);
+    st_nt((uint16_t)(lo >> 16), p + 1);
+    st_nt((uint16_t)hi, p + 2);
+    st_nt((uint16_t)(hi >> 16), p + 3);
+  }
+}
+
+// Host: the store mode of store_bf16x4 for an output pointer.
+inline int bf16_out_mode(const void* out) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(out);
+  return (a & 7u) == 0 ? 0 : ((a & 3u) == 0 ? 1 : 2);
+}
+
 // ---- gradient contributions ----------------------------------------------------
 
 // Row pointers travel in the kernel-argument segment: uniform across the grid,

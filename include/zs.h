@@ -43,8 +43,10 @@
  *   - bf16 values are passed as uint16_t bit patterns (the top half of an
  *     IEEE fp32). fp32 -> bf16 is round-to-nearest-even; NaN stays a quiet
  *     NaN with its sign; overflow goes to infinity.
- *   - Alignment: any element-aligned pointer is accepted. Pointers on
- *     16-byte boundaries (8-byte for bf16 outputs) take the vector path;
+ *   - Alignment: any element-aligned pointer is accepted. Inputs and fp32
+ *     state on 16-byte boundaries (8-byte for bf16 contributions) take the
+ *     vector path, whatever the alignment of a bf16 output (its 4-element
+ *     groups are stored as one 8-byte, two 4-byte or four 2-byte writes);
  *     others take an element-wise path with the same results.
  */
 #ifndef ZS_H_

@@ -145,6 +145,44 @@ def test_adamw_misaligned_and_8byte_slot():
     _adamw(50001, 2, hparams(), seed=320, offset=1)          # element-wise path
     _adamw(50001, 2, hparams(), seed=321, out_offset=4)      # bf16 slot on an 8-byte boundary
     _adamw(50001, 2, hparams(), seed=322, out_offset=1)      # bf16 slot on a 2-byte boundary
+    _adamw(50001, 2, hparams(), seed=323, out_offset=2)      # bf16 slot on a 4-byte boundary
+
+
+@pytest.mark.parametrize("world", [4, 64])
+def test_bf16_slot_at_every_alignment_is_bitwise_the_aligned_one(world):
+    # a rank's slot of the all-gather buffer starts at element r*S, so it can sit
+    # on an 8-, 4- or 2-byte boundary; the vector kernels split their bf16 stores
+    # to match, and every result must equal the 16-byte-aligned slot's bit for
+    # bit, with the elements around the slot left untouched
+    n = 262144 * 3 + 5
+    rows = device_rows(600 + world, world, n, "bf16")
+    base_state = device_state(610 + world, n)
+    results = {}
+    for off in (8, 1, 2, 3, 4):  # 8 elements = a 16-byte boundary, the reference
+        buf = torch.full((n + 16,), float("nan"), device="cuda", dtype=torch.bfloat16)
+        slot = buf[off:off + n]
+        st = [t.clone() for t in base_state]
+        zs.zs_sharded_step(rows, *st, step=3, bf16_out=slot, **hparams())
+        buf2 = torch.full_like(buf, float("nan"))
+        two = [t.clone() for t in base_state]
+        g = torch.empty(n, device="cuda")
+        zs.zs_reduce_grads(rows, g)
+        zs.zs_adamw_step(*two, g, step=3, bf16_out=buf2[off:off + n], **hparams())
+        buf3 = torch.full_like(buf, float("nan"))
+        zs.zs_cast_for_gather(st[0], buf3[off:off + n])
+        torch.cuda.synchronize()
+        nan = host(torch.full((1,), float("nan"), device="cuda", dtype=torch.bfloat16))[0]
+        for b in (buf, buf2, buf3):
+            hb = host(b)
+            assert np.all(hb[:off] == nan) and np.all(hb[off + n:] == nan), off
+        results[off] = (host(slot).copy(), host(buf2)[off:off + n].copy(), host(buf3)[off:off + n].copy(),
+                        *(host(t).copy() for t in st))
+    ref = results[8]
+    assert np.array_equal(ref[0], ref[1]) and np.array_equal(ref[0], ref[2])
+    assert np.array_equal(ref[0], obf16.to_bf16_bits(ref[3]))
+    for off, got in results.items():
+        for a, b in zip(got, ref):
+            assert np.array_equal(a, b), off
 
 
 def test_adamw_lr_zero_keeps_theta_bitwise():
