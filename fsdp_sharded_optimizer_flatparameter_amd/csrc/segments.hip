@@ -11,14 +11,18 @@
 // Atlas) s5.1 (even, contiguous split); "03 - FSDP (ZeRO-3)" s1 and s3 (the
 // all-gather result is copied out per parameter).
 //
-// Both kernels walk a contiguous flat range in chunks of kChunk elements, one
-// chunk per workgroup iteration. The workgroup finds the parameters that
-// overlap its chunk by binary search over the parameter offsets (staged in LDS
-// when the table is small), then copies each overlap with 16-byte vectors when
-// source and destination reach 16-byte alignment at the same element, and
-// with lane-contiguous element accesses otherwise (still coalesced: 64 lanes
-// touch 64 consecutive elements). Every access lies inside the parameter's own
-// [0, numel) range, inside [0, total) of the flat buffer, or inside the shard.
+// Every kernel walks a contiguous range -- the flat buffer, the rank's shard,
+// or the rank-major gather buffer -- in chunks of kChunk elements, one chunk
+// per workgroup iteration. The workgroup finds the parameters that overlap its
+// chunk by binary search over the parameter offsets (staged in LDS when the
+// table is small), then copies each overlap with 16-byte vectors. A bf16 copy
+// whose source and destination sit at different offsets from the 16-byte grid
+// is realigned in registers (each destination vector is funnel-shifted from
+// two source vectors, the second taken from the neighbour lane); the pack's
+// fp32-widening copy falls back to lane-contiguous element accesses there
+// (still coalesced: 64 lanes touch 64 consecutive elements). Every access lies
+// inside the parameter's own [0, numel) range, inside the flat or gather
+// buffer, or inside the shard.
 #include "zs_device.hpp"
 #include "zs_launch.hpp"
 
