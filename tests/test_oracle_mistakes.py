@@ -416,3 +416,70 @@ def test_ledger_pins_catch(monkeypatch, name, fn):
 
 def test_ledger_pins_pass_the_oracle_itself():
     assert not _fails(_ledger_pins())
+
+
+# ---- the remaining helpers: sum of squares, windows, pack, copy-out, dim-0 counts
+
+def _sumsq_abs(g):  # sum of magnitudes instead of squares
+    return float(np.abs(np.asarray(g, dtype=np.float64)).sum())
+
+
+def _sumsq_fp32(g):  # accumulated in fp32
+    s = np.float32(0.0)
+    for x in np.asarray(g, dtype=np.float32):
+        s = np.float32(s + x * x)
+    return float(s)
+
+
+@pytest.mark.parametrize("fn", [_sumsq_abs, _sumsq_fp32])
+def test_sumsq_pins_catch(monkeypatch, fn):
+    monkeypatch.setattr(reduce, "sumsq", fn)
+    assert _fails([pins_reduce.test_sumsq_matches_exact_sum,
+                   pins_accumulate.test_clip_matches_torch_clip_grad_norm]), fn.__name__
+
+
+def _window_shifted(fetch, numels, f0, f1, dtype=np.float32):  # reads one element late
+    lay = layout.flat_layout(numels, 1)
+    out = np.zeros(max(f1 - f0, 0), dtype=dtype)
+    for i, (off, n) in enumerate(zip(lay.offsets, numels)):
+        a, b = max(f0, off), min(f1, off + int(n))
+        if a < b:
+            src = fetch(i, min(a - off + 1, int(n)), min(b - off + 1, int(n)))
+            out[a - f0:a - f0 + src.size] = src
+    return out
+
+
+def _pack_keeps_moments(params, world, rank):  # returns the master slice as m and v too
+    master, _, _ = _orig_pack_shard(params, world, rank)
+    return master, master.copy(), master.copy()
+
+
+def _copy_out_drops_last(gathered, shapes_):
+    sizes = [int(np.prod(s)) if len(s) else 1 for s in shapes_]
+    lay = layout.flat_layout(sizes, 1)
+    outs = []
+    for off, n, shape in zip(lay.offsets, sizes, shapes_):
+        a = gathered[off:off + n].copy()
+        if n:
+            a[-1] = 0
+        outs.append(a.reshape(shape))
+    return outs
+
+
+_orig_pack_shard = layout.pack_shard
+
+
+@pytest.mark.parametrize("name,fn", [("flat_window", _window_shifted), ("pack_shard", _pack_keeps_moments),
+                                     ("copy_out", _copy_out_drops_last)])
+def test_layout_helper_pins_catch(monkeypatch, name, fn):
+    monkeypatch.setattr(layout, name, fn)
+    assert _fails(LAYOUT_PINS), fn.__name__
+
+
+def _valid_off_by_one(numel, chunk, rank):  # counts one padding element as real
+    return max(0, min(chunk, numel - rank * chunk + 1))
+
+
+def test_dim0_valid_pins_catch(monkeypatch):
+    monkeypatch.setattr(dim0, "valid", _valid_off_by_one)
+    assert _fails(DIM0_PINS)
