@@ -104,7 +104,7 @@ def test_copy_out_dim0_every_shift_into_guarded_views():
     from test_gpu_layout import LENGTHS, _check_guards, _guarded_views
     rng = np.random.default_rng(41)
     lengths = [int(x) for x in rng.permutation(LENGTHS * 2)]
-    for world in (3, 5, 8):
+    for world in (1, 3, 5, 8, 64):
         big, dst, starts = _guarded_views(lengths, seed=42 + world)
         table = zs.Dim0Table(dst, world)
         gathered = gen.device_normal(gen.device_generator(43 + world), world * table.local_total, 1.0,
