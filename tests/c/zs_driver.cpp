@@ -13,7 +13,15 @@
 //   zs_sharded_step on a second copy of the state, the bf16 slot copied out
 //   into the nparams parameters by zs_copy_out (n bf16, concatenated), and
 //   the fp32 master that zs_pack_shard (world 1) builds from theta split into
-//   the same parameters (n fp32).
+//   the same parameters (n fp32); then zs_cast_for_gather of the two-call
+//   theta' (n bf16); two zs_accumulate_grads calls (scale 0.5, first then
+//   not, the second with the sum of squares: n fp32 + fp64); two
+//   zs_accumulate_local calls on rows 0 and 1 % world (n fp32);
+//   zs_clip_coefficient of that sum of squares with max_norm 1e-3 (fp32
+//   coefficient + fp64 norm); and the dim-0 path with the parameters taken as
+//   1-D: L (int64), the last rank's zs_pack_shard_dim0 master (L fp32) and the
+//   unshard of all ranks' packed shards -- each rank packed, the whole cast to
+//   bf16, copied out by zs_copy_out_dim0 (n bf16, concatenated).
 // Exit status: 0 on success, 2 on a usage or I/O error, 3 on a HIP error, and
 // 10 + |status| when an entry point returns an error.
 #include <hip/hip_runtime.h>
@@ -131,6 +139,48 @@ int main(int argc, char** argv) {
   float* d_master = dev_copy<float>(nullptr, n);
   ZS_OK_OR_EXIT(zs_pack_shard(d_src_desc, nparams, total, ZS_F32, 1, 0, shard, d_master, nullptr,
                               nullptr, s));
+  // bf16 cast alone of the two-call theta'
+  uint16_t* c_out = dev_copy<uint16_t>(nullptr, n);
+  ZS_OK_OR_EXIT(zs_cast_for_gather(d_th, n, c_out, s));
+
+  // gradient accumulation over two micro-batches (the same rows twice), then
+  // the clipping coefficient from its sum of squares
+  float* acc = dev_copy<float>(nullptr, n);
+  double* acc_ss = dev_copy<double>(nullptr, 1);
+  ZS_OK_OR_EXIT(zs_accumulate_grads(rows.data(), world, dtype, n, acc, 0.5f, 1, nullptr, nullptr, 0, s));
+  ZS_OK_OR_EXIT(zs_accumulate_grads(rows.data(), world, dtype, n, acc, 0.5f, 0, acc_ss, d_ws, ws_bytes, s));
+  float* lacc = dev_copy<float>(nullptr, n);
+  ZS_OK_OR_EXIT(zs_accumulate_local(rows[0], dtype, n, lacc, 1, s));
+  ZS_OK_OR_EXIT(zs_accumulate_local(rows[1 % world], dtype, n, lacc, 0, s));
+  float* coef = dev_copy<float>(nullptr, 1);
+  double* norm = dev_copy<double>(nullptr, 1);
+  ZS_OK_OR_EXIT(zs_clip_coefficient(acc_ss, 1, 1e-3, coef, norm, s));
+
+  // dim-0 sharding of the same parameters taken as 1-D tensors
+  std::vector<int64_t> d0(numel), rs(nparams, 1), chunk(nparams), loff(nparams);
+  int64_t L = 0;
+  ZS_OK_OR_EXIT(zs_dim0_layout(d0.data(), rs.data(), nparams, world, chunk.data(), loff.data(), &L));
+  std::vector<zs_dim0_desc> src0(nparams), dst0(nparams);
+  std::vector<uint16_t*> outs0(nparams);
+  for (int32_t i = 0; i < nparams; ++i) {
+    outs0[i] = dev_copy<uint16_t>(nullptr, numel[i]);
+    src0[i] = zs_dim0_desc{srcs[i], offsets[i], numel[i], chunk[i], loff[i]};
+    dst0[i] = zs_dim0_desc{outs0[i], offsets[i], numel[i], chunk[i], loff[i]};
+  }
+  ZS_OK_OR_EXIT(zs_check_dim0_layout(src0.data(), nparams, world, total, L));
+  ZS_OK_OR_EXIT(zs_check_dim0_layout(dst0.data(), nparams, world, total, L));
+  zs_dim0_desc* d_src0 = dev_copy(src0.data(), nparams);
+  zs_dim0_desc* d_dst0 = dev_copy(dst0.data(), nparams);
+  const int64_t wl = (int64_t)world * L;
+  float* all_shards = dev_copy<float>(nullptr, (size_t)(wl > 0 ? wl : 1));
+  float* zm = dev_copy<float>(nullptr, (size_t)(L > 0 ? L : 1));
+  float* zv = dev_copy<float>(nullptr, (size_t)(L > 0 ? L : 1));
+  for (int32_t r = 0; r < world; ++r)
+    ZS_OK_OR_EXIT(zs_pack_shard_dim0(d_src0, nparams, ZS_F32, world, r, L, all_shards + (size_t)r * L,
+                                     zm, zv, s));
+  uint16_t* gathered0 = dev_copy<uint16_t>(nullptr, (size_t)(wl > 0 ? wl : 1));
+  ZS_OK_OR_EXIT(zs_cast_for_gather(all_shards, wl, gathered0, s));
+  ZS_OK_OR_EXIT(zs_copy_out_dim0(gathered0, wl, d_dst0, nparams, world, total, L, s));
   HIP_OK(hipStreamSynchronize(s));
 
   FILE* out = std::fopen(argv[2], "wb");
@@ -142,17 +192,27 @@ int main(int argc, char** argv) {
   ok = ok && put(out, host_copy(f_out, n).data(), n);
   for (int32_t i = 0; i < nparams; ++i) ok = ok && put(out, host_copy(outs[i], numel[i]).data(), numel[i]);
   ok = ok && put(out, host_copy(d_master, n).data(), n);
+  ok = ok && put(out, host_copy(c_out, n).data(), n);
+  ok = ok && put(out, host_copy(acc, n).data(), n) && put(out, host_copy(acc_ss, 1).data());
+  ok = ok && put(out, host_copy(lacc, n).data(), n);
+  ok = ok && put(out, host_copy(coef, 1).data()) && put(out, host_copy(norm, 1).data());
+  ok = ok && put(out, &L);
+  ok = ok && put(out, host_copy(all_shards + (size_t)(world - 1) * L, (size_t)L).data(), (size_t)L);
+  for (int32_t i = 0; i < nparams; ++i) ok = ok && put(out, host_copy(outs0[i], numel[i]).data(), numel[i]);
   ok = std::fclose(out) == 0 && ok;
   if (!ok) return 2;
 
   for (const void* r : rows) HIP_OK(hipFree(const_cast<void*>(r)));
   for (void* p : {(void*)d_th, (void*)d_m, (void*)d_v, (void*)f_th, (void*)f_m, (void*)f_v,
                   (void*)d_g, (void*)d_out, (void*)f_out, (void*)d_sumsq, d_ws, (void*)d_out_desc,
-                  (void*)d_src_desc, (void*)d_master})
+                  (void*)d_src_desc, (void*)d_master, (void*)c_out, (void*)acc, (void*)acc_ss,
+                  (void*)lacc, (void*)coef, (void*)norm, (void*)d_src0, (void*)d_dst0,
+                  (void*)all_shards, (void*)zm, (void*)zv, (void*)gathered0})
     HIP_OK(hipFree(p));
   for (int32_t i = 0; i < nparams; ++i) {
     HIP_OK(hipFree(outs[i]));
     HIP_OK(hipFree(srcs[i]));
+    HIP_OK(hipFree(outs0[i]));
   }
   HIP_OK(hipStreamDestroy(s));
   std::printf("zs_driver ok: world=%d dtype=%d n=%lld nparams=%d\n", world, dtype, (long long)n, nparams);

@@ -2,8 +2,10 @@
 or PyTorch in the process that calls the library), checked against the oracle.
 
 tests/c/zs_driver reads the inputs this test writes, runs zs_reduce_grads (with
-the sum of squares), zs_adamw_step, zs_sharded_step, zs_copy_out and
-zs_pack_shard on its own device buffers, and writes every output back.
+the sum of squares), zs_adamw_step, zs_sharded_step, zs_copy_out,
+zs_pack_shard, zs_cast_for_gather, zs_accumulate_grads, zs_accumulate_local,
+zs_clip_coefficient and the dim-0 layout, pack and copy-out on its own device
+buffers, and writes every output back.
 """
 import os
 import subprocess
@@ -11,8 +13,10 @@ import subprocess
 import numpy as np
 import pytest
 
+from oracle import accumulate as oacc
 from oracle import adamw as oadamw
 from oracle import bf16 as obf16
+from oracle import dim0 as odim0
 from oracle import layout as olayout
 from oracle import reduce as oreduce
 from synth import gen
@@ -57,7 +61,11 @@ def _run(tmp_path, world, dtype, numels, step, seed):
     out = dict(g=take(np.float32, n), sumsq=take(np.float64, 1)[0],
                two=tuple(take(np.float32, n) for _ in range(3)), two_bf16=take(np.uint16, n),
                one=tuple(take(np.float32, n) for _ in range(3)), one_bf16=take(np.uint16, n),
-               copied=take(np.uint16, n), packed=take(np.float32, n))
+               copied=take(np.uint16, n), packed=take(np.float32, n), cast=take(np.uint16, n),
+               acc=take(np.float32, n), acc_ss=take(np.float64, 1)[0], local=take(np.float32, n),
+               coef=take(np.float32, 1)[0], norm=take(np.float64, 1)[0])
+    L = int(take(np.int64, 1)[0])
+    out.update(L=L, last_shard=take(np.float32, L), unshard=take(np.uint16, n))
     assert pos == len(raw)
     return rows, (th, m, v), hp, out
 
@@ -95,3 +103,23 @@ def test_c_driver_matches_oracle(tmp_path, world, dtype, numels):
     th1, _, _ = oadamw.adamw_step(*state, g_exact, step, oadamw.HParams(**hp))
     assert np.max(np.abs(out["two"][0].astype(np.float64) - th1)) <= 1e-5 * np.max(np.abs(th1))
     assert np.array_equal(obf16.to_bf16_bits(out["two"][0]), out["two_bf16"])
+    # the standalone cast of the same theta'
+    assert np.array_equal(out["cast"], out["two_bf16"])
+    # ZeRO-2 accumulation of two micro-batches (the same rows twice, scale 1/2)
+    acc_want = oacc.zero2_accumulate([rows, rows], 0.5)
+    assert np.array_equal(bits32(out["acc"]), bits32(acc_want))
+    assert abs(out["acc_ss"] - oreduce.sumsq(out["acc"])) <= 1e-12 * oreduce.sumsq(out["acc"])
+    # ZeRO-1 local accumulation: one rank's fp32 sum of its two micro-batch gradients
+    dec = oreduce.decode_rows(rows)
+    local_want = (dec[0].copy() + dec[1 % world]).astype(np.float32)
+    assert np.array_equal(bits32(out["local"]), bits32(local_want))
+    # clipping coefficient from the accumulated gradient's sum of squares
+    want_coef, want_norm = oacc.clip_coefficient([out["acc_ss"]], 1e-3)
+    assert abs(out["norm"] - want_norm) <= 1e-15 * want_norm
+    assert abs(float(out["coef"]) - float(want_coef)) <= np.spacing(np.float32(want_coef))
+    # dim-0 sharding of the parameters taken as 1-D: the last rank's pack, and the
+    # unshard of every rank's packed shard (cast to bf16) is bf16 of theta
+    pieces = [state[0][o:o + k] for o, k in zip(np.cumsum([0] + numels[:-1]), numels)]
+    assert out["L"] == odim0.dim0_layout([(k,) for k in numels], world).local_total
+    assert np.array_equal(bits32(out["last_shard"]), bits32(odim0.shard_dim0(pieces, world, world - 1)))
+    assert np.array_equal(out["unshard"], obf16.to_bf16_bits(state[0]))
