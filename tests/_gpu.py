@@ -93,3 +93,31 @@ def max_scaled_adamw_error(after, before, g, step, hp):
     th1, m1, v1 = oadamw.adamw_step(before[0], before[1], before[2], g, step, hpo)
     st, _, _ = oadamw.error_scales(before[0], before[1], g, step, hpo, m1, v1)
     return float(np.max(np.abs(after[0].astype(np.float64) - th1) / st))
+
+
+GUARD_LENGTHS = [1, 7, 8, 15, 16, 23, 24, 25, 31, 32, 33, 40, 47, 63, 64, 100, 255, 256, 257, 1000,
+                 2047, 8191, 8192, 8193, 20000, 70001]
+
+
+def guarded_views(lengths, seed):
+    """Destinations as views of one NaN-filled bf16 buffer, each starting at a
+    different offset from the 16-byte grid, with guard gaps between them."""
+    rng = np.random.default_rng(seed)
+    starts, pos = [], 0
+    for n in lengths:
+        pos += 24 + int(rng.integers(0, 8))
+        starts.append(pos)
+        pos += n
+    big = torch.full((pos + 24,), float("nan"), device="cuda", dtype=torch.bfloat16)
+    views = [big[a:a + n] for a, n in zip(starts, lengths)]
+    return big, views, starts
+
+
+def check_guards(big, starts, lengths):
+    """Every element of the buffer outside the views still holds the NaN fill."""
+    mask = np.ones(big.numel(), dtype=bool)
+    for a, n in zip(starts, lengths):
+        mask[a:a + n] = False
+    guard = host(big)[mask]
+    nan_bits = np.uint16(torch.tensor(float("nan"), dtype=torch.bfloat16).view(torch.int16).item() & 0xFFFF)
+    assert np.all(guard == nan_bits)

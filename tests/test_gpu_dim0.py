@@ -8,7 +8,7 @@ import fsdp_sharded_optimizer_flatparameter_amd as zs
 from oracle import bf16 as obf16
 from oracle import dim0 as odim0
 from synth import gen, shapes
-from _gpu import bits32, host
+from _gpu import GUARD_LENGTHS, bits32, check_guards, guarded_views, host
 
 pytestmark = pytest.mark.gpu
 
@@ -101,11 +101,10 @@ def test_copy_out_dim0_every_shift_into_guarded_views():
     # 1-D parameters whose rank chunks are odd-sized, at world sizes that do not
     # divide them, copied into views of one buffer at every offset from the
     # 16-byte grid; the guard gaps between the views must stay untouched
-    from test_gpu_layout import LENGTHS, _check_guards, _guarded_views
     rng = np.random.default_rng(41)
-    lengths = [int(x) for x in rng.permutation(LENGTHS * 2)]
+    lengths = [int(x) for x in rng.permutation(GUARD_LENGTHS * 2)]
     for world in (1, 3, 5, 8, 64):
-        big, dst, starts = _guarded_views(lengths, seed=42 + world)
+        big, dst, starts = guarded_views(lengths, seed=42 + world)
         table = zs.Dim0Table(dst, world)
         gathered = gen.device_normal(gen.device_generator(43 + world), world * table.local_total, 1.0,
                                      torch.bfloat16)
@@ -114,7 +113,7 @@ def test_copy_out_dim0_every_shift_into_guarded_views():
         want = odim0.copy_out_dim0(host(gathered), [(n,) for n in lengths], world)
         for i, (d, w) in enumerate(zip(dst, want)):
             assert np.array_equal(host(d), w), (world, i, lengths[i])
-        _check_guards(big, starts, lengths)
+        check_guards(big, starts, lengths)
 
 
 def test_copy_out_dim0_llama8b_block_full():

@@ -7,7 +7,7 @@ import fsdp_sharded_optimizer_flatparameter_amd as zs
 from oracle import bf16 as obf16
 from oracle import layout as olayout
 from synth import gen, shapes
-from _gpu import bits32, host
+from _gpu import GUARD_LENGTHS, bits32, check_guards, guarded_views, host
 
 pytestmark = pytest.mark.gpu
 
@@ -86,39 +86,12 @@ def test_copy_out_misaligned_offsets_and_tiny_params():
     _copy_out_case(shp, seed=22, world=3)
 
 
-LENGTHS = [1, 7, 8, 15, 16, 23, 24, 25, 31, 32, 33, 40, 47, 63, 64, 100, 255, 256, 257, 1000,
-           2047, 8191, 8192, 8193, 20000, 70001]
-
-
-def _guarded_views(lengths, seed):
-    # destinations as views of one buffer, each starting at a different offset
-    # from the 16-byte grid, with guard gaps between them that must stay untouched
-    rng = np.random.default_rng(seed)
-    starts, pos = [], 0
-    for n in lengths:
-        pos += 24 + int(rng.integers(0, 8))
-        starts.append(pos)
-        pos += n
-    big = torch.full((pos + 24,), float("nan"), device="cuda", dtype=torch.bfloat16)
-    views = [big[a:a + n] for a, n in zip(starts, lengths)]
-    return big, views, starts
-
-
-def _check_guards(big, starts, lengths):
-    mask = np.ones(big.numel(), dtype=bool)
-    for a, n in zip(starts, lengths):
-        mask[a:a + n] = False
-    guard = host(big)[mask]
-    nan_bits = np.uint16(torch.tensor(float("nan"), dtype=torch.bfloat16).view(torch.int16).item() & 0xFFFF)
-    assert np.all(guard == nan_bits)
-
-
 def test_copy_out_every_source_and_destination_shift():
     # every offset of source and destination from the 16-byte grid, with lengths
     # around the vector thresholds and the per-workgroup chunk
     rng = np.random.default_rng(31)
-    lengths = [int(x) for x in rng.permutation(LENGTHS * 3)]
-    big, dst, starts = _guarded_views(lengths, seed=32)
+    lengths = [int(x) for x in rng.permutation(GUARD_LENGTHS * 3)]
+    big, dst, starts = guarded_views(lengths, seed=32)
     numels = lengths
     _, total, padded, _ = zs.zs_flat_layout(numels, 1)
     gathered = gen.device_normal(gen.device_generator(33), padded, 1.0, torch.bfloat16)
@@ -129,7 +102,7 @@ def test_copy_out_every_source_and_destination_shift():
     assert {o % 8 for o in offs} == set(range(8)) and {a % 8 for a in starts} == set(range(8))
     for i, (d, w) in enumerate(zip(dst, want)):
         assert np.array_equal(host(d), w), (i, lengths[i], offs[i] % 8, starts[i] % 8)
-    _check_guards(big, starts, lengths)
+    check_guards(big, starts, lengths)
 
 
 def test_copy_out_llama8b_block_full():
