@@ -361,3 +361,15 @@ def test_c_driver_is_built_and_rejects_bad_usage(tmp_path):
     bad.write_bytes(b"\x01\x00\x00\x00")
     assert subprocess.run([drv, str(bad), str(tmp_path / "o.bin")], capture_output=True,
                           timeout=60).returncode == 2
+
+
+def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
+    # no fallback of any kind: with the shared library absent, the first call
+    # through the binding raises instead of computing anything
+    monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "libzs_absent.so"))
+    monkeypatch.setattr(L, "_lib", None)
+    with pytest.raises(ImportError, match="not built"):
+        L.load()
+    from fsdp_sharded_optimizer_flatparameter_amd import api
+    with pytest.raises(ImportError):
+        api.zs_flat_layout([3, 5], 2)
