@@ -5,7 +5,10 @@ The knobs (ZS_* environment variables, read once per process) pick workgroup
 sizes, staging depths, rank-chunk widths, LDS reservations and grid caps. Each
 case below runs the same seeded update in a child process under one setting
 (a grid cap of a few workgroups forces every kernel through its grid-stride
-loop) and compares all outputs with the default setting's, bitwise.
+loop) and compares all outputs with the default setting's, bitwise: the
+single pass and the two calls, the accumulation, the cast, the flat and dim-0
+copy-outs (the latter with odd-sized chunks, so through the realigning copy),
+the single pass into a bf16 slot on a 2-byte boundary, and the pack.
 """
 import os
 import subprocess
@@ -53,6 +56,13 @@ for world, dt, n in ((8, torch.bfloat16, 300_007), (64, torch.bfloat16, 70_001),
     shapes = [(n // 3,), (n - n // 3 - 5,), (5,)]
     dst = [torch.empty(s, device="cuda", dtype=torch.bfloat16) for s in shapes]
     zs.zs_copy_out(slot, zs.ParamTable(dst))
+    dst0 = [torch.empty(sh, device="cuda", dtype=torch.bfloat16) for sh in shapes]
+    t0 = zs.Dim0Table(dst0, 5)
+    gathered0 = gen.device_normal(g0, 5 * t0.local_total, 1.0, torch.bfloat16)
+    zs.zs_copy_out_dim0(gathered0, t0)
+    odd = torch.empty(n + 1, device="cuda", dtype=torch.bfloat16)[1:]  # a slot on a 2-byte boundary
+    st_odd = [gen.device_normal(g0, n, 0.02), gen.device_normal(g0, n, 1e-4), gen.device_normal(g0, n, 1e-6).abs_()]
+    zs.zs_sharded_step(rows, *st_odd, step=3, bf16_out=odd, **hp)
     master = torch.empty(-(-n // 4), device="cuda")
     srcs = [gen.device_normal(g0, s[0], 0.02) for s in shapes]
     zs.zs_pack_shard(zs.ParamTable(srcs), 4, 3, master)
@@ -65,6 +75,10 @@ for world, dt, n in ((8, torch.bfloat16, 300_007), (64, torch.bfloat16, 70_001),
     out[f"{world}_ss"] = ss.cpu().numpy()
     out[f"{world}_ass"] = ass.cpu().numpy()
     out[f"{world}_copied"] = np.concatenate([h(d) for d in dst])
+    out[f"{world}_copied_dim0"] = np.concatenate([h(d) for d in dst0])
+    out[f"{world}_odd_slot"] = h(odd)
+    for i, x in enumerate(st_odd):
+        out[f"{world}_odd{i}"] = h(x)
 np.savez(sys.argv[1], **out)
 """
 
