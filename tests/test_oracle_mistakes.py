@@ -483,3 +483,23 @@ def _valid_off_by_one(numel, chunk, rank):  # counts one padding element as real
 def test_dim0_valid_pins_catch(monkeypatch):
     monkeypatch.setattr(dim0, "valid", _valid_off_by_one)
     assert _fails(DIM0_PINS)
+
+
+def _exact_mean_divides_by_ranks(rows_per_microbatch):  # forgets the micro-batch count
+    tot, n = None, 0
+    for rows in rows_per_microbatch:
+        c = reduce.decode_rows(rows).astype(np.float64)
+        tot = c.sum(axis=0) if tot is None else tot + c.sum(axis=0)
+        n = c.shape[0]
+    return (tot / n).astype(np.float32)
+
+
+def _global_norm_max(partials):  # the largest shard's norm instead of the global one
+    return float(np.sqrt(max(float(p) for p in partials)))
+
+
+@pytest.mark.parametrize("name,fn", [("exact_mean_over_microbatches", _exact_mean_divides_by_ranks),
+                                     ("global_norm", _global_norm_max)])
+def test_accumulate_helper_pins_catch(monkeypatch, name, fn):
+    monkeypatch.setattr(accumulate, name, fn)
+    assert _fails(ACCUM_PINS + [pins_accumulate.test_exact_mean_over_microbatches_is_rounded_once]), fn.__name__
