@@ -183,6 +183,29 @@ def test_70b_fp32_contributions_bench_chunk():
     torch.cuda.empty_cache()
 
 
+def test_full_size_accumulation_7p5b_n64():
+    # the ZeRO-2 accumulation over two micro-batches on the 7.5B/N=64 shard, in
+    # the launch configuration the bench times: bit-exact on sampled windows
+    # against the oracle's order, and the whole shard's sum of squares
+    from oracle import accumulate as oacc
+    n, world = 117_187_500, 64
+    mb = [device_rows(7300, world, n, "bf16"), device_rows(7301, world, n, "bf16")]
+    acc = torch.empty(n, device="cuda")
+    ss = torch.empty(1, device="cuda", dtype=torch.float64)
+    ws = torch.empty(zs.zs_workspace_bytes(n), device="cuda", dtype=torch.uint8)
+    zs.zs_accumulate_grads(mb[0], acc, scale=0.5, first=True)
+    zs.zs_accumulate_grads(mb[1], acc, scale=0.5, first=False, sumsq_out=ss, workspace=ws)
+    torch.cuda.synchronize()
+    for a, b in _windows(n, 65536, 6, 7302):
+        want = oacc.zero2_accumulate([np.stack([host(r[a:b]) for r in rows]) for rows in mb], 0.5)
+        assert np.array_equal(bits32(host(acc[a:b])), bits32(want)), (a, b)
+    acc_h = host(acc)
+    ref = oreduce.sumsq(acc_h)
+    assert abs(ss.item() - ref) <= 1e-12 * ref
+    del mb
+    torch.cuda.empty_cache()
+
+
 def test_resume_from_saved_state_is_bitwise_the_straight_run():
     # the rank's resumable state is {master, m, v, step}: 5 steps, save to host
     # bytes, reload into fresh device buffers, 5 more steps == 10 straight steps
