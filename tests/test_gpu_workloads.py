@@ -206,6 +206,40 @@ def test_full_size_accumulation_7p5b_n64():
     torch.cuda.empty_cache()
 
 
+def test_full_size_clipped_step_7p5b_n64():
+    # the clipped update at full size, as the bench times it: reduce with the sum
+    # of squares, the clip coefficient, AdamW with it as the gradient scale
+    from oracle import accumulate as oacc
+    n, world, max_norm = 117_187_500, 64, 1e-3
+    rows = device_rows(7400, world, n, "bf16")
+    g0 = gen.device_generator(7401)
+    th = gen.device_normal(g0, n, gen.THETA_SIGMA)
+    m = gen.device_normal(g0, n, 1e-4)
+    v = gen.device_normal(g0, n, 1e-6).abs_()
+    wins = _windows(n, 65536, 4, 7402)
+    before = [tuple(host(t[a:b]).copy() for t in (th, m, v)) for a, b in wins]
+    g = torch.empty(n, device="cuda")
+    ss = torch.empty(1, device="cuda", dtype=torch.float64)
+    ws = torch.empty(zs.zs_workspace_bytes(n), device="cuda", dtype=torch.uint8)
+    coef = torch.empty(1, device="cuda")
+    slot = torch.empty(n, device="cuda", dtype=torch.bfloat16)
+    hp = hparams(weight_decay=0.1)
+    zs.zs_reduce_grads(rows, g, sumsq_out=ss, workspace=ws)
+    zs.zs_clip_coefficient(ss, max_norm, coef)
+    zs.zs_adamw_step(th, m, v, g, step=2, grad_scale=coef, bf16_out=slot, **hp)
+    torch.cuda.synchronize()
+    want_coef, _ = oacc.clip_coefficient(host(ss), max_norm)
+    c = np.float32(coef.item())
+    assert abs(float(c) - float(want_coef)) <= np.spacing(np.float32(want_coef)) and c < 1
+    for (a, b), bef in zip(wins, before):
+        gh = (host(g[a:b]) * c).astype(np.float32)
+        after = tuple(host(t[a:b]) for t in (th, m, v))
+        th_or = check_adamw(after, bef, gh, 2, hp)
+        check_bf16(host(slot[a:b]), after[0], th_or)
+    del rows
+    torch.cuda.empty_cache()
+
+
 def test_resume_from_saved_state_is_bitwise_the_straight_run():
     # the rank's resumable state is {master, m, v, step}: 5 steps, save to host
     # bytes, reload into fresh device buffers, 5 more steps == 10 straight steps
