@@ -240,6 +240,35 @@ def test_full_size_clipped_step_7p5b_n64():
     torch.cuda.empty_cache()
 
 
+def test_full_size_local_accumulation_and_cast():
+    # the ZeRO-1 local accumulation at the Llama-3-8B shard's size (one rank's
+    # fp32 sum of two bf16 micro-batch gradients) and the standalone cast of the
+    # 7.5B shard into rank 63's 8-byte-aligned slot: windows bit-exact
+    n = 1_003_782_656
+    g0 = gen.device_generator(7500)
+    a = gen.device_normal(g0, n, 1e-3, torch.bfloat16)
+    b = gen.device_normal(g0, n, 1e-3, torch.bfloat16)
+    acc = torch.empty(n, device="cuda")
+    zs.zs_accumulate_local(a, acc, first=True)
+    zs.zs_accumulate_local(b, acc, first=False)
+    torch.cuda.synchronize()
+    for lo, hi in _windows(n, 65536, 4, 7501):
+        da = obf16.from_bf16_bits(host(a[lo:hi]))
+        db = obf16.from_bf16_bits(host(b[lo:hi]))
+        assert np.array_equal(bits32(host(acc[lo:hi])), bits32((da + db).astype(np.float32))), (lo, hi)
+    del a, b, acc
+    S = 117_187_500
+    th = gen.device_normal(g0, S, gen.THETA_SIGMA)
+    gather = torch.empty(64 * S, device="cuda", dtype=torch.bfloat16)
+    slot = gather[63 * S:]
+    zs.zs_cast_for_gather(th, slot)
+    torch.cuda.synchronize()
+    for lo, hi in _windows(S, 65536, 4, 7502):
+        assert np.array_equal(host(slot[lo:hi]), obf16.to_bf16_bits(host(th[lo:hi]))), (lo, hi)
+    del gather, th
+    torch.cuda.empty_cache()
+
+
 def test_resume_from_saved_state_is_bitwise_the_straight_run():
     # the rank's resumable state is {master, m, v, step}: 5 steps, save to host
     # bytes, reload into fresh device buffers, 5 more steps == 10 straight steps
