@@ -9,6 +9,11 @@ slot of the all-gather buffer -- one launch of the single-pass kernel
 (zs_sharded_step). Inputs are synthetic and resident in HBM before timing.
 Reported value: shard elements updated per second (Gelem/s).
 
+Before the W counted warm-up steps the device is settled: the step runs for at
+least --settle-ms of wall time (measured on MI355X, the first 20 steps after a
+cold start run 3-6% slower than the steady state, whatever W is). The JSON
+line reports the settle steps; the timed region is exactly K steps.
+
 The 70B shard (fp32 contributions, 64 x 4.4 GB of rows) does not fit in HBM
 whole: it is updated in 8 equal chunks, one launch each, with one chunk's worth
 of rows (35 GB) serving every chunk; a step is the 8 launches.
@@ -21,9 +26,11 @@ decoder block (flat and dim-0 sharded), GPT-2's dim-0 copy-out at N=5 (most
 pieces off the 16-byte grid), the dim-0 pack of that block, the
 pack of the shard, the step replayed from a captured HIP graph, and the same
 update composed from PyTorch's own ops (rank adds, fused AdamW, copy-cast) as a
-library reference. The JSON line carries the roofline of
-the dominant kernel (HIP-event time on the launch stream) and the CPU oracle
-timed on a bounded sample of the same inputs.
+library reference. With the default 7.5B workload, the second target shard --
+Llama-3-8B at N=8 -- is set up after the 7.5B buffers are freed and its single
+pass timed the same way ("llama8b_step", with its own roofline). The JSON line
+carries the roofline of the dominant kernel (HIP-event time on the launch
+stream) and the CPU oracle timed on a bounded sample of the same inputs.
 """
 from __future__ import annotations
 
@@ -31,6 +38,7 @@ import argparse
 import hashlib
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -57,6 +65,13 @@ WORKLOADS = {
     "tiny": dict(shapes="tiny", world=4, rank=3, wd=0.01,
                  desc="4 x 512x512 parameters, N=4 simulated ranks, rank 3's shard"),
 }
+
+# CPU sample: whole shards for the small workloads, a window of this many shard
+# elements for the large ones (elements per second do not depend on the size
+# beyond the last-level cache)
+CPU_WINDOW = 1 << 26
+CPU_CHUNK = 1 << 22      # elements per oracle call (bounds its temporaries)
+CPU_MAX_WORKERS = 16     # the host share of one GPU
 
 
 # Sources that define each timed kernel and its launch shape; counter-derived
@@ -117,17 +132,412 @@ def event_time_ms(fn, iters: int, stream, warmup: int = 2) -> float:
     return start.elapsed_time(end) / iters
 
 
+def settle(step, seconds: float) -> int:
+    """Run `step` until `seconds` of wall time have passed (synchronising every
+    few steps); returns the number of steps run."""
+    import torch
+
+    n, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(4):
+            step(n)
+            n += 1
+        torch.cuda.synchronize()
+    return n
+
+
+def timed_steps(step, stream, warmup: int, steps: int):
+    """W untimed steps, then exactly K steps between synchronisations, with an
+    event between steps for the per-step spread; returns (ms per step, spread)."""
+    import torch
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    marks[0].record(stream)
+    for i in range(steps):
+        step(i)
+        marks[i + 1].record(stream)
+    torch.cuda.synchronize()
+    ms = marks[0].elapsed_time(marks[-1]) / steps
+    per = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(steps))
+    spread = dict(median=round(per[len(per) // 2], 5), min=round(per[0], 5),
+                  max=round(per[-1], 5)) if per else None
+    return ms, spread
+
+
+def gbs_entry(ms: float, bpe: int, elems: int, **extra) -> dict:
+    gbs = bpe * elems / (ms * 1e-3) / 1e9
+    return dict(ms=round(ms, 5), elems=elems, bytes_per_elem=bpe, gb_s=round(gbs, 1),
+                frac_of_peak=round(gbs / PEAK_HBM_GBS, 4), **extra)
+
+
+# ---------------------------------------------------------------- CPU oracle leg
+
+def cpu_model() -> str:
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    try:
+        with open("/proc/cpuinfo") as f:
+            return next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "unknown")
+    except OSError:
+        return "unknown"
+
+
+def cpu_workers() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, CPU_MAX_WORKERS))
+
+
+def _cpu_worker(conn):
+    """Oracle worker process: receives one contiguous chunk of the sample, then
+    times the oracle's fp32-emulation update over it (ascending-rank fp32 sum and
+    one division by N, AdamW in fp64 from the fp32 state, bf16 cast) on request."""
+    data = None
+    while True:
+        msg = conn.recv()
+        if msg[0] == "data":
+            data = msg[1:]
+            conn.send(("ready", data[1].size))
+        elif msg[0] == "run":
+            from oracle import adamw as oadamw
+            from oracle import step as ostep
+
+            rows, th, m, v, hp = data
+            hpo = oadamw.HParams(**hp)
+            t0 = time.perf_counter()
+            for c0 in range(0, th.size, CPU_CHUNK):
+                c1 = min(th.size, c0 + CPU_CHUNK)
+                ostep.sharded_step(rows[:, c0:c1], th[c0:c1], m[c0:c1], v[c0:c1], 1, hpo, exact_mean=False)
+            conn.send(("done", th.size, time.perf_counter() - t0))
+        else:
+            conn.close()
+            return
+
+
+class CpuSample:
+    """Oracle processes (started before the GPU is touched), each holding one
+    contiguous chunk of a bounded, bit-identical host copy of the step's inputs."""
+
+    def __init__(self):
+        import multiprocessing as mp
+
+        ctx = mp.get_context("spawn")
+        self.workers = cpu_workers()
+        self.conns, self.procs = [], []
+        for _ in range(self.workers):
+            parent, child = ctx.Pipe()
+            p = ctx.Process(target=_cpu_worker, args=(child,), daemon=True)
+            p.start()
+            child.close()
+            self.conns.append(parent)
+            self.procs.append(p)
+        self.n = 0
+
+    def load(self, rows, theta, m, v, a: int, n: int, hp: dict):
+        import numpy as np
+        import torch
+
+        self.world, self.n = len(rows), n
+        self.row_code = "bf16" if rows[0].dtype == torch.bfloat16 else "f32"
+        per = -(-n // self.workers)
+        self.chunks = [(c, min(n, c + per)) for c in range(0, n, per)]
+        for conn, (c0, c1) in zip(self.conns, self.chunks):
+            lo, hi = a + c0, a + c1
+            if self.row_code == "bf16":
+                r = np.stack([x[lo:hi].view(torch.int16).cpu().numpy().view(np.uint16) for x in rows])
+            else:
+                r = np.stack([x[lo:hi].cpu().numpy() for x in rows])
+            conn.send(("data", r, theta[lo:hi].cpu().numpy(), m[lo:hi].cpu().numpy(),
+                       v[lo:hi].cpu().numpy(), dict(hp)))
+            del r
+        for conn in self.conns[:len(self.chunks)]:
+            assert conn.recv()[0] == "ready"
+
+    def measure(self) -> dict:
+        live = self.conns[:len(self.chunks)]
+        live[0].send(("run",))  # one process alone
+        _, n1, t1 = live[0].recv()
+        t0 = time.perf_counter()
+        for conn in live:
+            conn.send(("run",))
+        done = sum(conn.recv()[1] for conn in live)
+        tw = time.perf_counter() - t0
+        w = len(live)
+        return {"value": round(done / tw / 1e9, 6), "unit": "Gelem/s", "cores": w, "kind": "oracle",
+                "sample": f"{self.n} consecutive shard elements x {self.world} {self.row_code} rows (the GPU's "
+                          f"own inputs, copied to the host before the first update); the oracle's "
+                          f"fp32-emulation path: ascending-rank fp32 running sum and one division by N, AdamW "
+                          f"in fp64 from the fp32 state, bf16 cast; {w} contiguous chunks, one per process, "
+                          f"{tw:.2f} s wall",
+                "single_process_value": round(n1 / t1 / 1e9, 6),
+                "single_process_sample": f"the first chunk ({n1} elements) in one process, {t1:.2f} s",
+                "cpu_model": cpu_model()}
+
+    def close(self):
+        for conn in self.conns:
+            try:
+                conn.send(("exit",))
+            except (OSError, BrokenPipeError):
+                pass
+        for p in self.procs:
+            p.join(timeout=10)
+            if p.is_alive():
+                p.terminate()
+
+
+# ---------------------------------------------------------------- the step
+
+def make_shard(name: str, dev):
+    """Inputs of one workload's shard update, resident in HBM, and its step."""
+    import torch
+
+    import fsdp_sharded_optimizer_flatparameter_amd as zs
+    from synth import gen, shapes
+
+    wl = WORKLOADS[name]
+    numels = shapes.numels(getattr(shapes, wl["shapes"])())
+    world, rank = wl["world"], wl["rank"]
+    _, total, padded, S = zs.zs_flat_layout(numels, world)
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=wl["wd"])
+    row_dtype = torch.float32 if wl.get("rows") == "f32" else torch.bfloat16
+    csize = -(-S // wl.get("chunks", 1))
+    ranges = [(a, min(S, a + csize)) for a in range(0, S, csize)]
+    g0 = gen.device_generator(1000 + sorted(WORKLOADS).index(name), dev)
+    rows = [gen.device_normal(g0, csize, gen.GRAD_SIGMA, row_dtype, dev) for _ in range(world)]
+    theta = gen.device_normal(g0, S, gen.THETA_SIGMA, None, dev)
+    m = torch.zeros(S, device=dev)
+    v = torch.zeros(S, device=dev)
+    if len(ranges) == 1:
+        gather = torch.empty(padded, device=dev, dtype=torch.bfloat16)
+        slot = gather[rank * S:(rank + 1) * S]
+    else:  # the 70B gather buffer (141 GB) is not needed to time the rank's slot
+        slot = torch.empty(S, device=dev, dtype=torch.bfloat16)
+    sh = dict(name=name, wl=wl, numels=numels, world=world, rank=rank, S=S, padded=padded, hp=hp,
+              row_dtype=row_dtype, row_bytes=4 if row_dtype == torch.float32 else 2, csize=csize,
+              ranges=ranges, g0=g0, rows=rows, theta=theta, m=m, v=v, slot=slot, step_no=[0])
+
+    def rows_for(a, b):
+        return rows if b - a == csize else [r[:b - a] for r in rows]
+
+    sh["rows_for"] = rows_for
+
+    # zs_sharded_step per range, with its arguments marshalled once (on the
+    # stream current when the plans are made)
+    def make_plans():
+        return [zs.ShardedStep(rows_for(a, b), theta[a:b], m[a:b], v[a:b], bf16_out=slot[a:b], **hp)
+                for a, b in ranges]
+
+    sh["make_plans"] = make_plans
+    # A shard whose working set is near the 256 MB Infinity Cache (GPT-2: 0.65 GB)
+    # steps round-robin over independent copies of its inputs, so that no step
+    # finds the previous step's bytes still cached.
+    rotation = [make_plans()]
+    for _ in range(1, wl.get("rotate", 1)):
+        rk = [gen.device_normal(g0, csize, gen.GRAD_SIGMA, row_dtype, dev) for _ in range(world)]
+        tk = gen.device_normal(g0, S, gen.THETA_SIGMA, None, dev)
+        mk, vk = torch.zeros(S, device=dev), torch.zeros(S, device=dev)
+        sk = torch.empty(S, device=dev, dtype=torch.bfloat16)
+        rotation.append([zs.ShardedStep(rk, tk, mk, vk, bf16_out=sk, **hp)])
+    sh["rotation"] = rotation
+
+    def fused_step(_i):
+        sh["step_no"][0] += 1
+        for plan in rotation[sh["step_no"][0] % len(rotation)]:
+            plan(sh["step_no"][0])
+
+    sh["step"] = fused_step
+    sh["fused_bpe"] = sh["row_bytes"] * world + 26  # rows + read theta,m,v + write theta,m,v + bf16
+    torch.cuda.synchronize()
+    return sh
+
+
+def measure_parts(sh, dev, stream, iters: int, parts: dict) -> None:
+    import torch
+
+    import fsdp_sharded_optimizer_flatparameter_amd as zs
+    from synth import gen, shapes
+
+    S, world, hp, ranges, rows = sh["S"], sh["world"], sh["hp"], sh["ranges"], sh["rows"]
+    theta, m, v, slot, step_no, rows_for = sh["theta"], sh["m"], sh["v"], sh["slot"], sh["step_no"], sh["rows_for"]
+    g0, csize = sh["g0"], sh["csize"]
+    n_rows_bytes = sh["row_bytes"] * world
+    reduce_bpe, adamw_bpe, cast_bpe = n_rows_bytes + 4, 30, 6
+    gbuf = torch.empty(S, device=dev)
+
+    def reduce_call(i):
+        for a, b in ranges:
+            zs.zs_reduce_grads(rows_for(a, b), gbuf[a:b])
+
+    t_reduce = event_time_ms(reduce_call, iters, stream)
+
+    def adamw_call(i):
+        step_no[0] += 1
+        for a, b in ranges:
+            zs.zs_adamw_step(theta[a:b], m[a:b], v[a:b], gbuf[a:b], step=step_no[0], bf16_out=slot[a:b], **hp)
+
+    t_adamw = event_time_ms(adamw_call, iters, stream)
+    t_cast = event_time_ms(lambda i: zs.zs_cast_for_gather(theta, slot), iters, stream)
+    parts["two_call_step"] = dict(ms=round(t_reduce + t_adamw, 5),
+                                  gelem_s=round(S / ((t_reduce + t_adamw) * 1e-3) / 1e9, 3),
+                                  bytes_per_elem=reduce_bpe + adamw_bpe)
+    parts["reduce"] = gbs_entry(t_reduce, reduce_bpe, S)
+    parts["adamw_cast"] = gbs_entry(t_adamw, adamw_bpe, S)
+    parts["cast"] = gbs_entry(t_cast, cast_bpe, S)
+
+    # the step captured once in a HIP graph and replayed: no host launch work
+    # per step (what decides the launch-bound Tiny shard)
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        for plan in sh["make_plans"]():
+            plan(1)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for plan in sh["make_plans"]():  # bound to the capture stream
+            plan(1)
+    t_graph = event_time_ms(lambda i: graph.replay(), iters, stream)
+    parts["graph_replayed_step"] = dict(ms=round(t_graph, 5), gelem_s=round(S / (t_graph * 1e-3) / 1e9, 3))
+    del graph
+
+    # the same update composed from PyTorch's own ops, as a library reference:
+    # in-place fp32 adds of the N contributions in rank order, one division,
+    # PyTorch's fused AdamW, and a copy-cast into the slot
+    if len(ranges) == 1:
+        p = torch.nn.Parameter(theta.clone())
+        p.grad = torch.empty_like(p)
+        opt = torch.optim.AdamW([p], lr=hp["lr"], betas=(hp["beta1"], hp["beta2"]), eps=hp["eps"],
+                                weight_decay=hp["weight_decay"], fused=True)
+
+        def torch_step(i):
+            gg = p.grad
+            gg.copy_(rows[0])
+            for r in rows[1:]:
+                gg.add_(r)
+            gg.div_(world)
+            opt.step()
+            slot.copy_(p.detach())
+
+        t_torch = event_time_ms(torch_step, max(5, iters // 4), stream)
+        parts["torch_composed_step"] = dict(ms=round(t_torch, 5), gelem_s=round(S / (t_torch * 1e-3) / 1e9, 3))
+        del p, opt
+
+    # global-norm clipping: the reduce also returns the fp64 sum of squares of its
+    # output, the clip coefficient combines the shards' partials (here the N
+    # simulated ranks' copies of this one), and AdamW takes it as a gradient scale
+    ws = torch.empty(zs.zs_workspace_bytes(csize), device=dev, dtype=torch.uint8)
+    partials = torch.zeros(world, device=dev, dtype=torch.float64)
+    coef = torch.empty(1, device=dev)
+
+    def reduce_sumsq_call(i):
+        for j, (a, b) in enumerate(ranges):
+            zs.zs_reduce_grads(rows_for(a, b), gbuf[a:b], sumsq_out=partials[j:j + 1], workspace=ws)
+
+    parts["reduce_sumsq"] = gbs_entry(event_time_ms(reduce_sumsq_call, iters, stream), reduce_bpe, S)
+
+    def clipped_call(i):
+        step_no[0] += 1
+        reduce_sumsq_call(i)
+        zs.zs_clip_coefficient(partials, 1.0, coef)
+        for a, b in ranges:
+            zs.zs_adamw_step(theta[a:b], m[a:b], v[a:b], gbuf[a:b], step=step_no[0],
+                             grad_scale=coef, bf16_out=slot[a:b], **hp)
+
+    parts["clipped_step"] = gbs_entry(event_time_ms(clipped_call, iters, stream), reduce_bpe + adamw_bpe, S)
+
+    # fp32 gradient accumulation over micro-batches. ZeRO-2 order: every
+    # micro-batch's N contributions are reduced and added into the fp32 shard
+    # (gbuf serves as the accumulator). ZeRO-1 order: each rank adds its whole
+    # local bf16 gradient into a full-size fp32 buffer; timed on S elements of it.
+    def accum_call(i):
+        for a, b in ranges:
+            zs.zs_accumulate_grads(rows_for(a, b), gbuf[a:b], scale=0.25)
+
+    parts["accumulate_zero2"] = gbs_entry(event_time_ms(accum_call, iters, stream), n_rows_bytes + 8, S)
+    local = rows[0][:min(csize, S)]
+    lacc = gbuf[:local.numel()]
+    parts["accumulate_zero1_local"] = gbs_entry(
+        event_time_ms(lambda i: zs.zs_accumulate_local(local, lacc), iters, stream),
+        sh["row_bytes"] + 8, local.numel())
+    del gbuf, ws, partials, coef, lacc
+
+    # unshard copy-out of one decoder block: Llama-3-8B's (218,112,000 elements), or
+    # the 70B model's (855,654,400) for that workload
+    big = sh["name"] == "70b"
+    blk = shapes.llama_70b_block() if big else shapes.llama3_8b_block()
+    blk_name, blk_world = ("70b_block", 64) if big else ("llama8b_block", 8)
+    bn = shapes.numels(blk)
+    gathered_blk = gen.device_normal(g0, sum(bn), 1.0, torch.bfloat16, dev)
+    dst = [torch.empty(s, device=dev, dtype=torch.bfloat16) for _, s in blk]
+    table = zs.ParamTable(dst)
+    t_co = event_time_ms(lambda i: zs.zs_copy_out(gathered_blk, table), 10, stream)
+    parts[f"copy_out_{blk_name}"] = gbs_entry(t_co, 4, sum(bn))
+    if big:
+        # with reshard_after_forward every one of the 80 blocks is unsharded
+        # twice per step (forward and backward): the step's copy-out time
+        parts["copy_out_70b_per_step_ms"] = round(t_co * 160, 3)
+    # the same block under per-parameter dim-0 sharding (a scatter from the N rank
+    # regions of the gather buffer)
+    dtable = zs.Dim0Table(dst, blk_world)
+    gathered_d0 = gen.device_normal(g0, blk_world * dtable.local_total, 1.0, torch.bfloat16, dev)
+    t_cd = event_time_ms(lambda i: zs.zs_copy_out_dim0(gathered_d0, dtable), 10, stream)
+    parts[f"copy_out_dim0_{blk_name}_n{blk_world}"] = gbs_entry(t_cd, 4, sum(bn))
+    del gathered_blk, gathered_d0, dst, table, dtable
+    # GPT-2's list under dim-0 sharding at N=5: odd-sized bias and norm chunks
+    # put most pieces off the 16-byte grid (the realigning copy path)
+    g2 = shapes.gpt2_small()
+    g2n = shapes.numels(g2)
+    dst2 = [torch.empty(s, device=dev, dtype=torch.bfloat16) for _, s in g2]
+    dtab2 = zs.Dim0Table(dst2, 5)
+    gathered_g2 = gen.device_normal(g0, 5 * dtab2.local_total, 1.0, torch.bfloat16, dev)
+    t_g2 = event_time_ms(lambda i: zs.zs_copy_out_dim0(gathered_g2, dtab2), 10, stream)
+    parts["copy_out_dim0_gpt2_n5_misaligned"] = gbs_entry(t_g2, 4, sum(g2n))
+    del dst2, dtab2, gathered_g2
+    # dim-0 pack of the last rank's shard of the same block from fp32 parameters
+    src32 = [gen.device_normal(g0, shapes.numel(s), gen.THETA_SIGMA, None, dev).reshape(s) for _, s in blk]
+    ptab = zs.Dim0Table(src32, blk_world)
+    L = ptab.local_total
+    pm, pmm, pvv = (torch.empty(L, device=dev) for _ in range(3))
+    t_pd = event_time_ms(lambda i: zs.zs_pack_shard_dim0(ptab, blk_world - 1, pm, pmm, pvv), 10, stream)
+    parts[f"pack_dim0_{blk_name}_n{blk_world}"] = gbs_entry(t_pd, 16, L)
+    del src32, ptab, pm, pmm, pvv
+
+    # pack of this shard from per-parameter fp32 tensors (one-time setup work);
+    # a single 7.5e9-element parameter, or the 70B list (282 GB of fp32
+    # parameters), is represented by the rank's slice of it
+    if sh["name"] in ("7p5b", "70b"):
+        src = [gen.device_normal(g0, S, gen.THETA_SIGMA, None, dev)]
+        ptable, pworld, prank = zs.ParamTable(src), 1, 0
+    else:
+        src = [gen.device_normal(g0, n, gen.THETA_SIGMA, None, dev) for n in sh["numels"]]
+        ptable, pworld, prank = zs.ParamTable(src), world, sh["rank"]
+    t_pack = event_time_ms(lambda i: zs.zs_pack_shard(ptable, pworld, prank, theta, m, v), 5, stream)
+    parts["pack_shard"] = gbs_entry(t_pack, 16, S)
+    del src, ptable
+    torch.cuda.synchronize()
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="7p5b", choices=sorted(WORKLOADS))
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="wall time the step runs before the W warm-up steps (device settle)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parts", action="store_true", help="time only the step")
-    ap.add_argument("--cpu-windows", type=int, default=24, help="2^20-element windows for the oracle timing")
-    ap.add_argument("--cpu-threads", type=int, default=16, help="threads for the pooled oracle timing")
-    ap.add_argument("--cpu-seconds", type=float, default=3.0, help="wall time of the pooled oracle timing")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="before timing, run one plain 1 GiB device copy (torch copy_) as the known-size "
                          "reference for HBM byte counters")
@@ -141,11 +551,19 @@ def main() -> int:
         print("bench.py runs on one GPU only (WORLD_SIZE > 1 given)", file=sys.stderr)
         return 2
 
-    import numpy as np
+    # the oracle's process pool starts before anything touches the GPU
+    cpu = CpuSample() if not args.no_cpu_baseline else None
+    try:
+        return run(args, cpu)
+    finally:
+        if cpu is not None:
+            cpu.close()
+
+
+def run(args, cpu) -> int:
     import torch
 
     import fsdp_sharded_optimizer_flatparameter_amd as zs
-    from synth import gen, shapes
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -155,71 +573,14 @@ def main() -> int:
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
 
-    wl = WORKLOADS[args.workload]
-    numels = shapes.numels(getattr(shapes, wl["shapes"])())
-    world, rank = wl["world"], wl["rank"]
-    _, total, padded, S = zs.zs_flat_layout(numels, world)
-    hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=wl["wd"])
+    sh = make_shard(args.workload, dev)
+    S, world, hp = sh["S"], sh["world"], sh["hp"]
 
-    # ---- inputs, resident in HBM before any timing
-    row_dtype = torch.float32 if wl.get("rows") == "f32" else torch.bfloat16
-    row_bytes = 4 if row_dtype == torch.float32 else 2
-    csize = -(-S // wl.get("chunks", 1))
-    ranges = [(a, min(S, a + csize)) for a in range(0, S, csize)]
-    g0 = gen.device_generator(1000 + sorted(WORKLOADS).index(args.workload), dev)
-    rows = [gen.device_normal(g0, csize, gen.GRAD_SIGMA, row_dtype, dev) for _ in range(world)]
-    theta = gen.device_normal(g0, S, gen.THETA_SIGMA, None, dev)
-    m = torch.zeros(S, device=dev)
-    v = torch.zeros(S, device=dev)
-    if len(ranges) == 1:
-        gather = torch.empty(padded, device=dev, dtype=torch.bfloat16)
-        slot = gather[rank * S:(rank + 1) * S]
-    else:  # the 70B gather buffer (141 GB) is not needed to time the rank's slot
-        slot = torch.empty(S, device=dev, dtype=torch.bfloat16)
-    gbuf = torch.empty(S, device=dev)
-    torch.cuda.synchronize()
-
-    def rows_for(a, b):
-        return rows if b - a == csize else [r[:b - a] for r in rows]
-
-    # bit-identical host copies of the oracle's sample (taken before any update)
-    win = 1 << 20
-    nwin = max(1, min(args.cpu_windows, csize // win)) if not args.no_cpu_baseline else 0
-    rng = np.random.default_rng(0)
-    starts = sorted(int(x) for x in rng.choice(max(1, csize // win), size=nwin, replace=False)) if nwin else []
-    cpu_inputs = []
-    for s0 in starts:
-        a, b = s0 * win, min(csize, s0 * win + win)
-        if row_dtype == torch.bfloat16:
-            r_h = np.stack([r[a:b].view(torch.int16).cpu().numpy().view(np.uint16) for r in rows])
-        else:
-            r_h = np.stack([r[a:b].cpu().numpy() for r in rows])
-        cpu_inputs.append((r_h, theta[a:b].cpu().numpy(), m[a:b].cpu().numpy(), v[a:b].cpu().numpy()))
-
-    step_no = [0]
-
-    # zs_sharded_step per range, with its arguments marshalled once (on the
-    # stream current when the plans are made)
-    def make_plans():
-        return [zs.ShardedStep(rows_for(a, b), theta[a:b], m[a:b], v[a:b], bf16_out=slot[a:b], **hp)
-                for a, b in ranges]
-
-    plans = make_plans()
-    # A shard whose working set is near the 256 MB Infinity Cache (GPT-2: 0.65 GB)
-    # steps round-robin over independent copies of its inputs, so that no step
-    # finds the previous step's bytes still cached.
-    rotation = [plans]
-    for k in range(1, wl.get("rotate", 1)):
-        rk = [gen.device_normal(g0, csize, gen.GRAD_SIGMA, row_dtype, dev) for _ in range(world)]
-        tk = gen.device_normal(g0, S, gen.THETA_SIGMA, None, dev)
-        mk, vk = torch.zeros(S, device=dev), torch.zeros(S, device=dev)
-        sk = torch.empty(S, device=dev, dtype=torch.bfloat16)
-        rotation.append([zs.ShardedStep(rk, tk, mk, vk, bf16_out=sk, **hp)])
-
-    def fused_step(_i):
-        step_no[0] += 1
-        for plan in rotation[step_no[0] % len(rotation)]:
-            plan(step_no[0])
+    # bit-identical host copy of the oracle's sample, taken before any update
+    if cpu is not None:
+        n_cpu = min(sh["csize"], CPU_WINDOW)
+        a_cpu = 0 if n_cpu == sh["csize"] else (sh["csize"] - n_cpu) // 2
+        cpu.load(sh["rows"], sh["theta"], sh["m"], sh["v"], a_cpu, n_cpu, hp)
 
     if args.calibrate_copy:
         src = torch.ones(1 << 28, device=dev)
@@ -228,266 +589,62 @@ def main() -> int:
         torch.cuda.synchronize()
         del src, dst
 
-    # ---- the step: warmup, then exactly K timed steps between synchronisations;
-    # an event between steps gives the per-step spread
-    for i in range(args.warmup):
-        fused_step(i)
-    torch.cuda.synchronize()
-    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    marks[0].record(stream)
-    for i in range(args.steps):
-        fused_step(i)
-        marks[i + 1].record(stream)
-    torch.cuda.synchronize()
-    ms_step = marks[0].elapsed_time(marks[-1]) / args.steps
-    per_step = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
-    spread = dict(median=round(per_step[len(per_step) // 2], 5), min=round(per_step[0], 5),
-                  max=round(per_step[-1], 5)) if per_step else None
+    # ---- the step: settle, W warm-up steps, then exactly K timed steps
+    settle_steps = settle(sh["step"], args.settle_ms * 1e-3)
+    ms_step, spread = timed_steps(sh["step"], stream, args.warmup, args.steps)
     gelem = S / (ms_step * 1e-3) / 1e9
-
-    n_rows_bytes = row_bytes * world
-    fused_bpe = n_rows_bytes + 26          # rows + read theta,m,v + write theta,m,v + bf16
-    reduce_bpe = n_rows_bytes + 4          # rows + write g
-    adamw_bpe = 30                         # read g,theta,m,v + write theta,m,v + bf16
-    cast_bpe = 6
+    fused_bpe = sh["fused_bpe"]
     achieved = fused_bpe * S / (ms_step * 1e-3) / 1e9
     kernel_name = "k_fused"
     src_hash = source_hash(kernel_name)
     traffic = read_traffic(args.workload, kernel_name, src_hash)
 
     parts = {}
-    copy_gbs = None
-    runtime_copy_gbs = None
+    library_copy_gbs = runtime_copy_gbs = None
     if not args.no_parts and not args.calibrate_copy:
-        # practical copy ceilings, 2 GiB each way: the library's own streaming copy
-        # (zs_copy_out of a one-parameter unit) and the HIP runtime's copy kernel
+        # streaming copies of 2 GiB each way: the library's own (zs_copy_out of a
+        # one-parameter unit) and the HIP runtime's copy kernel
         src = torch.ones(1 << 30, device=dev, dtype=torch.bfloat16)
         dst = torch.empty_like(src)
         one = zs.ParamTable([dst])
         t_copy = event_time_ms(lambda i: zs.zs_copy_out(src, one), 10, stream)
-        copy_gbs = 2 * src.numel() * 2 / (t_copy * 1e-3) / 1e9
+        library_copy_gbs = 2 * src.numel() * 2 / (t_copy * 1e-3) / 1e9
         t_copy = event_time_ms(lambda i: dst.copy_(src), 10, stream)
         runtime_copy_gbs = 2 * src.numel() * 2 / (t_copy * 1e-3) / 1e9
         del src, dst, one
-    if not args.no_parts:
-        iters = max(10, args.steps)
+        parts["fused_step"] = gbs_entry(ms_step, fused_bpe, S)
+        measure_parts(sh, dev, stream, max(10, args.steps), parts)
+        if "torch_composed_step" in parts:
+            parts["torch_composed_step"]["fused_step_speedup"] = round(parts["torch_composed_step"]["ms"] / ms_step, 3)
+        parts["two_call_step"]["fused_step_speedup"] = round(parts["two_call_step"]["ms"] / ms_step, 4)
 
-        def reduce_call(i):
-            for a, b in ranges:
-                zs.zs_reduce_grads(rows_for(a, b), gbuf[a:b])
+    config = {
+        "workload": sh["wl"]["desc"],
+        "shard_elems": S,
+        "world": world,
+        "rank": sh["rank"],
+        "contributions": "fp32" if sh["row_bytes"] == 4 else "bf16",
+        "launches_per_step": len(sh["ranges"]),
+        "step": "mean of N contributions + AdamW (fp32 master/m/v) + bf16 cast, one pass",
+        "adamw": hp,
+    }
+    del sh  # free the shard before the second target shard is set up
 
-        t_reduce = event_time_ms(reduce_call, iters, stream)
+    # ---- the second target shard: Llama-3-8B at N=8, its single pass timed the
+    # same way (settle, W warm-up steps, K steps)
+    if args.workload == "7p5b" and not args.no_parts and not args.calibrate_copy:
+        torch.cuda.empty_cache()
+        ll = make_shard("llama8b", dev)
+        settle(ll["step"], args.settle_ms * 1e-3)
+        ms_ll, spread_ll = timed_steps(ll["step"], stream, args.warmup, args.steps)
+        parts["llama8b_step"] = gbs_entry(ms_ll, ll["fused_bpe"], ll["S"], kernel=kernel_name,
+                                          workload=ll["wl"]["desc"],
+                                          gelem_s=round(ll["S"] / (ms_ll * 1e-3) / 1e9, 3),
+                                          step_ms=spread_ll)
+        del ll
+        torch.cuda.empty_cache()
 
-        def adamw_call(i):
-            step_no[0] += 1
-            for a, b in ranges:
-                zs.zs_adamw_step(theta[a:b], m[a:b], v[a:b], gbuf[a:b], step=step_no[0],
-                                 bf16_out=slot[a:b], **hp)
-
-        t_adamw = event_time_ms(adamw_call, iters, stream)
-        t_cast = event_time_ms(lambda i: zs.zs_cast_for_gather(theta, slot), iters, stream)
-        parts["two_call_step"] = dict(ms=t_reduce + t_adamw, gelem_s=S / ((t_reduce + t_adamw) * 1e-3) / 1e9,
-                                      bytes_per_elem=reduce_bpe + adamw_bpe)
-        for name, t, bpe in (("reduce", t_reduce, reduce_bpe), ("adamw_cast", t_adamw, adamw_bpe),
-                             ("cast", t_cast, cast_bpe), ("fused_step", ms_step, fused_bpe)):
-            gbs = bpe * S / (t * 1e-3) / 1e9
-            parts[name] = dict(ms=round(t, 5), bytes_per_elem=bpe, gb_s=round(gbs, 1),
-                               frac_of_peak=round(gbs / PEAK_HBM_GBS, 4))
-
-        def put(name, t, bpe, elems=S):
-            gbs = bpe * elems / (t * 1e-3) / 1e9
-            parts[name] = dict(ms=round(t, 5), elems=elems, bytes_per_elem=bpe, gb_s=round(gbs, 1),
-                               frac_of_peak=round(gbs / PEAK_HBM_GBS, 4))
-
-        # the step captured once in a HIP graph and replayed: no host launch work
-        # per step (what decides the launch-bound Tiny shard)
-        side = torch.cuda.Stream()
-        side.wait_stream(stream)
-        with torch.cuda.stream(side):
-            for plan in make_plans():
-                plan(1)
-        stream.wait_stream(side)
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for plan in make_plans():  # bound to the capture stream
-                plan(1)
-        t_graph = event_time_ms(lambda i: graph.replay(), iters, stream)
-        parts["graph_replayed_step"] = dict(ms=round(t_graph, 5), gelem_s=round(S / (t_graph * 1e-3) / 1e9, 3))
-        del graph
-
-        # the same update composed from PyTorch's own ops, as a library reference:
-        # in-place fp32 adds of the N contributions in rank order, one division,
-        # PyTorch's fused AdamW, and a copy-cast into the slot
-        if len(ranges) == 1:
-            p = torch.nn.Parameter(theta.clone())
-            p.grad = torch.empty_like(p)
-            opt = torch.optim.AdamW([p], lr=hp["lr"], betas=(hp["beta1"], hp["beta2"]), eps=hp["eps"],
-                                    weight_decay=hp["weight_decay"], fused=True)
-
-            def torch_step(i):
-                gg = p.grad
-                gg.copy_(rows[0])
-                for r in rows[1:]:
-                    gg.add_(r)
-                gg.div_(world)
-                opt.step()
-                slot.copy_(p.detach())
-
-            t_torch = event_time_ms(torch_step, max(5, iters // 4), stream)
-            parts["torch_composed_step"] = dict(
-                ms=round(t_torch, 5), gelem_s=round(S / (t_torch * 1e-3) / 1e9, 3),
-                fused_step_speedup=round(t_torch / ms_step, 3))
-            del p, opt
-
-        # global-norm clipping: the reduce also returns the fp64 sum of squares of its
-        # output, the clip coefficient combines the shards' partials (here the N
-        # simulated ranks' copies of this one), and AdamW takes it as a gradient scale
-        ws = torch.empty(zs.zs_workspace_bytes(csize), device=dev, dtype=torch.uint8)
-        partials = torch.zeros(world, device=dev, dtype=torch.float64)
-        coef = torch.empty(1, device=dev)
-
-        def reduce_sumsq_call(i):
-            for j, (a, b) in enumerate(ranges):
-                zs.zs_reduce_grads(rows_for(a, b), gbuf[a:b], sumsq_out=partials[j:j + 1], workspace=ws)
-
-        t_rs = event_time_ms(reduce_sumsq_call, iters, stream)
-        put("reduce_sumsq", t_rs, reduce_bpe)
-
-        def clipped_call(i):
-            step_no[0] += 1
-            reduce_sumsq_call(i)
-            zs.zs_clip_coefficient(partials, 1.0, coef)
-            for a, b in ranges:
-                zs.zs_adamw_step(theta[a:b], m[a:b], v[a:b], gbuf[a:b], step=step_no[0],
-                                 grad_scale=coef, bf16_out=slot[a:b], **hp)
-
-        put("clipped_step", event_time_ms(clipped_call, iters, stream), reduce_bpe + adamw_bpe)
-
-        # fp32 gradient accumulation over micro-batches. ZeRO-2 order: every
-        # micro-batch's N contributions are reduced and added into the fp32 shard
-        # (gbuf serves as the accumulator). ZeRO-1 order: each rank adds its whole
-        # local bf16 gradient into a full-size fp32 buffer; timed on S elements of it.
-        def accum_call(i):
-            for a, b in ranges:
-                zs.zs_accumulate_grads(rows_for(a, b), gbuf[a:b], scale=0.25)
-
-        put("accumulate_zero2", event_time_ms(accum_call, iters, stream), n_rows_bytes + 8)
-        local = rows[0][:min(csize, S)]
-        lacc = gbuf[:local.numel()]
-        put("accumulate_zero1_local", event_time_ms(lambda i: zs.zs_accumulate_local(local, lacc), iters,
-                                                    stream), row_bytes + 8, local.numel())
-        del gbuf, ws, partials, coef, lacc
-
-        # unshard copy-out of one decoder block: Llama-3-8B's (218,112,000 elements), or
-        # the 70B model's (855,654,400) for that workload
-        big = args.workload == "70b"
-        blk = shapes.llama_70b_block() if big else shapes.llama3_8b_block()
-        blk_name, blk_world = ("70b_block", 64) if big else ("llama8b_block", 8)
-        bn = shapes.numels(blk)
-        gathered_blk = gen.device_normal(g0, sum(bn), 1.0, torch.bfloat16, dev)
-        dst = [torch.empty(s, device=dev, dtype=torch.bfloat16) for _, s in blk]
-        table = zs.ParamTable(dst)
-        t_co = event_time_ms(lambda i: zs.zs_copy_out(gathered_blk, table), 10, stream)
-        gbs = 4 * sum(bn) / (t_co * 1e-3) / 1e9
-        parts[f"copy_out_{blk_name}"] = dict(ms=round(t_co, 5), elems=sum(bn), bytes_per_elem=4,
-                                               gb_s=round(gbs, 1), frac_of_peak=round(gbs / PEAK_HBM_GBS, 4))
-        if big:
-            # with reshard_after_forward every one of the 80 blocks is unsharded
-            # twice per step (forward and backward): the step's copy-out time
-            parts["copy_out_70b_per_step_ms"] = round(t_co * 160, 3)
-        # the same block under per-parameter dim-0 sharding (a scatter from the N rank
-        # regions of the gather buffer)
-        dtable = zs.Dim0Table(dst, blk_world)
-        gathered_d0 = gen.device_normal(g0, blk_world * dtable.local_total, 1.0, torch.bfloat16, dev)
-        t_cd = event_time_ms(lambda i: zs.zs_copy_out_dim0(gathered_d0, dtable), 10, stream)
-        gbs = 4 * sum(bn) / (t_cd * 1e-3) / 1e9
-        parts[f"copy_out_dim0_{blk_name}_n{blk_world}"] = dict(
-            ms=round(t_cd, 5), elems=sum(bn), bytes_per_elem=4, gb_s=round(gbs, 1),
-            frac_of_peak=round(gbs / PEAK_HBM_GBS, 4))
-        del gathered_blk, gathered_d0, dst, table, dtable
-        # GPT-2's list under dim-0 sharding at N=5: odd-sized bias and norm chunks
-        # put most pieces off the 16-byte grid (the realigning copy path)
-        g2 = shapes.gpt2_small()
-        g2n = shapes.numels(g2)
-        dst2 = [torch.empty(s, device=dev, dtype=torch.bfloat16) for _, s in g2]
-        dtab2 = zs.Dim0Table(dst2, 5)
-        gathered_g2 = gen.device_normal(g0, 5 * dtab2.local_total, 1.0, torch.bfloat16, dev)
-        t_g2 = event_time_ms(lambda i: zs.zs_copy_out_dim0(gathered_g2, dtab2), 10, stream)
-        gbs = 4 * sum(g2n) / (t_g2 * 1e-3) / 1e9
-        parts["copy_out_dim0_gpt2_n5_misaligned"] = dict(
-            ms=round(t_g2, 5), elems=sum(g2n), bytes_per_elem=4, gb_s=round(gbs, 1),
-            frac_of_peak=round(gbs / PEAK_HBM_GBS, 4))
-        del dst2, dtab2, gathered_g2
-        # dim-0 pack of the last rank's shard of the same block from fp32 parameters
-        src32 = [gen.device_normal(g0, shapes.numel(s), gen.THETA_SIGMA, None, dev).reshape(s) for _, s in blk]
-        ptab = zs.Dim0Table(src32, blk_world)
-        L = ptab.local_total
-        pm, pmm, pvv = (torch.empty(L, device=dev) for _ in range(3))
-        t_pd = event_time_ms(lambda i: zs.zs_pack_shard_dim0(ptab, blk_world - 1, pm, pmm, pvv), 10, stream)
-        put(f"pack_dim0_{blk_name}_n{blk_world}", t_pd, 16, L)
-        del src32, ptab, pm, pmm, pvv
-
-        # pack of this shard from per-parameter fp32 tensors (one-time setup work);
-        # a single 7.5e9-element parameter, or the 70B list (282 GB of fp32
-        # parameters), is represented by the rank's slice of it
-        if args.workload in ("7p5b", "70b"):
-            src = [gen.device_normal(g0, S, gen.THETA_SIGMA, None, dev)]
-            ptable, pworld, prank = zs.ParamTable(src), 1, 0
-        else:
-            src = [gen.device_normal(g0, n, gen.THETA_SIGMA, None, dev) for n in numels]
-            ptable, pworld, prank = zs.ParamTable(src), world, rank
-        t_pack = event_time_ms(lambda i: zs.zs_pack_shard(ptable, pworld, prank, theta, m, v), 5, stream)
-        gbs = 16 * S / (t_pack * 1e-3) / 1e9
-        parts["pack_shard"] = dict(ms=round(t_pack, 5), bytes_per_elem=16, gb_s=round(gbs, 1),
-                                   frac_of_peak=round(gbs / PEAK_HBM_GBS, 4))
-        del src, ptable
-        torch.cuda.synchronize()
-
-    # ---- CPU oracle on a bounded sample of the same inputs: one pass on one
-    # thread, then repeated passes spread over the host's cores (NumPy releases
-    # the GIL inside its array loops, so a thread pool runs them in parallel)
-    cpu = None
-    if cpu_inputs:
-        from concurrent.futures import ThreadPoolExecutor
-
-        from oracle import adamw as oadamw
-        from oracle import step as ostep
-
-        hpo = oadamw.HParams(**hp)
-
-        def one(win_in):
-            r_h, th_h, m_h, v_h = win_in
-            ostep.sharded_step(r_h, th_h, m_h, v_h, 1, hpo)
-            return th_h.size
-
-        w0 = time.perf_counter()
-        done1 = sum(one(x) for x in cpu_inputs)
-        wall1 = time.perf_counter() - w0
-        threads = max(1, min(args.cpu_threads, os.cpu_count() or 1))
-        c0, w0 = time.process_time(), time.perf_counter()
-        done, passes = 0, 0
-        with ThreadPoolExecutor(max_workers=threads) as ex:
-            while passes < 1 or time.perf_counter() - w0 < args.cpu_seconds:
-                done += sum(ex.map(one, cpu_inputs))
-                passes += 1
-        wall = time.perf_counter() - w0
-        cpu_s = time.process_time() - c0
-        model = "unknown"
-        try:
-            with open("/proc/cpuinfo") as f:
-                model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), model)
-        except OSError:
-            pass
-        cpu = {"value": round(done / wall / 1e9, 6), "unit": "Gelem/s",
-               "cores": max(1, round(cpu_s / wall)), "kind": "oracle",
-               "sample": f"{len(cpu_inputs)} windows of {win} shard elements x {world} "
-                         f"{'fp32' if row_bytes == 4 else 'bf16'} rows "
-                         f"(the GPU's own inputs), fp64 NumPy oracle: exact mean, AdamW, bf16 cast; "
-                         f"{passes} passes over a pool of {threads} threads, {wall:.1f} s wall, "
-                         f"{cpu_s:.1f} s of CPU time",
-               "single_thread_value": round(done1 / wall1 / 1e9, 6),
-               "cpu_model": model}
+    cpu_out = cpu.measure() if cpu is not None else None
 
     out = {
         "metric": METRIC,
@@ -496,6 +653,7 @@ def main() -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_steps": settle_steps,
         "ms_per_step": round(ms_step, 5),
         "step_ms": spread,
         "higher_is_better": True,
@@ -503,16 +661,7 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {
-            "workload": wl["desc"],
-            "shard_elems": S,
-            "world": world,
-            "rank": rank,
-            "contributions": "fp32" if row_bytes == 4 else "bf16",
-            "launches_per_step": len(ranges),
-            "step": "mean of N contributions + AdamW (fp32 master/m/v) + bf16 cast, one pass",
-            "adamw": hp,
-        },
+        "config": config,
         "roofline": {
             "bound": "hbm",
             "kernel": kernel_name,
@@ -522,11 +671,10 @@ def main() -> int:
             "frac": round(achieved / PEAK_HBM_GBS, 4),
             "algorithmic_bytes_per_elem": fused_bpe,
             "traffic": traffic,
-            "copy_ceiling_gb_s": round(copy_gbs, 1) if copy_gbs else None,
-            "frac_of_copy_ceiling": round(achieved / copy_gbs, 4) if copy_gbs else None,
+            "library_copy_gb_s": round(library_copy_gbs, 1) if library_copy_gbs else None,
             "runtime_copy_gb_s": round(runtime_copy_gbs, 1) if runtime_copy_gbs else None,
         },
-        "cpu_baseline": cpu,
+        "cpu_baseline": cpu_out,
         "parts": parts,
         "source_hash": src_hash,
     }

@@ -39,7 +39,7 @@ class AdamWHParams(C.Structure):
 _I64P = C.POINTER(C.c_int64)
 SIGNATURES = {
     "zs_flat_layout": (C.c_int32, [_I64P, C.c_int32, C.c_int32, _I64P, _I64P, _I64P, _I64P]),
-    "zs_check_layout": (C.c_int32, [C.POINTER(ParamDesc), C.c_int32, C.c_int64]),
+    "zs_check_layout": (C.c_int32, [C.POINTER(ParamDesc), C.c_int32, C.c_int64, C.c_int32]),
     "zs_pack_shard": (C.c_int32, [C.c_void_p, C.c_int32, C.c_int64, C.c_int32, C.c_int32,
                                   C.c_int32, C.c_int64, C.c_void_p, C.c_void_p, C.c_void_p,
                                   C.c_void_p]),
@@ -63,7 +63,7 @@ SIGNATURES = {
                                         C.c_void_p]),
     "zs_dim0_layout": (C.c_int32, [_I64P, _I64P, C.c_int32, C.c_int32, _I64P, _I64P, _I64P]),
     "zs_check_dim0_layout": (C.c_int32, [C.POINTER(Dim0Desc), C.c_int32, C.c_int32, C.c_int64,
-                                         C.c_int64]),
+                                         C.c_int64, C.c_int32]),
     "zs_pack_shard_dim0": (C.c_int32, [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
                                        C.c_int64, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]),
     "zs_copy_out_dim0": (C.c_int32, [C.c_void_p, C.c_int64, C.c_void_p, C.c_int32, C.c_int32,

@@ -91,7 +91,7 @@ class ParamTable:
             host[i].ptr = t.data_ptr()
             host[i].flat_offset = off
             host[i].numel = t.numel()
-        L.check("zs_check_layout", _lib().zs_check_layout(host, self.nparams, self.total))
+        L.check("zs_check_layout", _lib().zs_check_layout(host, self.nparams, self.total, _DTYPES[dtype]))
         device = device if device is not None else tensors[0].device
         raw = torch.frombuffer(bytearray(bytes(host)), dtype=torch.uint8)
         self.device_table = raw.to(device)
@@ -182,7 +182,7 @@ class Dim0Table:
             host[i].chunk = self.chunks[i]
             host[i].local_offset = self.local_offsets[i]
         L.check("zs_check_dim0_layout", _lib().zs_check_dim0_layout(
-            host, self.nparams, self.world, self.total, self.local_total))
+            host, self.nparams, self.world, self.total, self.local_total, _DTYPES[dtype]))
         device = device if device is not None else tensors[0].device
         raw = torch.frombuffer(bytearray(bytes(host)), dtype=torch.uint8)
         self.device_table = raw.to(device)

@@ -42,7 +42,15 @@ zs_status check_rows(const void* const* rows, int32_t world, int32_t dtype, int6
   return ZS_OK;
 }
 
-inline zs_status hip_status(hipError_t e) { return e == hipSuccess ? ZS_OK : ZS_ERR_HIP; }
+// Device work goes through launch(): a HIP error already pending on this thread
+// (left by an earlier, unrelated call) is handed back as ZS_ERR_HIP before
+// anything is enqueued, and stays pending for the caller; otherwise the status
+// is that of this call's own launches.
+template <typename F>
+zs_status launch(F&& f) {
+  if (hipPeekAtLastError() != hipSuccess) return ZS_ERR_HIP;
+  return f() == hipSuccess ? ZS_OK : ZS_ERR_HIP;
+}
 
 // The sum of squares' workspace and result are written while the rows are read
 // and `out` (n fp32) is written: none of them may share bytes.
@@ -117,7 +125,9 @@ zs_status zs_flat_layout(const int64_t* numels, int32_t nparams, int32_t world,
   return ZS_OK;
 }
 
-zs_status zs_check_layout(const zs_param_desc* host_desc, int32_t nparams, int64_t total) {
+zs_status zs_check_layout(const zs_param_desc* host_desc, int32_t nparams, int64_t total,
+                          int32_t dtype) {
+  if (dtype != ZS_F32 && dtype != ZS_BF16) return ZS_ERR_DTYPE;
   if (nparams < 0 || total < 0) return ZS_ERR_SIZE;
   if (nparams == 0) return total == 0 ? ZS_OK : ZS_ERR_LAYOUT;
   if (!host_desc) return ZS_ERR_NULL;
@@ -127,6 +137,7 @@ zs_status zs_check_layout(const zs_param_desc* host_desc, int32_t nparams, int64
     if (d.numel < 0) return ZS_ERR_SIZE;
     if (d.flat_offset != run) return ZS_ERR_LAYOUT;
     if (d.numel > 0 && !d.ptr) return ZS_ERR_NULL;
+    if (d.numel > 0 && !aligned(d.ptr, (uintptr_t)elem_size(dtype))) return ZS_ERR_ALIGN;
     if (d.numel > INT64_MAX - run) return ZS_ERR_SIZE;
     run += d.numel;
   }
@@ -158,9 +169,9 @@ zs_status zs_pack_shard(const zs_param_desc* d_desc, int32_t nparams, int64_t to
       overlaps(master, b, exp_avg_sq, exp_avg_sq ? b : 0) ||
       overlaps(exp_avg, exp_avg ? b : 0, exp_avg_sq, exp_avg_sq ? b : 0))
     return ZS_ERR_OVERLAP;
-  return hip_status(zs::launch_pack(d_desc, nparams, total_numel, src_dtype,
+  return launch([&] { return zs::launch_pack(d_desc, nparams, total_numel, src_dtype,
                                     (int64_t)rank * shard_numel, shard_numel, master, exp_avg,
-                                    exp_avg_sq, stream));
+                                    exp_avg_sq, stream); });
 }
 
 zs_status zs_reduce_grads(const void* const* rows, int32_t world, int32_t dtype, int64_t n,
@@ -180,13 +191,13 @@ zs_status zs_reduce_grads(const void* const* rows, int32_t world, int32_t dtype,
   if (n == 0) {
     if (!sumsq_out) return ZS_OK;
     // an empty shard's sum of squares is 0; written by the finalize kernel
-    return hip_status(zs::launch_reduce(rows, world, dtype, 0, grad_out, sumsq_out,
-                                        static_cast<double*>(workspace), stream));
+    return launch([&] { return zs::launch_reduce(rows, world, dtype, 0, grad_out, sumsq_out,
+                                        static_cast<double*>(workspace), stream); });
   }
   for (int32_t q = 0; q < world; ++q)
     if (overlaps(grad_out, n * 4, rows[q], n * elem_size(dtype))) return ZS_ERR_OVERLAP;
-  return hip_status(zs::launch_reduce(rows, world, dtype, n, grad_out, sumsq_out,
-                                      static_cast<double*>(workspace), stream));
+  return launch([&] { return zs::launch_reduce(rows, world, dtype, n, grad_out, sumsq_out,
+                                      static_cast<double*>(workspace), stream); });
 }
 
 zs_status zs_adamw_step(float* master, float* exp_avg, float* exp_avg_sq, const float* grad,
@@ -210,8 +221,9 @@ zs_status zs_adamw_step(float* master, float* exp_avg, float* exp_avg_sq, const 
                    overlaps(bf16_out, n * 2, exp_avg_sq, b) || overlaps(bf16_out, n * 2, grad, b)))
     return ZS_ERR_OVERLAP;
   if (scale_overlaps(grad_scale, master, exp_avg, exp_avg_sq, n, bf16_out)) return ZS_ERR_OVERLAP;
-  return hip_status(
-      zs::launch_adamw(master, exp_avg, exp_avg_sq, grad, n, *hp, grad_scale, bf16_out, stream));
+  return launch([&] {
+    return zs::launch_adamw(master, exp_avg, exp_avg_sq, grad, n, *hp, grad_scale, bf16_out, stream);
+  });
 }
 
 zs_status zs_cast_for_gather(const float* master, int64_t n, uint16_t* gather_slot,
@@ -221,7 +233,7 @@ zs_status zs_cast_for_gather(const float* master, int64_t n, uint16_t* gather_sl
   if (!master || !gather_slot) return ZS_ERR_NULL;
   if (!aligned(master, 4) || !aligned(gather_slot, 2)) return ZS_ERR_ALIGN;
   if (overlaps(master, n * 4, gather_slot, n * 2)) return ZS_ERR_OVERLAP;
-  return hip_status(zs::launch_cast(master, n, gather_slot, stream));
+  return launch([&] { return zs::launch_cast(master, n, gather_slot, stream); });
 }
 
 zs_status zs_copy_out(const uint16_t* gathered, int64_t gathered_numel, const zs_param_desc* d_desc,
@@ -232,7 +244,7 @@ zs_status zs_copy_out(const uint16_t* gathered, int64_t gathered_numel, const zs
   if (total_numel == 0) return ZS_OK;
   if (!gathered || !d_desc) return ZS_ERR_NULL;
   if (!aligned(gathered, 2) || !aligned(d_desc, 8)) return ZS_ERR_ALIGN;
-  return hip_status(zs::launch_copy_out(gathered, d_desc, nparams, total_numel, stream));
+  return launch([&] { return zs::launch_copy_out(gathered, d_desc, nparams, total_numel, stream); });
 }
 
 zs_status zs_dim0_layout(const int64_t* dim0, const int64_t* rowsize, int32_t nparams, int32_t world,
@@ -256,7 +268,8 @@ zs_status zs_dim0_layout(const int64_t* dim0, const int64_t* rowsize, int32_t np
 }
 
 zs_status zs_check_dim0_layout(const zs_dim0_desc* host_desc, int32_t nparams, int32_t world,
-                               int64_t total, int64_t local_total) {
+                               int64_t total, int64_t local_total, int32_t dtype) {
+  if (dtype != ZS_F32 && dtype != ZS_BF16) return ZS_ERR_DTYPE;
   if (nparams < 0 || total < 0 || local_total < 0) return ZS_ERR_SIZE;
   if (world < 1) return ZS_ERR_WORLD;
   if (nparams == 0) return total == 0 && local_total == 0 ? ZS_OK : ZS_ERR_LAYOUT;
@@ -267,6 +280,7 @@ zs_status zs_check_dim0_layout(const zs_dim0_desc* host_desc, int32_t nparams, i
     if (d.numel < 0 || d.chunk < 0) return ZS_ERR_SIZE;
     if (d.flat_offset != run || d.local_offset != lrun) return ZS_ERR_LAYOUT;
     if (d.numel > 0 && !d.ptr) return ZS_ERR_NULL;
+    if (d.numel > 0 && !aligned(d.ptr, (uintptr_t)elem_size(dtype))) return ZS_ERR_ALIGN;
     // the N chunks must cover the parameter: numel <= world * chunk
     if (d.chunk < d.numel / world + (d.numel % world != 0)) return ZS_ERR_LAYOUT;
     if (d.numel > INT64_MAX - run || d.chunk > INT64_MAX - lrun) return ZS_ERR_SIZE;
@@ -295,8 +309,8 @@ zs_status zs_pack_shard_dim0(const zs_dim0_desc* d_desc, int32_t nparams, int32_
       overlaps(master, b, exp_avg_sq, exp_avg_sq ? b : 0) ||
       overlaps(exp_avg, exp_avg ? b : 0, exp_avg_sq, exp_avg_sq ? b : 0))
     return ZS_ERR_OVERLAP;
-  return hip_status(zs::launch_pack_dim0(d_desc, nparams, src_dtype, rank, local_total, master,
-                                         exp_avg, exp_avg_sq, stream));
+  return launch([&] { return zs::launch_pack_dim0(d_desc, nparams, src_dtype, rank, local_total, master,
+                                         exp_avg, exp_avg_sq, stream); });
 }
 
 zs_status zs_copy_out_dim0(const uint16_t* gathered, int64_t gathered_numel,
@@ -310,8 +324,9 @@ zs_status zs_copy_out_dim0(const uint16_t* gathered, int64_t gathered_numel,
   if (total == 0) return ZS_OK;
   if (!gathered || !d_desc) return ZS_ERR_NULL;
   if (!aligned(gathered, 2) || !aligned(d_desc, 8)) return ZS_ERR_ALIGN;
-  return hip_status(
-      zs::launch_copy_out_dim0(gathered, d_desc, nparams, world, total, local_total, stream));
+  return launch([&] {
+    return zs::launch_copy_out_dim0(gathered, d_desc, nparams, world, total, local_total, stream);
+  });
 }
 
 zs_status zs_sharded_step(const void* const* rows, int32_t world, int32_t dtype, int64_t n,
@@ -341,8 +356,8 @@ zs_status zs_sharded_step(const void* const* rows, int32_t world, int32_t dtype,
                    overlaps(bf16_out, n * 2, exp_avg_sq, b)))
     return ZS_ERR_OVERLAP;
   if (scale_overlaps(grad_scale, master, exp_avg, exp_avg_sq, n, bf16_out)) return ZS_ERR_OVERLAP;
-  return hip_status(zs::launch_fused(rows, world, dtype, n, master, exp_avg, exp_avg_sq, *hp,
-                                     grad_scale, bf16_out, stream));
+  return launch([&] { return zs::launch_fused(rows, world, dtype, n, master, exp_avg, exp_avg_sq, *hp,
+                                     grad_scale, bf16_out, stream); });
 }
 
 zs_status zs_accumulate_grads(const void* const* rows, int32_t world, int32_t dtype, int64_t n,
@@ -363,8 +378,8 @@ zs_status zs_accumulate_grads(const void* const* rows, int32_t world, int32_t dt
   if (n == 0 && !sumsq_out) return ZS_OK;
   for (int32_t q = 0; q < world && n > 0; ++q)
     if (overlaps(acc, n * 4, rows[q], n * elem_size(dtype))) return ZS_ERR_OVERLAP;
-  return hip_status(zs::launch_accumulate(rows, world, dtype, n, acc, scale, first != 0, sumsq_out,
-                                          static_cast<double*>(workspace), stream));
+  return launch([&] { return zs::launch_accumulate(rows, world, dtype, n, acc, scale, first != 0, sumsq_out,
+                                          static_cast<double*>(workspace), stream); });
 }
 
 zs_status zs_accumulate_local(const void* grad, int32_t dtype, int64_t n, float* acc,
@@ -375,7 +390,7 @@ zs_status zs_accumulate_local(const void* grad, int32_t dtype, int64_t n, float*
   if (!grad || !acc) return ZS_ERR_NULL;
   if (!aligned(grad, (uintptr_t)elem_size(dtype)) || !aligned(acc, 4)) return ZS_ERR_ALIGN;
   if (overlaps(grad, n * elem_size(dtype), acc, n * 4)) return ZS_ERR_OVERLAP;
-  return hip_status(zs::launch_accumulate_local(grad, dtype, n, acc, first != 0, stream));
+  return launch([&] { return zs::launch_accumulate_local(grad, dtype, n, acc, first != 0, stream); });
 }
 
 zs_status zs_clip_coefficient(const double* partials, int32_t count, double max_norm,
@@ -385,7 +400,7 @@ zs_status zs_clip_coefficient(const double* partials, int32_t count, double max_
   if (!partials || !coef_out) return ZS_ERR_NULL;
   if (!aligned(partials, 8) || !aligned(coef_out, 4) || (norm_out && !aligned(norm_out, 8)))
     return ZS_ERR_ALIGN;
-  return hip_status(zs::launch_clip(partials, count, max_norm, coef_out, norm_out, stream));
+  return launch([&] { return zs::launch_clip(partials, count, max_norm, coef_out, norm_out, stream); });
 }
 
 }  // extern "C"

@@ -10,27 +10,32 @@ namespace zs {
 const Tuning& tuning() {
   static const Tuning t = [] {
     Tuning x{0, 0, 0, 0, 0, 0, 0, 0, 0};
+    // the overrides below are read only when ZS_TUNING=1 opts in, so that a
+    // stray variable cannot change launch shapes unnoticed
+    const char* on = std::getenv("ZS_TUNING");
+    const bool use_env = on && on[0] == '1' && on[1] == '\0';
+    auto env = [use_env](const char* name) -> const char* { return use_env ? std::getenv(name) : nullptr; };
     const char* e;
-    x.adamw_v = (e = std::getenv("ZS_ADAMW_V")) ? std::atoi(e) : 1;
+    x.adamw_v = (e = env("ZS_ADAMW_V")) ? std::atoi(e) : 1;
     if (x.adamw_v != 1 && x.adamw_v != 2 && x.adamw_v != 4) x.adamw_v = 1;
     // a 16 KiB reservation (10 one-wave workgroups per CU) measured best for AdamW
-    x.adamw_lds = (e = std::getenv("ZS_ADAMW_LDS")) ? std::atoll(e) : 16384;
+    x.adamw_lds = (e = env("ZS_ADAMW_LDS")) ? std::atoll(e) : 16384;
     if (x.adamw_lds < 0 || x.adamw_lds > 65536) x.adamw_lds = 16384;
-    x.rank_chunk = (e = std::getenv("ZS_RANK_CHUNK")) ? std::atoi(e) : 8;
+    x.rank_chunk = (e = env("ZS_RANK_CHUNK")) ? std::atoi(e) : 8;
     if (x.rank_chunk != 4 && x.rank_chunk != 8) x.rank_chunk = 8;
-    x.fused_g = (e = std::getenv("ZS_FUSED_G")) ? std::atoi(e) : 0;
+    x.fused_g = (e = env("ZS_FUSED_G")) ? std::atoi(e) : 0;
     if (x.fused_g != 1 && x.fused_g != 2 && x.fused_g != 4 && x.fused_g != 8 && x.fused_g != 16) x.fused_g = 0;
-    x.fused_lds = (e = std::getenv("ZS_FUSED_LDS")) ? std::atoll(e) : 0;
+    x.fused_lds = (e = env("ZS_FUSED_LDS")) ? std::atoll(e) : 0;
     if (x.fused_lds < 0 || x.fused_lds > 65536) x.fused_lds = 0;
-    x.fused_bs = (e = std::getenv("ZS_FUSED_BS")) ? std::atoi(e) : 0;
+    x.fused_bs = (e = env("ZS_FUSED_BS")) ? std::atoi(e) : 0;
     if (x.fused_bs != 64 && x.fused_bs != 256) x.fused_bs = 0;
-    x.accum_shape = (e = std::getenv("ZS_ACCUM_SHAPE")) ? std::atoi(e) : 0;
+    x.accum_shape = (e = env("ZS_ACCUM_SHAPE")) ? std::atoi(e) : 0;
     if (x.accum_shape != 1) x.accum_shape = 0;
-    x.reduce_g = (e = std::getenv("ZS_REDUCE_G")) ? std::atoi(e) : 0;
+    x.reduce_g = (e = env("ZS_REDUCE_G")) ? std::atoi(e) : 0;
     if (x.reduce_g != 1 && x.reduce_g != 4 && x.reduce_g != 16) x.reduce_g = 0;
     // an optional cap on workgroups per launch (grid-stride loops cover the
     // rest); launches also stay within the 32-bit work-item count of a dispatch
-    x.grid_cap = (e = std::getenv("ZS_GRID_CAP")) ? std::atoll(e) : 0;
+    x.grid_cap = (e = env("ZS_GRID_CAP")) ? std::atoll(e) : 0;
     if (x.grid_cap <= 0) x.grid_cap = INT64_MAX;
     return x;
   }();

@@ -37,8 +37,17 @@
  *     stream has completed. No call synchronises.
  *   - Errors: arguments are checked on the host before anything is enqueued;
  *     a failed check returns a negative ZS_ERR_* code and enqueues nothing.
- *     A HIP launch failure returns ZS_ERR_HIP. zs_status_string() names
- *     every code.
+ *     A HIP launch failure returns ZS_ERR_HIP. A HIP error already pending on
+ *     the calling thread when a call that launches work begins (left by an
+ *     earlier, unrelated HIP call) is also returned as ZS_ERR_HIP, before
+ *     anything is enqueued, and is left pending for the caller to read and
+ *     clear (hipGetLastError). zs_status_string() names every code.
+ *   - Launch shapes: chosen per call from the sizes and world size. The
+ *     environment variables ZS_ADAMW_V, ZS_ADAMW_LDS, ZS_RANK_CHUNK,
+ *     ZS_FUSED_G, ZS_FUSED_LDS, ZS_FUSED_BS, ZS_ACCUM_SHAPE, ZS_REDUCE_G and
+ *     ZS_GRID_CAP override them for measurement sweeps, and are read only when
+ *     ZS_TUNING=1 is set, once per process, at the first call; they change
+ *     speed, never results.
  *   - Sizes are element counts (int64_t); n == 0 is a valid no-op.
  *   - bf16 values are passed as uint16_t bit patterns (the top half of an
  *     IEEE fp32). fp32 -> bf16 is round-to-nearest-even; NaN stays a quiet
@@ -136,10 +145,14 @@ zs_status zs_flat_layout(const int64_t* numels, int32_t nparams, int32_t world,
 /*
  * zs_check_layout -- verify on the host that a descriptor table (HOST memory)
  * tiles [0, total) in order and that every non-empty parameter has a non-NULL
- * pointer. Returns ZS_OK or ZS_ERR_NULL / ZS_ERR_SIZE / ZS_ERR_LAYOUT.
- * Callers build the device copy of the table from a table that passed.
+ * pointer aligned to its element size (`dtype`: ZS_F32 sources 4 bytes, ZS_BF16
+ * sources and copy-out destinations 2 bytes). Returns ZS_OK or ZS_ERR_NULL /
+ * ZS_ERR_SIZE / ZS_ERR_LAYOUT / ZS_ERR_ALIGN / ZS_ERR_DTYPE. The pack and
+ * copy-out kernels rely on these properties of the device table without
+ * re-checking it, so callers build the device copy from a table that passed.
  */
-zs_status zs_check_layout(const zs_param_desc* host_desc, int32_t nparams, int64_t total);
+zs_status zs_check_layout(const zs_param_desc* host_desc, int32_t nparams, int64_t total,
+                          int32_t dtype);
 
 /*
  * zs_pack_shard -- the rank's fp32 master slice of the padded FlatParameter.
@@ -358,11 +371,12 @@ zs_status zs_dim0_layout(const int64_t* dim0, const int64_t* rowsize, int32_t np
 /*
  * zs_check_dim0_layout -- verify a HOST table: flat offsets tile [0, total),
  * local offsets tile [0, local_total) with the chunk sizes, numel <= world *
- * chunk, and non-empty parameters have storage. Returns ZS_OK or
- * ZS_ERR_NULL / ZS_ERR_SIZE / ZS_ERR_WORLD / ZS_ERR_LAYOUT.
+ * chunk, and non-empty parameters have storage aligned to the element size of
+ * `dtype` (as zs_check_layout). Returns ZS_OK or ZS_ERR_NULL / ZS_ERR_SIZE /
+ * ZS_ERR_WORLD / ZS_ERR_LAYOUT / ZS_ERR_ALIGN / ZS_ERR_DTYPE.
  */
 zs_status zs_check_dim0_layout(const zs_dim0_desc* host_desc, int32_t nparams, int32_t world,
-                               int64_t total, int64_t local_total);
+                               int64_t total, int64_t local_total, int32_t dtype);
 
 /*
  * zs_pack_shard_dim0 -- rank r's fp32 master shard under dim-0 sharding

@@ -131,8 +131,8 @@ int main(int argc, char** argv) {
     out_desc[i] = zs_param_desc{outs[i], offsets[i], numel[i]};
     src_desc[i] = zs_param_desc{srcs[i], offsets[i], numel[i]};
   }
-  ZS_OK_OR_EXIT(zs_check_layout(out_desc.data(), nparams, total));
-  ZS_OK_OR_EXIT(zs_check_layout(src_desc.data(), nparams, total));
+  ZS_OK_OR_EXIT(zs_check_layout(out_desc.data(), nparams, total, ZS_BF16));
+  ZS_OK_OR_EXIT(zs_check_layout(src_desc.data(), nparams, total, ZS_F32));
   zs_param_desc* d_out_desc = dev_copy(out_desc.data(), nparams);
   zs_param_desc* d_src_desc = dev_copy(src_desc.data(), nparams);
   ZS_OK_OR_EXIT(zs_copy_out(d_out, n, d_out_desc, nparams, total, s));
@@ -167,8 +167,8 @@ int main(int argc, char** argv) {
     src0[i] = zs_dim0_desc{srcs[i], offsets[i], numel[i], chunk[i], loff[i]};
     dst0[i] = zs_dim0_desc{outs0[i], offsets[i], numel[i], chunk[i], loff[i]};
   }
-  ZS_OK_OR_EXIT(zs_check_dim0_layout(src0.data(), nparams, world, total, L));
-  ZS_OK_OR_EXIT(zs_check_dim0_layout(dst0.data(), nparams, world, total, L));
+  ZS_OK_OR_EXIT(zs_check_dim0_layout(src0.data(), nparams, world, total, L, ZS_F32));
+  ZS_OK_OR_EXIT(zs_check_dim0_layout(dst0.data(), nparams, world, total, L, ZS_BF16));
   zs_dim0_desc* d_src0 = dev_copy(src0.data(), nparams);
   zs_dim0_desc* d_dst0 = dev_copy(dst0.data(), nparams);
   const int64_t wl = (int64_t)world * L;

@@ -98,15 +98,30 @@ def _table(entries):
 
 def test_check_layout(lib):
     ok = _table([(0x1000, 0, 4), (0x2000, 4, 0), (0x3000, 4, 6)])
-    assert lib.zs_check_layout(ok, 3, 10) == 0
-    assert lib.zs_check_layout(ok, 3, 11) == -9
-    assert lib.zs_check_layout(_table([(0x1000, 1, 4)]), 1, 5) == -9
-    assert lib.zs_check_layout(_table([(0x1000, 0, 4), (0x2000, 5, 1)]), 2, 6) == -9
-    assert lib.zs_check_layout(_table([(None, 0, 4)]), 1, 4) == -1
-    assert lib.zs_check_layout(_table([(None, 0, 0)]), 1, 0) == 0  # empty params need no storage
-    assert lib.zs_check_layout(_table([(0x1000, 0, -1)]), 1, -1) == -2
-    assert lib.zs_check_layout(None, 0, 0) == 0
-    assert lib.zs_check_layout(None, 0, 3) == -9
+    assert lib.zs_check_layout(ok, 3, 10, 1) == 0
+    assert lib.zs_check_layout(ok, 3, 11, 1) == -9
+    assert lib.zs_check_layout(_table([(0x1000, 1, 4)]), 1, 5, 1) == -9
+    assert lib.zs_check_layout(_table([(0x1000, 0, 4), (0x2000, 5, 1)]), 2, 6, 1) == -9
+    assert lib.zs_check_layout(_table([(None, 0, 4)]), 1, 4, 1) == -1
+    assert lib.zs_check_layout(_table([(None, 0, 0)]), 1, 0, 1) == 0  # empty params need no storage
+    assert lib.zs_check_layout(_table([(0x1000, 0, -1)]), 1, -1, 1) == -2
+    assert lib.zs_check_layout(None, 0, 0, 1) == 0
+    assert lib.zs_check_layout(None, 0, 3, 1) == -9
+
+
+def test_check_layout_element_alignment(lib):
+    # fp32 parameters need 4-byte storage, bf16 ones 2-byte storage; the pack and
+    # copy-out kernels derive their vector heads from these addresses
+    assert lib.zs_check_layout(_table([(0x1002, 0, 4)]), 1, 4, 1) == 0
+    assert lib.zs_check_layout(_table([(0x1002, 0, 4)]), 1, 4, 0) == -10
+    assert lib.zs_check_layout(_table([(0x1000, 0, 4), (0x2001, 4, 3)]), 2, 7, 1) == -10
+    assert lib.zs_check_layout(_table([(0x1000, 0, 4), (0x2001, 4, 0)]), 2, 4, 0) == 0  # empty: unused
+    assert lib.zs_check_layout(_table([(0x1000, 0, 4)]), 1, 4, 7) == -5
+    f = lib.zs_check_dim0_layout
+    assert f(_dtable([(0x1006, 0, 10, 5, 0)]), 1, 2, 10, 5, 1) == 0
+    assert f(_dtable([(0x1006, 0, 10, 5, 0)]), 1, 2, 10, 5, 0) == -10
+    assert f(_dtable([(0x1003, 0, 10, 5, 0)]), 1, 2, 10, 5, 1) == -10
+    assert f(_dtable([(0x1000, 0, 10, 5, 0)]), 1, 2, 10, 5, 2) == -5
 
 
 def test_workspace_bytes(lib):
@@ -303,19 +318,19 @@ def _dtable(entries):
 def test_check_dim0_layout(lib):
     ok = _dtable([(0x1000, 0, 10, 6, 0), (0x2000, 10, 0, 0, 6), (0x3000, 10, 7, 4, 6)])
     f = lib.zs_check_dim0_layout
-    assert f(ok, 3, 2, 17, 10) == 0
-    assert f(ok, 3, 2, 18, 10) == -9
-    assert f(ok, 3, 2, 17, 11) == -9
-    assert f(ok, 3, 1, 17, 10) == -9       # one rank cannot hold 10 elements in a chunk of 6
-    assert f(ok, 3, 0, 17, 10) == -3
-    assert f(_dtable([(0x1000, 0, 10, 4, 0)]), 1, 2, 10, 4) == -9      # 2 * 4 < 10
-    assert f(_dtable([(0x1000, 0, 10, 5, 1)]), 1, 2, 10, 6) == -9      # local offset gap
-    assert f(_dtable([(0x1000, 1, 10, 5, 0)]), 1, 2, 11, 5) == -9      # flat offset gap
-    assert f(_dtable([(None, 0, 4, 2, 0)]), 1, 2, 4, 2) == -1
-    assert f(_dtable([(None, 0, 0, 3, 0)]), 1, 2, 0, 3) == 0   # empty params need no storage
-    assert f(_dtable([(0x1000, 0, -1, 2, 0)]), 1, 2, -1, 2) == -2
-    assert f(None, 0, 2, 0, 0) == 0
-    assert f(None, 0, 2, 0, 1) == -9
+    assert f(ok, 3, 2, 17, 10, 1) == 0
+    assert f(ok, 3, 2, 18, 10, 1) == -9
+    assert f(ok, 3, 2, 17, 11, 1) == -9
+    assert f(ok, 3, 1, 17, 10, 1) == -9       # one rank cannot hold 10 elements in a chunk of 6
+    assert f(ok, 3, 0, 17, 10, 1) == -3
+    assert f(_dtable([(0x1000, 0, 10, 4, 0)]), 1, 2, 10, 4, 1) == -9      # 2 * 4 < 10
+    assert f(_dtable([(0x1000, 0, 10, 5, 1)]), 1, 2, 10, 6, 1) == -9      # local offset gap
+    assert f(_dtable([(0x1000, 1, 10, 5, 0)]), 1, 2, 11, 5, 1) == -9      # flat offset gap
+    assert f(_dtable([(None, 0, 4, 2, 0)]), 1, 2, 4, 2, 1) == -1
+    assert f(_dtable([(None, 0, 0, 3, 0)]), 1, 2, 0, 3, 1) == 0   # empty params need no storage
+    assert f(_dtable([(0x1000, 0, -1, 2, 0)]), 1, 2, -1, 2, 1) == -2
+    assert f(None, 0, 2, 0, 0, 1) == 0
+    assert f(None, 0, 2, 0, 1, 1) == -9
 
 
 def test_dim0_pack_copy_out_errors(lib):

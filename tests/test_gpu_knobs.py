@@ -1,7 +1,8 @@
 """Every launch-shape knob leaves every result unchanged, bit for bit (the fp64
 sum of squares to within its rounding, since it is associated per workgroup).
 
-The knobs (ZS_* environment variables, read once per process) pick workgroup
+The knobs (ZS_* environment variables, read once per process and only when
+ZS_TUNING=1 opts in) pick workgroup
 sizes, staging depths, rank-chunk widths, LDS reservations and grid caps. Each
 case below runs the same seeded update in a child process under one setting
 (a grid cap of a few workgroups forces every kernel through its grid-stride
@@ -94,6 +95,8 @@ SETTINGS = [
 def _run(tmp_path, env_over, tag):
     env = {k: v for k, v in os.environ.items() if not k.startswith("ZS_")}
     env.update(env_over)
+    if env_over:
+        env["ZS_TUNING"] = "1"
     path = str(tmp_path / f"{tag}.npz")
     print(f"knobs {env_over}", flush=True)
     res = subprocess.run([sys.executable, "-c", CHILD, path, ROOT], env=env, capture_output=True,

@@ -1,0 +1,153 @@
+"""Non-finite gradients reach exactly the elements they touch, through every
+update entry point.
+
+"Data parallelism and ZeRO memory sharding" s4.2 (exception recovery): a NaN
+or Inf in one rank's gradient must be visible where it lands -- so that a
+loss-scaler or a skip-step check can see it -- and must not leak into other
+elements. Each case runs the same inputs twice, once clean and once with NaN
+and +Inf planted at a few indices of one rank's contribution (or of the
+gradient given to AdamW): the poisoned run's theta, m, v and bf16 output are
+non-finite at exactly those indices, of the kind the oracle's arithmetic gives
+(+Inf in g: m and v are +Inf, theta NaN), and every other element is
+bit-identical to the clean run. The indices cover the first element, workgroup
+tile boundaries and the ragged tail that the element-wise code handles.
+"""
+import numpy as np
+import pytest
+import torch
+
+import fsdp_sharded_optimizer_flatparameter_amd as zs
+from oracle import adamw as oadamw
+from _gpu import device_rows, device_state, hparams, host
+
+pytestmark = pytest.mark.gpu
+
+
+def _indices(n, tile):
+    """Planted NaN and +Inf positions: first element, around tile boundaries,
+    the last 4-element group and the ragged tail (n % 4 elements)."""
+    nan = sorted({0, tile - 1, n - 1, (2 * tile + 5) % n})
+    inf = sorted({tile, tile + 1, n - 4, (3 * tile // 2) % n} - set(nan))
+    return nan, inf
+
+
+def _bits(t):
+    a = host(t)
+    return a.view(np.uint32) if a.dtype == np.float32 else a
+
+
+def _classes(a):
+    """Per element: 0 finite, 1 NaN, 2 +Inf, 3 -Inf."""
+    a = np.asarray(a)
+    if a.dtype == np.uint16:  # bf16 patterns
+        a = (a.astype(np.uint32) << 16).view(np.float32)
+    elif a.dtype == np.uint32:  # fp32 patterns
+        a = a.view(np.float32)
+    c = np.zeros(a.shape, np.int8)
+    c[np.isnan(a)] = 1
+    c[np.isposinf(a)] = 2
+    c[np.isneginf(a)] = 3
+    return c
+
+
+def _expected_classes(n, nan, inf, scale=1.0):
+    """What the oracle's AdamW gives at the planted positions, on the same
+    gradient magnitudes (a NaN or +Inf entry in g)."""
+    g = np.zeros(n, np.float32)
+    g[nan] = np.nan
+    g[inf] = np.inf
+    g = (g * np.float32(scale)).astype(np.float32)
+    with np.errstate(invalid="ignore", over="ignore"):
+        th, m, v = oadamw.adamw_step(np.full(n, 0.01, np.float32), np.zeros(n, np.float32),
+                                     np.zeros(n, np.float32), g, 3, oadamw.HParams(**hparams()))
+    return _classes(th), _classes(m), _classes(v)
+
+
+def _compare(clean, poisoned, nan, inf, n, expect):
+    planted = np.zeros(n, bool)
+    planted[nan + inf] = True
+    for name, a, b, want in zip(("theta", "m", "v", "bf16"), clean, poisoned, expect):
+        cb = _classes(b)
+        assert np.array_equal(np.nonzero(cb)[0], np.nonzero(planted)[0]), f"{name}: non-finite elsewhere"
+        assert np.array_equal(cb[planted], want[planted]), f"{name}: wrong kind of non-finite value"
+        assert np.array_equal(a[~planted], b[~planted]), f"{name}: a clean element changed"
+        assert np.all(_classes(a) == 0), f"{name}: the clean run is not finite"
+
+
+def _state_copies(n, seed):
+    th, m, v = device_state(seed, n)
+    return (th, m, v), tuple(t.clone() for t in (th, m, v))
+
+
+# (world, n, tile of the launch shape that world selects: 4-wave workgroups of 16
+# staged groups with many contributions, one-wave single-group ones with few)
+SHAPES = [(64, 3 * 16384 + 4096 + 3, 16384), (8, 70001, 256), (3, 9 * 256 + 2, 256)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("world,n,tile", SHAPES)
+def test_sharded_step_nonfinite_reach_exactly_their_elements(dtype, world, n, tile):
+    nan, inf = _indices(n, tile)
+    rows = device_rows(700 + world, world, n, dtype)
+    bad = [r.clone() for r in rows]
+    q = world // 2
+    bad[q][nan] = float("nan")
+    bad[q][inf] = float("inf")
+    (st_c, st_p) = _state_copies(n, 701 + world)
+    outs = []
+    for rr, (th, m, v) in ((rows, st_c), (bad, st_p)):
+        out = torch.empty(n, device="cuda", dtype=torch.bfloat16)
+        zs.zs_sharded_step(rr, th, m, v, step=3, bf16_out=out, **hparams())
+        outs.append((th, m, v, out))
+    torch.cuda.synchronize()
+    clean = [_bits(t) for t in outs[0]]
+    poisoned = [_bits(t) for t in outs[1]]
+    th_c, m_c, v_c = _expected_classes(n, nan, inf)
+    _compare(clean, poisoned, nan, inf, n, (th_c, m_c, v_c, th_c))
+
+
+@pytest.mark.parametrize("scaled", [False, True])
+def test_adamw_nonfinite_gradient_reaches_exactly_its_elements(scaled):
+    n = 262144 + 5
+    nan, inf = _indices(n, 256)
+    g = device_rows(710, 1, n, "f32")[0]
+    gb = g.clone()
+    gb[nan] = float("nan")
+    gb[inf] = float("inf")
+    sc = torch.tensor([0.5], device="cuda") if scaled else None
+    (st_c, st_p) = _state_copies(n, 711)
+    outs = []
+    for gg, (th, m, v) in ((g, st_c), (gb, st_p)):
+        out = torch.empty(n, device="cuda", dtype=torch.bfloat16)
+        zs.zs_adamw_step(th, m, v, gg, step=3, grad_scale=sc, bf16_out=out, **hparams())
+        outs.append((th, m, v, out))
+    torch.cuda.synchronize()
+    th_c, m_c, v_c = _expected_classes(n, nan, inf, 0.5 if scaled else 1.0)
+    _compare([_bits(t) for t in outs[0]], [_bits(t) for t in outs[1]], nan, inf, n, (th_c, m_c, v_c, th_c))
+
+
+@pytest.mark.parametrize("world,n,tile", SHAPES)
+def test_accumulate_nonfinite_reach_exactly_their_elements(world, n, tile):
+    nan, inf = _indices(n, tile)
+    rows = device_rows(720 + world, world, n, "bf16")
+    bad = [r.clone() for r in rows]
+    bad[0][nan] = float("nan")
+    bad[world - 1][inf] = float("inf")
+    planted = np.zeros(n, bool)
+    planted[nan + inf] = True
+    for first in (True, False):
+        accs, sums = [], []
+        for rr in (rows, bad):
+            acc = device_rows(722, 1, n, "f32")[0]
+            s = torch.empty(1, device="cuda", dtype=torch.float64)
+            ws = torch.empty(zs.zs_workspace_bytes(n), device="cuda", dtype=torch.uint8)
+            zs.zs_accumulate_grads(rr, acc, scale=0.25, first=first, sumsq_out=s, workspace=ws)
+            accs.append(host(acc))
+            sums.append(s)
+        torch.cuda.synchronize()
+        c, p = accs
+        cp = _classes(p)
+        assert np.array_equal(np.nonzero(cp)[0], np.nonzero(planted)[0])
+        assert np.all(cp[nan] == 1) and np.all(cp[inf] == 2)
+        assert np.array_equal(c.view(np.uint32)[~planted], p.view(np.uint32)[~planted])
+        assert np.isfinite(sums[0].item()) and np.isnan(sums[1].item())

@@ -143,6 +143,28 @@ def test_reduce_pins_pass_the_oracle_itself():
     assert not _fails(REDUCE_PINS)
 
 
+def _abs_mean_no_division(rows):  # sum of magnitudes, not divided by N
+    return np.abs(reduce.decode_rows(rows).astype(np.float64)).sum(axis=0)
+
+
+def _abs_mean_of_sum(rows):  # |sum c_r| / N in place of sum |c_r| / N
+    c = reduce.decode_rows(rows).astype(np.float64)
+    return np.abs(c.sum(axis=0)) / c.shape[0]
+
+
+ABS_MEAN_PINS = [pins_reduce.test_abs_mean_hand_values, pins_reduce.test_abs_mean_special_cases]
+
+
+@pytest.mark.parametrize("fn", [_abs_mean_no_division, _abs_mean_of_sum])
+def test_abs_mean_pins_catch(monkeypatch, fn):
+    monkeypatch.setattr(reduce, "abs_mean", fn)
+    assert _fails(ABS_MEAN_PINS), fn.__name__
+
+
+def test_abs_mean_pins_pass_the_oracle_itself():
+    assert not _fails(ABS_MEAN_PINS)
+
+
 # ---- layout: flatten, pad, shard
 
 def _shard_shifted(flat, world, rank):  # starts one element late

@@ -145,3 +145,33 @@ def test_bad_rows():
         reduce.decode_rows(np.zeros(4, np.float32))
     with pytest.raises(ValueError):
         reduce.decode_rows(np.zeros((2, 4), np.float64))
+
+
+def test_abs_mean_hand_values():
+    # The reduction's error scale (sum_r |c_r|) / N, worked by hand.
+    # [1, -3]: (1 + 3) / 2 = 2, where |sum| / N would give 1 and sum|c| alone 4.
+    got = reduce.abs_mean(np.array([[1.0], [-3.0]], dtype=np.float32))
+    assert got.dtype == np.float64 and got.tolist() == [2.0]
+    # three ranks, two columns: (1 + 3 + 5) / 3 = 3 and (2 + 4 + 0) / 3 = 2
+    rows = np.array([[1.0, -2.0], [3.0, 4.0], [-5.0, 0.0]], dtype=np.float32)
+    assert reduce.abs_mean(rows).tolist() == [3.0, 2.0]
+    # bf16 patterns: 0x3f80 = 1.0, 0xc040 = -3.0, 0x4000 = 2.0, 0x8000 = -0.0
+    rows16 = np.array([[0x3F80, 0x8000], [0xC040, 0x4000]], dtype=np.uint16)
+    assert reduce.abs_mean(rows16).tolist() == [2.0, 1.0]
+
+
+def test_abs_mean_special_cases():
+    c = gen.host_grad_rows(21, 1, 300, "bf16")
+    mag = np.abs(bf16.from_bf16_bits(c[0]).astype(np.float64))
+    for world in (1, 2, 5, 64):
+        # N identical contributions: the scale is |c| itself, whatever N
+        assert np.array_equal(reduce.abs_mean(np.repeat(c, world, axis=0)), mag)
+    # contributions of one sign: the scale is the magnitude of the exact mean
+    rows = gen.host_grad_rows(22, 6, 300, "f32")
+    pos = np.abs(rows)
+    assert np.array_equal(reduce.abs_mean(pos), pos.astype(np.float64).sum(axis=0) / 6)
+    # flipping the sign of any one rank leaves it unchanged; it bounds |mean|
+    flipped = rows.copy()
+    flipped[2] = -flipped[2]
+    assert np.array_equal(reduce.abs_mean(flipped), reduce.abs_mean(rows))
+    assert np.all(np.abs(reduce.mean_exact(rows).astype(np.float64)) <= reduce.abs_mean(rows) * (1 + 2.0 ** -23))
