@@ -23,6 +23,7 @@ from .api import (  # noqa: F401
     zs_pack_shard,
     zs_pack_shard_dim0,
     zs_reduce_grads,
+    zs_reduce_grads_noalloc,
     zs_sharded_step,
     zs_version,
     zs_workspace_bytes,

@@ -14,6 +14,7 @@ ZS_OK = 0
 ZS_F32 = 0
 ZS_BF16 = 1
 ZS_MAX_WORLD = 256
+ZS_NOALLOC_MAX_N = 1 << 28
 STATUS = {
     0: "ZS_OK", -1: "ZS_ERR_NULL", -2: "ZS_ERR_SIZE", -3: "ZS_ERR_WORLD", -4: "ZS_ERR_RANK",
     -5: "ZS_ERR_DTYPE", -6: "ZS_ERR_HPARAM", -7: "ZS_ERR_SHARD", -8: "ZS_ERR_WORKSPACE",
@@ -45,6 +46,8 @@ SIGNATURES = {
                                   C.c_void_p]),
     "zs_reduce_grads": (C.c_int32, [C.POINTER(C.c_void_p), C.c_int32, C.c_int32, C.c_int64,
                                     C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
+    "zs_reduce_grads_noalloc": (C.c_int32, [C.POINTER(C.c_void_p), C.c_int32, C.c_int32, C.c_int64,
+                                            C.c_void_p, C.c_void_p, C.c_void_p]),
     "zs_workspace_bytes": (C.c_size_t, [C.c_int64]),
     "zs_adamw_step": (C.c_int32, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int64,
                                   C.POINTER(AdamWHParams), C.c_void_p, C.c_void_p, C.c_void_p]),

@@ -251,6 +251,17 @@ def zs_reduce_grads(rows, grad_out, sumsq_out=None, workspace=None, stream=None)
         ws_bytes, _stream(stream, grad_out.device)))
 
 
+def zs_reduce_grads_noalloc(rows, grad_out, sumsq_out=None, stream=None):
+    """zs_reduce_grads without a workspace: the sum of squares uses the
+    library's static scratch (no device allocation by the library)."""
+    _dev(grad_out, "grad_out", torch.float32)
+    arr, world, dt = _rows(rows, grad_out.numel())
+    if sumsq_out is not None:
+        _dev(sumsq_out, "sumsq_out", torch.float64)
+    L.check("zs_reduce_grads_noalloc", _lib().zs_reduce_grads_noalloc(
+        arr, world, dt, grad_out.numel(), _ptr(grad_out), _ptr(sumsq_out), _stream(stream, grad_out.device)))
+
+
 def _state(master, exp_avg, exp_avg_sq):
     _dev(master, "master", torch.float32)
     _dev(exp_avg, "exp_avg", torch.float32)

@@ -200,6 +200,31 @@ zs_status zs_reduce_grads(const void* const* rows, int32_t world, int32_t dtype,
                                       static_cast<double*>(workspace), stream); });
 }
 
+zs_status zs_reduce_grads_noalloc(const void* const* rows, int32_t world, int32_t dtype, int64_t n,
+                                  float* grad_out, double* sumsq_out, hipStream_t stream) {
+  zs_status st = check_rows(rows, world, dtype, n);
+  if (st != ZS_OK) return st;
+  if (n > 0 && !grad_out) return ZS_ERR_NULL;
+  if (grad_out && !aligned(grad_out, 4)) return ZS_ERR_ALIGN;
+  if (sumsq_out) {
+    if (n > ZS_NOALLOC_MAX_N) return ZS_ERR_WORKSPACE;  // beyond the library's scratch
+    if (!aligned(sumsq_out, 8)) return ZS_ERR_ALIGN;
+    st = check_sumsq_buffers(rows, world, dtype, n, grad_out, sumsq_out, nullptr, 0);
+    if (st != ZS_OK) return st;
+  }
+  if (n == 0 && !sumsq_out) return ZS_OK;
+  for (int32_t q = 0; q < world && n > 0; ++q)
+    if (overlaps(grad_out, n * 4, rows[q], n * elem_size(dtype))) return ZS_ERR_OVERLAP;
+  return launch([&] {
+    double* partials = nullptr;
+    if (sumsq_out) {
+      const hipError_t e = zs::static_partials(stream, &partials);
+      if (e != hipSuccess) return e;
+    }
+    return zs::launch_reduce(rows, world, dtype, n, grad_out, sumsq_out, partials, stream);
+  });
+}
+
 zs_status zs_adamw_step(float* master, float* exp_avg, float* exp_avg_sq, const float* grad,
                         int64_t n, const zs_adamw_hparams* hp, const float* grad_scale,
                         uint16_t* bf16_out, hipStream_t stream) {

@@ -21,10 +21,19 @@
 //   * one IEEE division by N (a multiply by the exact reciprocal when N is a
 //     power of two), so the result is independent of the launch shape;
 //   * rows are read with the nontemporal hint (each byte is used once).
+#include <mutex>
+
 #include "zs_device.hpp"
 #include "zs_launch.hpp"
 
 namespace zs {
+
+// Scratch of zs_reduce_grads_noalloc, for callers that cannot allocate: the
+// first-level fp64 partials of the sum of squares (at most one per 256
+// elements, so ZS_NOALLOC_MAX_N / 256 of them) and the finalize's second level.
+// Each device holds its own copy at its own address; host code reaches it only
+// through the address hipGetSymbolAddress returns for that device.
+__device__ __align__(256) double scratch[kStaticPartials + kFinalizeBlocks];
 
 namespace {
 
@@ -221,6 +230,32 @@ hipError_t launch_reduce(const void* const* rows, int world, int dtype, int64_t 
   if (err != hipSuccess) return err;
   if (sumsq) err = launch_sumsq_finalize(partials, grid, sumsq, s);
   return err;
+}
+
+hipError_t static_partials(hipStream_t s, double** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static double* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = s ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {  // once per device, with that device current
+    int cur = 0;
+    if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t back = hipSetDevice(cur);
+      if (e == hipSuccess) e = back;
+    }
+    if (e != hipSuccess) return e;
+    addr[dev] = static_cast<double*>(p);
+  }
+  *out = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_sumsq_finalize(double* partials, int64_t count, double* out, hipStream_t s) {

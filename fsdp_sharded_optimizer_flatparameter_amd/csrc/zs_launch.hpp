@@ -51,6 +51,15 @@ int64_t max_partials(int64_t n);
 // first-level ones in the caller's workspace.
 constexpr int64_t kFinalizeBlocks = 256;
 
+// First-level partials the library's own scratch holds (zs_reduce_grads_noalloc):
+// one per 256 elements of the largest shard it accepts with a sum of squares.
+constexpr int64_t kStaticPartials = ZS_NOALLOC_MAX_N / 256;
+static_assert(ZS_NOALLOC_MAX_N % 256 == 0, "whole tiles");
+
+// Device address of that scratch on the device of stream `s` (the current
+// device for the null stream), looked up once per device; allocates nothing.
+hipError_t static_partials(hipStream_t s, double** out);
+
 // Deterministic fp64 sum of partials[0, count) into *out: one workgroup for a
 // short list, else kFinalizeBlocks workgroups over fixed contiguous ranges
 // (their sums go to partials[count, count + kFinalizeBlocks)) and a second pass.

@@ -203,6 +203,26 @@ zs_status zs_reduce_grads(const void* const* rows, int32_t world, int32_t dtype,
                           float* grad_out, double* sumsq_out, void* workspace,
                           size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * zs_reduce_grads_noalloc -- zs_reduce_grads for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same arguments, results and errors without the
+ * workspace. The sum of squares' partials live in the library's own scratch,
+ * a static device array of ZS_NOALLOC_MAX_N / 256 + 256 doubles (8 MiB + 2 KiB)
+ * that every device the library runs on holds until the process ends. The
+ * call allocates nothing; its first call on a device looks up that device's
+ * copy once.
+ *   n > ZS_NOALLOC_MAX_N with sumsq_out != NULL: ZS_ERR_WORKSPACE (the scratch
+ *   is too small); without a sum of squares any n is accepted.
+ * All calls on one device share its scratch: two calls with a sum of squares
+ * that overlap in time on one device (on different streams, or from different
+ * threads) race and may return a wrong sum of squares. Serialise them. Nothing
+ * in the scratch needs clearing: every call overwrites what it reads.
+ */
+#define ZS_NOALLOC_MAX_N (INT64_C(1) << 28)
+zs_status zs_reduce_grads_noalloc(const void* const* rows, int32_t world, int32_t dtype, int64_t n,
+                                  float* grad_out, double* sumsq_out, hipStream_t stream);
+
 /* Bytes of workspace zs_reduce_grads / zs_accumulate_grads need for a sum of
  * squares over n elements: one fp64 partial per 256-element tile (at most
  * 2^24 - 1 of them) plus 256 second-level partials; 0 for n < 0. The contents

@@ -176,6 +176,26 @@ def test_reduce_argument_errors(lib):
     assert f(_rows(4), 4, 1, 4096, g, s, C.c_void_p(FAKE + 64), wsb, None) == -11
 
 
+def test_reduce_noalloc_argument_errors(lib):
+    f = lib.zs_reduce_grads_noalloc
+    g = C.c_void_p(FAKE + (1 << 40))
+    s = C.c_void_p(FAKE + (1 << 41))
+    assert f(_rows(4), 0, 1, 100, g, None, None) == -3
+    assert f(_rows(4), 4, 7, 100, g, None, None) == -5
+    assert f(_rows(4), 4, 1, -1, g, None, None) == -2
+    assert f(None, 4, 1, 100, g, None, None) == -1
+    assert f(_rows(4), 4, 1, 100, None, None, None) == -1
+    assert f(_rows(4, base=FAKE + 1), 4, 1, 100, g, None, None) == -10
+    assert f(_rows(4), 4, 1, 4096, g, C.c_void_p(FAKE + (1 << 41) + 4), None) == -10
+    # a sum of squares over more elements than the library's scratch covers
+    big = (1 << 28) + 1
+    assert f(_rows(4, stride=1 << 31), 4, 1, big, C.c_void_p(FAKE + (1 << 44)), s, None) == -8
+    # overlaps: output and a contribution; the sum of squares inside the output or a row
+    assert f(_rows(4), 4, 1, 100, C.c_void_p(FAKE + 16), None, None) == -11
+    assert f(_rows(4), 4, 1, 4096, g, C.c_void_p(FAKE + (1 << 40) + 8), None) == -11
+    assert f(_rows(4), 4, 1, 4096, g, C.c_void_p(FAKE + (1 << 30) + 8), None) == -11
+
+
 def test_adamw_argument_errors(lib):
     f = lib.zs_adamw_step
     a, b, c, g = (C.c_void_p(FAKE + i * (1 << 32)) for i in range(4))
