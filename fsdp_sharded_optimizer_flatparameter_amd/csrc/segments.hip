@@ -87,6 +87,8 @@ __device__ void seg_to_f32(const Src* __restrict__ src, float* __restrict__ dst,
 // source vectors sa[k] and sa[k + 1]. Each lane loads its own sa[k] and gets
 // sa[k + 1] from the next lane by a wave shuffle (the last active lane of a
 // wave loads it itself), then funnel-shifts the pair into one aligned store.
+// Each lane keeps 4 source vectors in flight: with one at a time the realigning
+// copy was bound by load latency.
 // The caller keeps every loaded vector inside the copied range: k_begin >= 1
 // and k_end <= nv - 1 for nv destination vectors, so sa[k_begin] starts after
 // the range's first element and sa[k_end] ends before its last.
@@ -95,24 +97,32 @@ __device__ void realign_bf16(const u32x4* __restrict__ sa, u32x4* __restrict__ d
                              int64_t k_end) {
   constexpr int q = SH / 2;          // whole 32-bit words to skip
   constexpr bool half = (SH & 1) != 0;  // plus one bf16
+  constexpr int U = 4;               // source vectors in flight per lane
   const int lane = threadIdx.x & 63;
-  for (int64_t kb = k_begin; kb < k_end; kb += kThreads) {  // uniform across the workgroup
-    const int64_t k = kb + threadIdx.x;
-    const bool act = k < k_end;
-    const u32x4 lo = act ? ld_nt(sa + k) : u32x4{0u, 0u, 0u, 0u};
-    u32x4 hi;
-    hi.x = __shfl_down(lo.x, 1, 64);
-    hi.y = __shfl_down(lo.y, 1, 64);
-    hi.z = __shfl_down(lo.z, 1, 64);
-    hi.w = __shfl_down(lo.w, 1, 64);
-    if (!act) continue;
-    if (lane == 63 || k + 1 >= k_end) hi = ld_nt(sa + k + 1);
-    const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-    u32x4 o;
+  for (int64_t kb = k_begin; kb < k_end; kb += U * kThreads) {  // uniform across the workgroup
+    u32x4 lo[U];
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
-      o[t] = half ? (w[q + t] >> 16) | (w[q + t + 1] << 16) : w[q + t];
-    st_nt(o, da + k);
+    for (int j = 0; j < U; ++j) {
+      const int64_t k = kb + (int64_t)j * kThreads + threadIdx.x;
+      lo[j] = k < k_end ? ld_nt(sa + k) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const int64_t k = kb + (int64_t)j * kThreads + threadIdx.x;
+      u32x4 hi;  // sa[k + 1]: the next lane's vector of the same round
+      hi.x = __shfl_down(lo[j].x, 1, 64);
+      hi.y = __shfl_down(lo[j].y, 1, 64);
+      hi.z = __shfl_down(lo[j].z, 1, 64);
+      hi.w = __shfl_down(lo[j].w, 1, 64);
+      if (k >= k_end) continue;
+      if (lane == 63 || k + 1 >= k_end) hi = ld_nt(sa + k + 1);
+      const uint32_t w[8] = {lo[j].x, lo[j].y, lo[j].z, lo[j].w, hi.x, hi.y, hi.z, hi.w};
+      u32x4 o;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        o[t] = half ? (w[q + t] >> 16) | (w[q + t + 1] << 16) : w[q + t];
+      st_nt(o, da + k);
+    }
   }
 }
 

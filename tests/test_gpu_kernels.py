@@ -226,6 +226,25 @@ def test_cast_matches_oracle_including_special_values():
         assert np.array_equal(host(out), obf16.to_bf16_bits(pats.view(np.float32)))
 
 
+def test_cast_at_every_offset_in_a_cache_line():
+    # the standalone cast starts its vector part at the output's first 128-byte
+    # boundary when the output is 8-byte aligned; every start offset within a
+    # line (64 bf16 elements), lengths shorter and longer than that shift, and
+    # the guard elements around the slot left untouched
+    src = device_rows(640, 1, 100_003 + 64, "f32")[0]
+    nan16 = torch.tensor(float("nan"), dtype=torch.bfloat16).view(torch.int16).item() & 0xFFFF
+    for off in range(64):
+        for n in (1, 3, 4, 5, 31, 64, 65, 1000, 100_003):
+            x = src[:n]
+            buf = torch.full((n + 64 + 16,), float("nan"), device="cuda", dtype=torch.bfloat16)
+            out = buf[8 + off:8 + off + n]
+            zs.zs_cast_for_gather(x, out)
+            torch.cuda.synchronize()
+            assert np.array_equal(host(out), obf16.to_bf16_bits(host(x))), (off, n)
+            b = host(buf)
+            assert np.all(b[:8 + off] == nan16) and np.all(b[8 + off + n:] == nan16), (off, n)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("world", [1, 3, 4, 8, 64])
 def test_fused_step_is_bitwise_the_two_call_path(dtype, world):
