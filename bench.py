@@ -15,8 +15,10 @@ cold start run 3-6% slower than the steady state, whatever W is). The JSON
 line reports the settle steps; the timed region is exactly K steps.
 
 The 70B shard (fp32 contributions, 64 x 4.4 GB of rows) does not fit in HBM
-whole: it is updated in 8 equal chunks, one launch each, with one chunk's worth
-of rows (35 GB) serving every chunk; a step is the 8 launches.
+whole: it is updated in 8 chunks of 137,800,448 elements (the last one 1,680
+shorter: chunk boundaries on 256-element multiples, so that every launch's
+fp32 state starts on a 128-byte line), one launch each, with one chunk's
+worth of rows (35 GB) serving every chunk; a step is the 8 launches.
 
 Also measured (in "parts"): the same update as two launches (reduce, then AdamW
 with the fused cast), each kernel alone, the clipped update (reduce with its sum
@@ -311,6 +313,11 @@ def make_shard(name: str, dev):
     hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=wl["wd"])
     row_dtype = torch.float32 if wl.get("rows") == "f32" else torch.bfloat16
     csize = -(-S // wl.get("chunks", 1))
+    if wl.get("chunks", 1) > 1:
+        # chunk boundaries on 1 KiB of fp32 state (256 elements), so that every
+        # launch's theta, m and v start on the 128-byte line grid; the last chunk
+        # is the shorter one
+        csize = -(-csize // 256) * 256
     ranges = [(a, min(S, a + csize)) for a in range(0, S, csize)]
     g0 = gen.device_generator(1000 + sorted(WORKLOADS).index(name), dev)
     rows = [gen.device_normal(g0, csize, gen.GRAD_SIGMA, row_dtype, dev) for _ in range(world)]

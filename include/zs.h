@@ -181,6 +181,9 @@ zs_status zs_pack_shard(const zs_param_desc* d_desc, int32_t nparams, int64_t to
  *   rows[world]   HOST array of `world` DEVICE pointers; rows[q] points at
  *                 contribution q for this slice, n elements of `dtype`
  *                 (ZS_BF16 or ZS_F32); unused (may be NULL) when n == 0.
+ *                 The pointers travel by value in the kernel arguments, so a
+ *                 launch captured into a HIP graph keeps them: a replay reads
+ *                 the same row buffers.
  *                 Rows that start on 128-byte boundaries stream fastest: the
  *                 N rows of one [N, n] receive buffer whose row pitch is not a
  *                 multiple of 64 bytes start off the cache-line grid, and each
@@ -247,7 +250,11 @@ size_t zs_workspace_bytes(int64_t n);
  *   bf16_out[n]   optional DEVICE bf16 output (NULL = skip): bf16(theta'),
  *                 typically the rank's slot of the all-gather buffer
  * No two of master, exp_avg, exp_avg_sq, grad and bf16_out may share bytes, and
- * grad_scale may not overlap an output (ZS_ERR_OVERLAP).
+ * grad_scale may not overlap an output (ZS_ERR_OVERLAP). Arrays that start on
+ * 128-byte boundaries stream fastest: a wave's 1 KiB access to an array that
+ * starts elsewhere straddles a partial cache line at each end, and a
+ * partial-line write costs HBM a read-modify-write (a shard split into chunks
+ * should split on multiples of 32 elements).
  * Errors: ZS_ERR_NULL, ZS_ERR_SIZE, ZS_ERR_HPARAM (non-finite values, lr, eps
  * or wd < 0, betas outside [0, 1), step < 1), ZS_ERR_ALIGN, ZS_ERR_OVERLAP,
  * ZS_ERR_HIP.

@@ -173,14 +173,18 @@ def test_70b_fp32_contributions_chunk():
 
 
 def test_70b_fp32_contributions_bench_chunk():
-    # one of the eight equal chunks the 70B shard is updated in (1,102,401,664 / 8
-    # = 137,800,208 elements; 64 fp32 rows of it are 35.3 GB)
+    # the chunks the 70B shard is updated in: 1,102,401,664 / 8 rounded up to a
+    # multiple of 256 elements (every chunk's state on the 128-byte line grid) is
+    # 137,800,448, and the last chunk is 137,798,528; 64 fp32 rows of a chunk are
+    # 35.3 GB
     lay = olayout.flat_layout(shapes.numels(shapes.llama_70b()), 64)
-    chunk = -(-lay.shard // 8)
-    assert chunk == 137_800_208
-    _full_size_case(chunk, 64, "f32", step=4, moments=True, slot_offset=0, seed=7100,
-                    windows=16, width=65536)
-    torch.cuda.empty_cache()
+    chunk = -(-(-(-lay.shard // 8)) // 256) * 256
+    last = lay.shard - 7 * chunk
+    assert (chunk, last) == (137_800_448, 137_798_528)
+    for i, n in enumerate((chunk, last)):
+        _full_size_case(n, 64, "f32", step=4, moments=True, slot_offset=0, seed=7100 + i,
+                        windows=8, width=65536)
+        torch.cuda.empty_cache()
 
 
 def test_full_size_accumulation_7p5b_n64():
