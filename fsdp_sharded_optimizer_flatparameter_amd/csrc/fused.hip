@@ -24,7 +24,11 @@ namespace {
 // Keeping the row streams and the state read-modify-write apart in time, and
 // the LDS reservation (which caps the workgroups resident per CU), keeps fewer
 // DRAM pages open at once; both were measured to raise HBM throughput.
-template <int NW, int CAP, int G, int C, int BS, typename In, bool CAST, bool SCALE>
+// RM selects the rank-major walk (rank_sums_rank_major: each chunk of C ranks
+// is added into all G groups before the next chunk is read, so every row is
+// read as one long run per chunk), otherwise the group-major one
+// (rank_sums_streamed).
+template <int NW, int CAP, int G, int C, int BS, typename In, bool CAST, bool SCALE, bool RM>
 __global__ __launch_bounds__(BS) void k_fused(RowTable<CAP> rows, int world, MeanDiv div,
                                                     int64_t ngroups, int64_t n,
                                                     float* __restrict__ th, float* __restrict__ m,
@@ -38,12 +42,14 @@ __global__ __launch_bounds__(BS) void k_fused(RowTable<CAP> rows, int world, Mea
   const int64_t span = (int64_t)BS * G;
 
   for (int64_t base = (int64_t)blockIdx.x * span; base < ngroups; base += (int64_t)gridDim.x * span) {
-    rank_sums_streamed<In, C, G, CAP, BS>(rows, nw, base, ngroups, [&](int k, const float* acc) {
+    auto sink = [&](int k, const float* acc) {
       f32x4 gv;
 #pragma unroll
       for (int e = 0; e < 4; ++e) gv[e] = SCALE ? div(acc[e]) * sc : div(acc[e]);
       gl[k * BS + threadIdx.x] = gv;
-    });
+    };
+    if constexpr (RM) rank_sums_rank_major<In, C, G, CAP, BS>(rows, nw, base, ngroups, gl, sink);
+    else rank_sums_streamed<In, C, G, CAP, BS>(rows, nw, base, ngroups, sink);
     // phase 2: with bf16 contributions double-buffered (group k+1's state loads
     // are in flight while group k is updated and stored)
     auto qidx = [&](int k) { return base + (int64_t)k * BS + threadIdx.x; };
@@ -70,9 +76,10 @@ __global__ __launch_bounds__(BS) void k_fused(RowTable<CAP> rows, int world, Mea
       st_nt(W, reinterpret_cast<f32x4*>(v) + qq);
       if (CAST) store_bf16x4(out, qq, T, om);
     };
-    if constexpr (sizeof(In) == 4) {
-      // fp32 contributions: all G groups' state loads are issued before the
-      // first update (measured 2% faster than two in flight at N=64)
+    if constexpr (sizeof(In) == 4 && !RM) {
+      // fp32 contributions, group-major walk: all G groups' state loads are
+      // issued before the first update (measured 2% faster than two in flight
+      // at N=64)
       f32x4 T[G], M[G], W[G];
 #pragma unroll
       for (int k = 0; k < G; ++k) load(k, T[k], M[k], W[k]);
@@ -135,31 +142,44 @@ __global__ __launch_bounds__(kThreads) void k_fused_scalar(RowTable<ZS_MAX_WORLD
 
 
 struct Shape {
-  int bs;      // workgroup size: 256 (4 waves) or 64 (one wave)
+  int bs;      // workgroup size: 512 or 256 (8 or 4 waves), or 64 (one wave)
   int g;       // groups per lane staged in LDS
   size_t lds;  // dynamic LDS bytes per workgroup (>= g * bs * 16)
+  bool rm;     // rank-major walk
 };
 
-// Measured on MI355X. With many contributions the row walk dominates: 4-wave
-// workgroups with deep staging (16 groups in 64 KiB, 2 workgroups per CU) are
-// best. With few contributions the state read-modify-write dominates:
-// one-wave workgroups of a single group each, with a 16 KiB reservation (10
-// waves per CU), ran the Llama-3-8B shard at N=8 11% faster than 4-wave
-// workgroups (which were best with 2 groups and 64 KiB); residency matters
-// sharply there (5 waves per CU ran 35% slower, 20 waves 8% slower).
-Shape fused_shape(int world) {
+// Ranks per chunk of the rank-major walk: about 2 KiB of row loads per lane
+// group in flight, double-buffered (4 bf16 or 2 fp32 rows).
+template <typename In>
+constexpr int rm_chunk() { return sizeof(In) == 2 ? 4 : 2; }
+
+// Measured on MI355X. With many contributions the row walk dominates: 8-wave
+// workgroups walking the ranks rank-major over 16 staged groups (128 KiB of
+// LDS, one workgroup per CU) read every row in 64 KiB runs and ran the 7.5B
+// shard at N=64 3.5% faster, and the 70B chunk with fp32 rows 10% faster, than
+// 4-wave workgroups walking group-major over 16 groups (64 KiB, two per CU),
+// which remain for world sizes the chunk width does not divide. With few
+// contributions the state read-modify-write dominates: one-wave workgroups
+// of a single group each, with a 16 KiB reservation (10 waves per CU), ran
+// the Llama-3-8B shard at N=8 11% faster than 4-wave workgroups (which were
+// best with 2 groups and 64 KiB); residency matters sharply there (5 waves
+// per CU ran 35% slower, 20 waves 8% slower).
+Shape fused_shape(int world, int chunk) {
   Shape sh;
   const bool many = world >= 16;
-  sh.bs = tuning().fused_bs > 0 ? tuning().fused_bs : (many ? 256 : 64);
+  sh.bs = tuning().fused_bs > 0 ? tuning().fused_bs : (many ? 512 : 64);
+  if (sh.bs == 512 && world % chunk != 0) sh.bs = 256;  // the rank-major walk takes whole chunks
+  sh.rm = sh.bs == 512;
   sh.g = tuning().fused_g > 0 ? tuning().fused_g : (many ? 16 : 1);
   if (sh.bs == 64 && sh.g > 4) sh.g = 4;  // one-wave workgroups are built for 1, 2 or 4 groups
+  if (sh.rm) sh.g = 16;                     // the rank-major shape is built for 16 groups
   const size_t need = (size_t)sh.g * sh.bs * 16;
   sh.lds = tuning().fused_lds > 0 ? (size_t)tuning().fused_lds : (sh.bs == 64 ? 16384 : 65536);
   if (sh.lds < need) sh.lds = need;
   return sh;
 }
 
-template <int NW, int CAP, int G, int C, int BS, typename In>
+template <int NW, int CAP, int G, int C, int BS, typename In, bool RM = false>
 void run_fused(const void* const* rows, int world, int64_t n, float* th, float* m, float* v,
                const AdamConsts& c, const float* scale, uint16_t* out, size_t lds, hipStream_t s) {
   RowTable<CAP> t;
@@ -169,13 +189,13 @@ void run_fused(const void* const* rows, int world, int64_t n, float* th, float* 
   const MeanDiv d = mean_div(world);
   const int om = out ? bf16_out_mode(out) : 0;
   if (out && scale)
-    hipLaunchKernelGGL((k_fused<NW, CAP, G, C, BS, In, true, true>), gd, bd, lds, s, t, world, d, ngroups, n, th, m, v, c, scale, out, om);
+    hipLaunchKernelGGL((k_fused<NW, CAP, G, C, BS, In, true, true, RM>), gd, bd, lds, s, t, world, d, ngroups, n, th, m, v, c, scale, out, om);
   else if (out)
-    hipLaunchKernelGGL((k_fused<NW, CAP, G, C, BS, In, true, false>), gd, bd, lds, s, t, world, d, ngroups, n, th, m, v, c, scale, out, om);
+    hipLaunchKernelGGL((k_fused<NW, CAP, G, C, BS, In, true, false, RM>), gd, bd, lds, s, t, world, d, ngroups, n, th, m, v, c, scale, out, om);
   else if (scale)
-    hipLaunchKernelGGL((k_fused<NW, CAP, G, C, BS, In, false, true>), gd, bd, lds, s, t, world, d, ngroups, n, th, m, v, c, scale, out, om);
+    hipLaunchKernelGGL((k_fused<NW, CAP, G, C, BS, In, false, true, RM>), gd, bd, lds, s, t, world, d, ngroups, n, th, m, v, c, scale, out, om);
   else
-    hipLaunchKernelGGL((k_fused<NW, CAP, G, C, BS, In, false, false>), gd, bd, lds, s, t, world, d, ngroups, n, th, m, v, c, scale, out, om);
+    hipLaunchKernelGGL((k_fused<NW, CAP, G, C, BS, In, false, false, RM>), gd, bd, lds, s, t, world, d, ngroups, n, th, m, v, c, scale, out, om);
 }
 
 template <typename In, int G, int C, int BS>
@@ -215,10 +235,25 @@ void dispatch_g(const Shape& sh, const void* const* rows, int world, int64_t n, 
 }
 
 template <typename In>
+void dispatch_world_rm(const void* const* rows, int world, int64_t n, float* th, float* m, float* v,
+                       const AdamConsts& c, const float* scale, uint16_t* out, size_t lds, hipStream_t s) {
+  constexpr int C = rm_chunk<In>();
+  switch (world) {
+    case 16: run_fused<16, 16, 16, C, 512, In, true>(rows, world, n, th, m, v, c, scale, out, lds, s); break;
+    case 32: run_fused<32, 32, 16, C, 512, In, true>(rows, world, n, th, m, v, c, scale, out, lds, s); break;
+    case 64: run_fused<64, 64, 16, C, 512, In, true>(rows, world, n, th, m, v, c, scale, out, lds, s); break;
+    default:
+      if (world <= 64) run_fused<0, 64, 16, C, 512, In, true>(rows, world, n, th, m, v, c, scale, out, lds, s);
+      else run_fused<0, ZS_MAX_WORLD, 16, C, 512, In, true>(rows, world, n, th, m, v, c, scale, out, lds, s);
+  }
+}
+
+template <typename In>
 void dispatch(const void* const* rows, int world, int64_t n, float* th, float* m, float* v,
               const AdamConsts& c, const float* scale, uint16_t* out, hipStream_t s) {
-  const Shape sh = fused_shape(world);
-  if (tuning().rank_chunk == 4) dispatch_g<In, 4>(sh, rows, world, n, th, m, v, c, scale, out, s);
+  const Shape sh = fused_shape(world, rm_chunk<In>());
+  if (sh.rm) dispatch_world_rm<In>(rows, world, n, th, m, v, c, scale, out, sh.lds, s);
+  else if (tuning().rank_chunk == 4) dispatch_g<In, 4>(sh, rows, world, n, th, m, v, c, scale, out, s);
   else dispatch_g<In, 8>(sh, rows, world, n, th, m, v, c, scale, out, s);
 }
 

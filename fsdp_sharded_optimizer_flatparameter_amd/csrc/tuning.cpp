@@ -26,9 +26,9 @@ const Tuning& tuning() {
     x.fused_g = (e = env("ZS_FUSED_G")) ? std::atoi(e) : 0;
     if (x.fused_g != 1 && x.fused_g != 2 && x.fused_g != 4 && x.fused_g != 8 && x.fused_g != 16) x.fused_g = 0;
     x.fused_lds = (e = env("ZS_FUSED_LDS")) ? std::atoll(e) : 0;
-    if (x.fused_lds < 0 || x.fused_lds > 65536) x.fused_lds = 0;
+    if (x.fused_lds < 0 || x.fused_lds > 163840) x.fused_lds = 0;
     x.fused_bs = (e = env("ZS_FUSED_BS")) ? std::atoi(e) : 0;
-    if (x.fused_bs != 64 && x.fused_bs != 256) x.fused_bs = 0;
+    if (x.fused_bs != 64 && x.fused_bs != 256 && x.fused_bs != 512) x.fused_bs = 0;
     x.accum_shape = (e = env("ZS_ACCUM_SHAPE")) ? std::atoi(e) : 0;
     if (x.accum_shape != 1) x.accum_shape = 0;
     x.reduce_g = (e = env("ZS_REDUCE_G")) ? std::atoi(e) : 0;

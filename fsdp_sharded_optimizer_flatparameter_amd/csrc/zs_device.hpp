@@ -183,6 +183,54 @@ __device__ __forceinline__ void rank_sums_streamed(const RowTable<CAP>& rows, in
   }
 }
 
+// Rank sums of G groups per lane in rank-major order: the C ranks of one chunk
+// are added into all G groups' running sums before the next chunk is read, so
+// a workgroup reads each row as one contiguous run of G*BS*4 elements per
+// chunk (64 KiB of bf16 rows for G = 16, BS = 512) instead of G separate runs
+// of BS*4. The running sums live in `sums` (LDS, G*BS vectors; each lane
+// touches only its own entries, so no barrier is involved), initialised to
+// -0.0 here; each element still adds c_0, c_1, ..., c_{N-1} in that order in
+// fp32, so the result is bit-identical to rank_sums_streamed. The loads of
+// step i+1 (C rows of one group) are in flight while step i is added.
+// nw must be a multiple of C. sink(k, acc) receives group k's finished sums
+// after the last chunk.
+template <typename In, int C, int G, int CAP, int BS, typename Sink>
+__device__ __forceinline__ void rank_sums_rank_major(const RowTable<CAP>& rows, int nw, int64_t base,
+                                                     int64_t ngroups, f32x4* sums, Sink&& sink) {
+  using L = Lanes<In>;
+  using Vec = typename L::Vec;
+  const int nch = nw / C;
+  const int total = nch * G;
+#pragma unroll
+  for (int k = 0; k < G; ++k) sums[k * BS + threadIdx.x] = f32x4{-0.0f, -0.0f, -0.0f, -0.0f};
+  auto load = [&](int idx, Vec* buf) {
+    const int c = idx / G, k = idx - c * G;
+    const int64_t qq = base + (int64_t)k * BS + threadIdx.x;
+    const int64_t q = qq < ngroups ? qq : ngroups - 1;  // clamped: loads stay in bounds
+#pragma unroll
+    for (int u = 0; u < C; ++u) buf[u] = ld_nt(static_cast<const Vec*>(rows.p[c * C + u]) + q);
+  };
+  auto consume = [&](int idx, const Vec* buf) {
+    const int c = idx / G, k = idx - c * G;
+    const f32x4 s = sums[k * BS + threadIdx.x];
+    float acc[4] = {s[0], s[1], s[2], s[3]};
+#pragma unroll
+    for (int u = 0; u < C; ++u) L::add(buf[u], acc);
+    if (c + 1 == nch) sink(k, acc);
+    else sums[k * BS + threadIdx.x] = f32x4{acc[0], acc[1], acc[2], acc[3]};
+  };
+  Vec a[C], b[C];
+  load(0, a);
+#pragma unroll 1
+  for (int idx = 0; idx < total; idx += 2) {
+    if (idx + 1 < total) load(idx + 1, b);
+    consume(idx, a);
+    if (idx + 1 >= total) break;
+    if (idx + 2 < total) load(idx + 2, a);
+    consume(idx + 1, b);
+  }
+}
+
 // Division of the rank sum by N. For N a power of two the product with the
 // exact reciprocal is the same correctly rounded value, so both branches give
 // the IEEE quotient.

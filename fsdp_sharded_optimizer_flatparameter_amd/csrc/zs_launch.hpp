@@ -21,7 +21,8 @@ struct Tuning {
   int rank_chunk;  // ranks per load chunk of the double-buffered rank walk (4 or 8)
   int fused_g;     // groups per lane staged in LDS by the single-pass kernel (0 = by world size)
   int64_t fused_lds;  // LDS bytes reserved per workgroup of the single-pass kernel (0 = default)
-  int fused_bs;    // workgroup size of the single-pass kernel (64 or 256; 0 = by world size)
+  int fused_bs;    // workgroup size of the single-pass kernel (64, 256, or 512 = the
+                   // rank-major shape; 0 = by world size)
   int accum_shape;  // ZeRO-2 accumulation with few contributions: 0 one-wave, 1 four-wave
   int reduce_g;    // groups per lane staged in LDS by the reduce kernel (0 = by world size)
   int64_t grid_cap;  // upper bound on workgroups of the streaming kernels

@@ -245,10 +245,14 @@ def test_cast_at_every_offset_in_a_cache_line():
             assert np.all(b[:8 + off] == nan16) and np.all(b[8 + off + n:] == nan16), (off, n)
 
 
+# world sizes: the one-wave shape (< 16), the rank-major 8-wave shape (16, 32,
+# 64, 100 and 30 with fp32 rows), and the group-major 4-wave shape that takes
+# over when the rank-major chunk does not divide N (30 and 33 with bf16 rows,
+# 33 with fp32 rows); sizes span several tiles of each and a ragged tail
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("world", [1, 3, 4, 8, 64])
+@pytest.mark.parametrize("world", [1, 3, 4, 8, 16, 30, 32, 33, 64, 100])
 def test_fused_step_is_bitwise_the_two_call_path(dtype, world):
-    for i, n in enumerate([5, 4096 + 3, 262144 + 7]):
+    for i, n in enumerate([5, 4096 + 3, 262144 + 7, 3 * 131072 + 4096 + 3]):
         rows = device_rows(500 + world + i, world, n, dtype)
         a = device_state(600 + i, n)
         b = tuple(t.clone() for t in a)

@@ -79,13 +79,19 @@ def _state_copies(n, seed):
     return (th, m, v), tuple(t.clone() for t in (th, m, v))
 
 
-# (world, n, tile of the launch shape that world selects: 4-wave workgroups of 16
-# staged groups with many contributions, one-wave single-group ones with few)
+# (world, n, tile of the launch shape that world selects). The single pass with
+# many contributions walks 16 staged groups per lane in 8-wave workgroups
+# (32,768 elements per tile), or in 4-wave ones when the rank-major chunk does
+# not divide N (33); the reduce and accumulation kernels take 4-wave workgroups
+# of 16 groups (16,384); with few contributions all take one-wave, single-group
+# workgroups (256).
+STEP_SHAPES = [(64, 3 * 32768 + 4096 + 3, 32768), (33, 3 * 16384 + 4096 + 3, 16384),
+               (8, 70001, 256), (3, 9 * 256 + 2, 256)]
 SHAPES = [(64, 3 * 16384 + 4096 + 3, 16384), (8, 70001, 256), (3, 9 * 256 + 2, 256)]
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("world,n,tile", SHAPES)
+@pytest.mark.parametrize("world,n,tile", STEP_SHAPES)
 def test_sharded_step_nonfinite_reach_exactly_their_elements(dtype, world, n, tile):
     nan, inf = _indices(n, tile)
     rows = device_rows(700 + world, world, n, dtype)
