@@ -23,8 +23,12 @@ namespace {
 // slots, the rank walk adds each group's scaled mean into its slot, and the G
 // results are written back as one burst of 16-byte stores. The row walk then
 // runs without a write stream beside it, and the LDS reservation caps the
-// workgroups resident per CU.
-template <int NW, int CAP, int G, int BS, typename In, bool SUMSQ, bool FIRST, bool SCALE>
+// workgroups resident per CU. With RM the ranks are walked rank-major
+// (rank_sums_rank_major), the slots holding the running sums and then the
+// scaled means; the previous sums are read after the walk, two groups in
+// flight, as the single pass reads its state.
+template <int NW, int CAP, int G, int BS, typename In, bool SUMSQ, bool FIRST, bool SCALE,
+          bool RM = false>
 __global__ __launch_bounds__(BS) void k_accum(RowTable<CAP> rows, int world, MeanDiv div,
                                                     float scale, int64_t ngroups, int64_t n,
                                                     float* __restrict__ acc,
@@ -35,6 +39,50 @@ __global__ __launch_bounds__(BS) void k_accum(RowTable<CAP> rows, int world, Mea
   const int64_t span = (int64_t)BS * G;
   double ss = 0.0;
   for (int64_t base = (int64_t)blockIdx.x * span; base < ngroups; base += (int64_t)gridDim.x * span) {
+    if constexpr (RM) {
+      constexpr int C = sizeof(In) == 2 ? 4 : 2;
+      rank_sums_rank_major<In, C, G, CAP, BS>(rows, nw, base, ngroups, slot, [&](int k, const float* s) {
+        f32x4 u;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          u[e] = div(s[e]);
+          if (SCALE) u[e] *= scale;
+        }
+        slot[k * BS + threadIdx.x] = u;
+      });
+      auto qidx = [&](int k) { return base + (int64_t)k * BS + threadIdx.x; };
+      auto finish = [&](int k, const f32x4& prev) {
+        const int64_t qq = qidx(k);
+        if (qq >= ngroups) return;
+        const f32x4 u = slot[k * BS + threadIdx.x];
+        f32x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          o[e] = FIRST ? u[e] : prev[e] + u[e];
+          if (SUMSQ) ss = fma((double)o[e], (double)o[e], ss);
+        }
+        st_nt(o, reinterpret_cast<f32x4*>(acc) + qq);
+      };
+      auto prev_of = [&](int k) {
+        const int64_t q = qidx(k) < ngroups ? qidx(k) : ngroups - 1;
+        return ld_nt(reinterpret_cast<const f32x4*>(acc) + q);
+      };
+      if (FIRST) {
+#pragma unroll
+        for (int k = 0; k < G; ++k) finish(k, f32x4{0.f, 0.f, 0.f, 0.f});
+      } else {
+        f32x4 p0 = prev_of(0), p1;
+#pragma unroll 1
+        for (int k = 0; k < G; k += 2) {
+          if (k + 1 < G) p1 = prev_of(k + 1);
+          finish(k, p0);
+          if (k + 1 >= G) break;
+          if (k + 2 < G) p0 = prev_of(k + 2);
+          finish(k + 1, p1);
+        }
+      }
+      continue;
+    }
     if (!FIRST) {
 #pragma unroll
       for (int k = 0; k < G; ++k) {
@@ -147,11 +195,13 @@ __global__ void k_clip(const double* __restrict__ partials, int count, double ma
 }
 
 
-// Measured on MI355X: with many contributions 16 groups per lane in 4-wave
-// workgroups (64 KiB of LDS, two workgroups per CU), as for the reduce; with
-// few, the shape of the single pass (ZS_ACCUM_SHAPE=1 selects the earlier
-// 4 groups per lane in 4-wave workgroups for comparison).
-template <int G, int BS, int NW, int CAP, typename In, bool SUMSQ, bool FIRST, bool SCALE>
+// Measured on MI355X: with many contributions the rank-major shape of the
+// single pass (16 groups per lane in 8-wave workgroups, 128 KiB of LDS), or
+// 16 groups in 4-wave workgroups (64 KiB, two per CU) where its chunk does not
+// divide the world size; with few, the shape of the single pass.
+// ZS_ACCUM_SHAPE=1 selects the earlier shapes for comparison (4-wave
+// workgroups of 16 groups with many contributions, of 4 with few).
+template <int G, int BS, int NW, int CAP, typename In, bool SUMSQ, bool FIRST, bool SCALE, bool RM = false>
 void launch_accum_shape(const RowTable<CAP>& t, int world, int64_t n, float* acc, float scale,
                         double* partials, int64_t* grid_out, size_t lds, hipStream_t s) {
   const int64_t ngroups = n / 4;
@@ -159,7 +209,7 @@ void launch_accum_shape(const RowTable<CAP>& t, int world, int64_t n, float* acc
   if (SUMSQ && grid > max_partials(n)) grid = max_partials(n);
   *grid_out = grid;
   if (lds < (size_t)G * BS * sizeof(f32x4)) lds = (size_t)G * BS * sizeof(f32x4);
-  hipLaunchKernelGGL((k_accum<NW, CAP, G, BS, In, SUMSQ, FIRST, SCALE>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((k_accum<NW, CAP, G, BS, In, SUMSQ, FIRST, SCALE, RM>), dim3((unsigned)grid),
                      dim3(BS), lds, s, t, world, mean_div(world), scale, ngroups, n, acc, partials);
 }
 
@@ -168,7 +218,10 @@ void run_accum(const void* const* rows, int world, int64_t n, float* acc, float 
                double* partials, int64_t* grid_out, hipStream_t s) {
   RowTable<CAP> t;
   for (int i = 0; i < CAP; ++i) t.p[i] = i < world ? rows[i] : nullptr;
-  if (world >= 16)
+  constexpr int rm_c = sizeof(In) == 2 ? 4 : 2;
+  if (world >= 16 && world % rm_c == 0 && tuning().accum_shape == 0)
+    launch_accum_shape<16, 512, NW, CAP, In, SUMSQ, FIRST, SCALE, true>(t, world, n, acc, scale, partials, grid_out, 0, s);
+  else if (world >= 16)
     launch_accum_shape<16, 256, NW, CAP, In, SUMSQ, FIRST, SCALE>(t, world, n, acc, scale, partials, grid_out, 0, s);
   else if (tuning().accum_shape == 1)
     launch_accum_shape<4, 256, NW, CAP, In, SUMSQ, FIRST, SCALE>(t, world, n, acc, scale, partials, grid_out, 0, s);

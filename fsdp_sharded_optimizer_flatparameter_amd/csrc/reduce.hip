@@ -41,7 +41,9 @@ namespace {
 // LDS during the rank walk and written out afterwards as one burst of
 // nontemporal 16-byte stores (the LDS reservation also caps the workgroups
 // resident per CU); with G == 1 each group is stored as soon as it is summed.
-template <int NW, int CAP, int G, int C, int BS, typename In, bool SUMSQ>
+// RM walks the ranks rank-major (rank_sums_rank_major), its running sums in
+// the same LDS slots.
+template <int NW, int CAP, int G, int C, int BS, typename In, bool SUMSQ, bool RM = false>
 __global__ __launch_bounds__(BS) void k_reduce(RowTable<CAP> rows, int world, MeanDiv div,
                                                      int64_t ngroups, int64_t n,
                                                      float* __restrict__ g,
@@ -53,7 +55,7 @@ __global__ __launch_bounds__(BS) void k_reduce(RowTable<CAP> rows, int world, Me
   double ss = 0.0;
 
   for (int64_t base = (int64_t)blockIdx.x * span; base < ngroups; base += (int64_t)gridDim.x * span) {
-    rank_sums_streamed<In, C, G, CAP, BS>(rows, nw, base, ngroups, [&](int k, const float* acc) {
+    auto sink = [&](int k, const float* acc) {
       const int64_t qq = base + (int64_t)k * BS + threadIdx.x;
       f32x4 o;
 #pragma unroll
@@ -66,7 +68,9 @@ __global__ __launch_bounds__(BS) void k_reduce(RowTable<CAP> rows, int world, Me
       } else {
         gl[k * BS + threadIdx.x] = o;
       }
-    });
+    };
+    if constexpr (RM) rank_sums_rank_major<In, C, G, CAP, BS>(rows, nw, base, ngroups, gl, sink);
+    else rank_sums_streamed<In, C, G, CAP, BS>(rows, nw, base, ngroups, sink);
     if (G > 1) {
       for (int k = 0; k < G; ++k) {  // each lane writes back only its own entries
         const int64_t qq = base + k * BS + threadIdx.x;
@@ -138,10 +142,10 @@ __global__ __launch_bounds__(kThreads) void k_sumsq_finalize(const double* __res
 // without the sum of squares), where 10 or 20 per CU gained less.
 constexpr size_t kOneWaveLds = 11264;
 
-template <int NW, int CAP, int G, int C, typename In>
+template <int NW, int CAP, int G, int C, typename In, bool RM = false>
 hipError_t run_vec(const void* const* rows, int world, int64_t n, float* g, double* partials,
                    int64_t* grid_out, hipStream_t s) {
-  constexpr int BS = G == 1 ? 64 : kThreads;
+  constexpr int BS = RM ? 512 : (G == 1 ? 64 : kThreads);
   RowTable<CAP> t;
   for (int i = 0; i < CAP; ++i) t.p[i] = i < world ? rows[i] : nullptr;
   const int64_t ngroups = n / 4;
@@ -151,10 +155,10 @@ hipError_t run_vec(const void* const* rows, int world, int64_t n, float* g, doub
   *grid_out = grid;
   const size_t lds = G > 1 ? (size_t)G * BS * 16 : kOneWaveLds;
   if (partials)
-    hipLaunchKernelGGL((k_reduce<NW, CAP, G, C, BS, In, true>), dim3((unsigned)grid), dim3(BS), lds,
+    hipLaunchKernelGGL((k_reduce<NW, CAP, G, C, BS, In, true, RM>), dim3((unsigned)grid), dim3(BS), lds,
                        s, t, world, mean_div(world), ngroups, n, g, partials);
   else
-    hipLaunchKernelGGL((k_reduce<NW, CAP, G, C, BS, In, false>), dim3((unsigned)grid), dim3(BS), lds,
+    hipLaunchKernelGGL((k_reduce<NW, CAP, G, C, BS, In, false, RM>), dim3((unsigned)grid), dim3(BS), lds,
                        s, t, world, mean_div(world), ngroups, n, g, partials);
   return hipGetLastError();
 }
@@ -175,13 +179,34 @@ hipError_t dispatch_world(const void* const* rows, int world, int64_t n, float* 
   }
 }
 
+// The rank-major shape of the single pass: 16 groups per lane in 8-wave
+// workgroups, 128 KiB of LDS, the ranks walked in chunks of C.
+template <typename In>
+hipError_t dispatch_world_rm(const void* const* rows, int world, int64_t n, float* g,
+                             double* partials, int64_t* grid, hipStream_t s) {
+  constexpr int C = sizeof(In) == 2 ? 4 : 2;
+  switch (world) {
+    case 16: return run_vec<16, 16, 16, C, In, true>(rows, world, n, g, partials, grid, s);
+    case 32: return run_vec<32, 32, 16, C, In, true>(rows, world, n, g, partials, grid, s);
+    case 64: return run_vec<64, 64, 16, C, In, true>(rows, world, n, g, partials, grid, s);
+    default:
+      if (world <= 64) return run_vec<0, 64, 16, C, In, true>(rows, world, n, g, partials, grid, s);
+      return run_vec<0, ZS_MAX_WORLD, 16, C, In, true>(rows, world, n, g, partials, grid, s);
+  }
+}
+
 // Measured on MI355X: deep staging (16 groups, 64 KiB) pays off when the
-// rank walk is long; with few contributions direct stores are faster.
+// rank walk is long, and the rank-major walk in 8-wave workgroups more so
+// (where its chunk divides the world size); with few contributions direct
+// stores are faster.
 template <typename In>
 hipError_t dispatch_shape(const void* const* rows, int world, int64_t n, float* g,
                           double* partials, int64_t* grid, hipStream_t s) {
   const int gsel = tuning().reduce_g > 0 ? tuning().reduce_g : (world >= 16 ? 16 : 1);
   const bool c4 = tuning().rank_chunk == 4;
+  const int rm_c = sizeof(In) == 2 ? 4 : 2;
+  if (tuning().reduce_g == 0 && world >= 16 && world % rm_c == 0)
+    return dispatch_world_rm<In>(rows, world, n, g, partials, grid, s);
   switch (gsel) {
     case 16:
       return c4 ? dispatch_world<16, 4, In>(rows, world, n, g, partials, grid, s)

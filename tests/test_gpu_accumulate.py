@@ -24,8 +24,10 @@ def _zero2(mbs, n, scale, sumsq=False, offset=0):
     return host(acc), (float(s.item()) if sumsq else None)
 
 
+# world sizes of each launch shape: one-wave (3, 8), rank-major 8-wave (16, 64,
+# 100; 30 with fp32 rows), group-major 4-wave (30 with bf16 rows, 33)
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("world", [3, 8, 64])
+@pytest.mark.parametrize("world", [3, 8, 16, 30, 33, 64, 100])
 def test_zero2_accumulation_matches_oracle(dtype, world):
     k, n = 4, 262144 + 5
     for scale in (1.0 / 4, 1.0 / 3, 1.0):

@@ -32,7 +32,7 @@ def _reduce(rows, n, sumsq=False):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("world", [1, 2, 3, 4, 7, 8, 64])
+@pytest.mark.parametrize("world", [1, 2, 3, 4, 7, 8, 16, 30, 33, 64, 100])
 def test_reduce_matches_oracle(dtype, world):
     for i, n in enumerate(SIZES):
         rows = device_rows(100 + world * 10 + i, world, n, dtype)
