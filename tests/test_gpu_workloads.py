@@ -148,6 +148,63 @@ def _full_size_case(n, world, dtype, step, moments, slot_offset, seed, windows=6
     assert torch.equal(slot.view(torch.int16), fslot.view(torch.int16))
 
 
+@pytest.mark.parametrize("world", [8, 7, 5])
+def test_gpt2_shard_end_to_end_every_element(world):
+    # GPT-2's 148 parameters (124,439,808 elements) as one FlatParameter over N
+    # ranks (tail pad 0, 4 and 2 elements). The last rank's shard, which holds
+    # the pad when there is one, is packed from the parameters and takes two
+    # single-pass steps from N bf16 contributions into its slot of the gather
+    # buffer; the other ranks' slots are the cast of their packed shards; the
+    # gathered buffer is then copied out per parameter. Every element of every
+    # stage is checked against the oracle, and the pad stays +0 throughout.
+    shp = shapes.gpt2_small()
+    rank = world - 1
+    g0 = gen.device_generator(7600 + world)
+    params = [gen.device_normal(g0, shapes.numel(s), gen.THETA_SIGMA).reshape(s) for _, s in shp]
+    params_h = [host(p).ravel() for p in params]
+    table = zs.ParamTable(params)
+    _, total, padded, S = zs.zs_flat_layout([p.numel() for p in params], world)
+    gather = torch.empty(padded, device="cuda", dtype=torch.bfloat16)
+    for r in range(world - 1):
+        t = torch.empty(S, device="cuda")
+        zs.zs_pack_shard(table, world, r, t)
+        zs.zs_cast_for_gather(t, gather[r * S:(r + 1) * S])
+    th, m, v = (torch.empty(S, device="cuda") for _ in range(3))
+    zs.zs_pack_shard(table, world, rank, th, m, v)
+    torch.cuda.synchronize()
+    want = olayout.pack_shard(params_h, world, rank)
+    for got, w in zip((th, m, v), want):
+        assert np.array_equal(bits32(host(got)), bits32(w))
+    slot = gather[rank * S:(rank + 1) * S]
+    gbuf = torch.empty(S, device="cuda")
+    hp = hparams()
+    pad = padded - total
+    for step in (1, 2):
+        rows = device_rows(7610 + 10 * world + step, world, S, "bf16")
+        for r in rows:
+            r[S - pad:] = 0  # the ranks' gradients of the tail pad are zero
+        before = tuple(host(t).copy() for t in (th, m, v))
+        zs.zs_reduce_grads(rows, gbuf)
+        zs.zs_sharded_step(rows, th, m, v, step=step, bf16_out=slot, **hp)
+        torch.cuda.synchronize()
+        g = host(gbuf)
+        check_mean(g, np.stack([host(r) for r in rows]))
+        after = tuple(host(t) for t in (th, m, v))
+        th_or = check_adamw(after, before, g, step, hp)
+        check_bf16(host(slot), after[0], th_or)
+        for t in after:
+            assert not bits32(t)[S - pad:].any()  # +0 bits in the pad
+    dst = [torch.empty(sh, device="cuda", dtype=torch.bfloat16) for _, sh in shp]
+    zs.zs_copy_out(gather, zs.ParamTable(dst))
+    torch.cuda.synchronize()
+    gathered = host(gather)
+    assert not gathered[total:].any()
+    for d, w in zip(dst, olayout.copy_out(gathered, [s for _, s in shp])):
+        assert np.array_equal(host(d), w)
+    del params, gather
+    torch.cuda.empty_cache()
+
+
 def test_full_size_7p5b_n64():
     numels = shapes.numels(shapes.flat_7p5b())
     lay = olayout.flat_layout(numels, 64)
