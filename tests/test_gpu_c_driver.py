@@ -75,6 +75,7 @@ def _run(tmp_path, world, dtype, numels, step, seed):
     (8, "bf16", [262144, 7, 65536 + 1]),           # several tiles and a ragged tail
     (64, "bf16", [100000, 31]),
     (8, "f32", [70000, 3]),
+    (32, "f32", [140000, 5]),                      # the rank-major shape with fp32 rows
 ])
 def test_c_driver_matches_oracle(tmp_path, world, dtype, numels):
     step = 3

@@ -78,8 +78,9 @@ def test_graph_replay_of_the_clipped_update(world, dtype):
         assert float(eb["coef"].item()) < 1.0  # the clip is active: max_norm is below the norm
 
 
-def test_graph_replay_of_the_single_pass():
-    n, world, hp, step = 1_000_003, 8, hparams(), 2
+@pytest.mark.parametrize("world", [8, 64])  # the one-wave and the rank-major 8-wave shape
+def test_graph_replay_of_the_single_pass(world):
+    n, hp, step = 1_000_003, hparams(), 2
     rows = device_rows(8400, world, n, "bf16")
     gs = device_state(8401, n)
     es = tuple(t.clone() for t in gs)
@@ -88,7 +89,7 @@ def test_graph_replay_of_the_single_pass():
     graph = _capture(lambda: zs.zs_sharded_step(rows, *gs, step=step, bf16_out=gslot, **hp))
     zs.zs_sharded_step(rows, *es, step=step, bf16_out=eslot, **hp)
     for it in range(4):
-        for r, fresh in zip(rows, device_rows(8500 + it, world, n, "bf16")):
+        for r, fresh in zip(rows, device_rows(8500 + 10 * world + it, world, n, "bf16")):
             r.copy_(fresh)
         zs.zs_sharded_step(rows, *es, step=step, bf16_out=eslot, **hp)
         torch.cuda.synchronize()

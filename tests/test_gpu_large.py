@@ -9,6 +9,8 @@
 * World sizes above 64, up to the ABI's maximum of 256 contributions (the row
   table of the widest kernel instantiation).
 """
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -30,9 +32,10 @@ def _windows(n, width=32768):
     return [(0, width), (EDGE - width, min(n, EDGE + width)), (n - width, n)]
 
 
-def test_step_beyond_2g_elements():
-    n, world = BIG, 2
-    rows = device_rows(31000, world, n, "bf16")
+@pytest.mark.parametrize("world", [2, 16])  # the one-wave and the rank-major 8-wave shape
+def test_step_beyond_2g_elements(world):
+    n = BIG
+    rows = device_rows(31000 + world, world, n, "bf16")
     g0 = gen.device_generator(31001)
     th = gen.device_normal(g0, n, gen.THETA_SIGMA)
     m = gen.device_normal(g0, n, 1e-4)
@@ -61,8 +64,11 @@ def test_step_beyond_2g_elements():
         assert torch.equal(x.view(torch.int32), y.view(torch.int32))
     assert torch.equal(slot.view(torch.int16), fslot.view(torch.int16))
     del rows, fused, fslot, m, v
-    # the fp64 sum of squares of all 2^31 + 12 reduced values, in halves on the host
-    ref = sum(oreduce.sumsq(host(g[a:b])) for a, b in ((0, EDGE), (EDGE, n)))
+    # the fp64 sum of squares of all 2^31 + 12 reduced values on the host: the
+    # oracle on 2^24-element chunks, whose partials fsum adds exactly (one
+    # sequential fp64 dot over 2^31 values is itself off by a few parts in 1e12)
+    chunk = 1 << 24
+    ref = math.fsum(oreduce.sumsq(host(g[a:min(a + chunk, n)])) for a in range(0, n, chunk))
     assert abs(sumsq.item() - ref) <= 1e-12 * ref
     # the standalone cast over the same range
     zs.zs_cast_for_gather(th, slot)
