@@ -10,8 +10,9 @@
 //
 // HBM-bound: 28 bytes per element (read g, theta, m, v; write theta, m, v),
 // +2 with the fused bf16 store. Lanes move 16-byte vectors of 4 fp32 and
-// 8-byte vectors of 4 bf16 (the bf16 slot of an odd rank can sit on an
-// 8-byte boundary when S is 4 mod 8).
+// aligned 8-byte words of 4 bf16 (a rank's bf16 slot can sit 2, 4 or 6 bytes
+// past an 8-byte boundary when S is not a multiple of 4; the words then
+// straddle neighbouring lanes' groups).
 #include <cmath>
 
 #include "zs_device.hpp"
@@ -61,20 +62,28 @@ __global__ __launch_bounds__(BS) void k_adamw(float* __restrict__ th, float* __r
     }
 #pragma unroll
     for (int j = 0; j < V; ++j) {
-      if (base + threadIdx.x + (int64_t)j * BS >= ngroups) continue;
+      const bool ok = base + threadIdx.x + (int64_t)j * BS < ngroups;
+      uint32_t lo = 0, hi = 0;  // the bf16 group, packed on live lanes only
+      if (ok) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float tt = T[j][e], mm = M[j][e], vv = W[j][e];
-        const float gg = SCALE ? G[j][e] * sc : G[j][e];
-        adamw_elem(tt, mm, vv, gg, c);
-        T[j][e] = tt;
-        M[j][e] = mm;
-        W[j][e] = vv;
+        for (int e = 0; e < 4; ++e) {
+          float tt = T[j][e], mm = M[j][e], vv = W[j][e];
+          const float gg = SCALE ? G[j][e] * sc : G[j][e];
+          adamw_elem(tt, mm, vv, gg, c);
+          T[j][e] = tt;
+          M[j][e] = mm;
+          W[j][e] = vv;
+        }
+        st_nt(T[j], reinterpret_cast<f32x4*>(th) + q[j]);
+        st_nt(M[j], reinterpret_cast<f32x4*>(m) + q[j]);
+        st_nt(W[j], reinterpret_cast<f32x4*>(v) + q[j]);
+        if (CAST) {
+          lo = pack_bf16x2(T[j][0], T[j][1]);
+          hi = pack_bf16x2(T[j][2], T[j][3]);
+          if (!(om & 1)) store_bf16_even(out, q[j], lo, hi, om);
+        }
       }
-      st_nt(T[j], reinterpret_cast<f32x4*>(th) + q[j]);
-      st_nt(M[j], reinterpret_cast<f32x4*>(m) + q[j]);
-      st_nt(W[j], reinterpret_cast<f32x4*>(v) + q[j]);
-      if (CAST) store_bf16x4(out, q[j], T[j], om);
+      if (CAST && (om & 1)) store_bf16_odd(out, q[j], lo, hi, ok, om);  // every lane
     }
   }
   if (blockIdx.x == 0) {  // ragged tail
@@ -133,8 +142,10 @@ __global__ __launch_bounds__(BS) void k_cast(const float* __restrict__ src, int6
     }
 #pragma unroll
     for (int j = 0; j < V; ++j) {
-      if (base + threadIdx.x + (int64_t)j * BS >= ngroups) continue;
-      store_bf16x4(vout, q[j], x[j], om);
+      const bool ok = base + threadIdx.x + (int64_t)j * BS < ngroups;
+      const uint32_t lo = pack_bf16x2(x[j][0], x[j][1]), hi = pack_bf16x2(x[j][2], x[j][3]);
+      if (om & 1) store_bf16_odd(vout, q[j], lo, hi, ok, om);  // every lane
+      else if (ok) store_bf16_even(vout, q[j], lo, hi, om);
     }
   }
   if (blockIdx.x == 0) {
@@ -201,17 +212,20 @@ hipError_t launch_adamw(float* th, float* m, float* v, const float* g, int64_t n
 hipError_t launch_cast(const float* src, int64_t n, uint16_t* out, hipStream_t s) {
   if (n == 0) return hipSuccess;
   if (aligned_to(src, 16) && aligned_to(out, 2)) {
-    // An output on an 8-byte boundary starts its vector part at its first
+    // The vector part starts where the waves' aligned 8-byte words fall on a
     // 128-byte boundary, so that each wave stores whole cache lines: HBM3E
     // turns a partial-line write into a read-modify-write, and the rank-63
     // slot of the 7.5B shard (8 bytes off the 16-byte grid) ran at 70% of
-    // peak against 83% for an aligned slot. The shift is a multiple of 4
-    // elements, so the fp32 loads stay 16-byte aligned.
-    int64_t head = 0;
-    if (aligned_to(out, 8)) {
-      head = (int64_t)(((128u - (reinterpret_cast<uintptr_t>(out) & 127u)) & 127u) / 2u);
-      if (head > n) head = n;
-    }
+    // peak against 83% for an aligned slot. The words begin at each group for
+    // an output on an 8-byte boundary and 3 or 1 elements into it for one 2
+    // or 6 bytes past (see store_bf16_odd); an output 4 bytes past stores
+    // 4-byte halves, whose waves straddle a line at either end whatever the
+    // shift. The shift is a multiple of 4 elements, so the fp32 loads stay
+    // 16-byte aligned.
+    const uintptr_t a = reinterpret_cast<uintptr_t>(out);
+    const uintptr_t lead = ((8u - (a & 7u)) & 7u) / 2u;  // elements to the next 8-byte boundary
+    int64_t head = (int64_t)(((128u - ((a + 2u * lead) & 127u)) & 127u) / 2u);
+    if (head > n) head = n;
     const int64_t ngroups = (n - head) / 4;
     const dim3 gd((unsigned)grid_for(ngroups, 2 * kAdamBS, kAdamBS));
     hipLaunchKernelGGL((k_cast<2, kAdamBS>), gd, dim3(kAdamBS), 0, s, src, head, ngroups, n, out,

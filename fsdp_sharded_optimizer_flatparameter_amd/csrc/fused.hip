@@ -59,22 +59,30 @@ __global__ __launch_bounds__(BS) void k_fused(RowTable<CAP> rows, int world, Mea
       M = ld_nt(reinterpret_cast<const f32x4*>(m) + q);
       W = ld_nt(reinterpret_cast<const f32x4*>(v) + q);
     };
-    auto update = [&](int k, f32x4& T, f32x4& M, f32x4& W) {
+    auto update = [&](int k, f32x4& T, f32x4& M, f32x4& W) {  // every lane calls it
       const int64_t qq = qidx(k);
-      if (qq >= ngroups) return;
-      const f32x4 gv = gl[k * BS + threadIdx.x];
+      const bool ok = qq < ngroups;
+      uint32_t lo = 0, hi = 0;  // the bf16 group, packed on live lanes only
+      if (ok) {
+        const f32x4 gv = gl[k * BS + threadIdx.x];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float tt = T[e], mm = M[e], vv = W[e];
-        adamw_elem(tt, mm, vv, gv[e], c);
-        T[e] = tt;
-        M[e] = mm;
-        W[e] = vv;
+        for (int e = 0; e < 4; ++e) {
+          float tt = T[e], mm = M[e], vv = W[e];
+          adamw_elem(tt, mm, vv, gv[e], c);
+          T[e] = tt;
+          M[e] = mm;
+          W[e] = vv;
+        }
+        st_nt(T, reinterpret_cast<f32x4*>(th) + qq);
+        st_nt(M, reinterpret_cast<f32x4*>(m) + qq);
+        st_nt(W, reinterpret_cast<f32x4*>(v) + qq);
+        if (CAST) {
+          lo = pack_bf16x2(T[0], T[1]);
+          hi = pack_bf16x2(T[2], T[3]);
+          if (!(om & 1)) store_bf16_even(out, qq, lo, hi, om);
+        }
       }
-      st_nt(T, reinterpret_cast<f32x4*>(th) + qq);
-      st_nt(M, reinterpret_cast<f32x4*>(m) + qq);
-      st_nt(W, reinterpret_cast<f32x4*>(v) + qq);
-      if (CAST) store_bf16x4(out, qq, T, om);
+      if (CAST && (om & 1)) store_bf16_odd(out, qq, lo, hi, ok, om);
     };
     if constexpr (sizeof(In) == 4 && !RM) {
       // fp32 contributions, group-major walk: all G groups' state loads are

@@ -66,31 +66,62 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
 }
 
-// bf16 store of one 4-element group into out[4q .. 4q + 3]. The group's 8
-// bytes go out as one 8-byte store when out is 8-byte aligned, as two 4-byte
-// stores when it is 4-byte aligned and as four 2-byte stores otherwise (a
-// rank's slot of the all-gather buffer starts at element r*S, so its alignment
-// follows S). `om` is uniform across the launch: 0, 1 or 2 for those cases.
-__device__ __forceinline__ void store_bf16x4(uint16_t* out, int64_t q, const f32x4& x, int om) {
-  const uint32_t lo = pack_bf16x2(x[0], x[1]), hi = pack_bf16x2(x[2], x[3]);
+// bf16 stores of a lane's 4-element group q into out[4q .. 4q + 3], packed as
+// pack_bf16x2 gives them (lo = elements 0-1, hi = 2-3). `d` is out's distance
+// from an 8-byte boundary in elements (0..3, uniform across the launch: a
+// rank's slot of the all-gather buffer starts at element r*S, so it follows S).
+//
+// d even: one 8-byte store (d == 0) or two aligned 4-byte stores (d == 2), by
+// the lane alone; callers issue it inside their live-lane branch.
+__device__ __forceinline__ void store_bf16_even(uint16_t* out, int64_t q, uint32_t lo, uint32_t hi,
+                                                int d) {
   uint16_t* p = out + 4 * q;
-  if (om == 0) {
+  if (d == 0) {
     st_nt(u32x2{lo, hi}, reinterpret_cast<u32x2*>(p));
-  } else if (om == 1) {
+  } else {
     st_nt(lo, reinterpret_cast<uint32_t*>(p));
     st_nt(hi, reinterpret_cast<uint32_t*>(p) + 1);
-  } else {
-    st_nt((uint16_t)lo, p);
-    st_nt((uint16_t)(lo >> 16), p + 1);
-    st_nt((uint16_t)hi, p + 2);
-    st_nt((uint16_t)(hi >> 16), p + 3);
   }
 }
 
-// Host: the store mode of store_bf16x4 for an output pointer.
+// d odd (odd S): called by every lane of the wave (it shuffles across it),
+// lane i+1 holding group q+1; `ok` is false for lanes past the end of the
+// range, which store nothing and should pass constants (packed inside the
+// callers' live-lane branch, so that the wave never waits for such a lane's
+// pending loads). Each lane stores the aligned 8-byte word that starts
+// s = 4 - d elements into its group -- its own last d elements and the next
+// lane's first s, taken by a wave shuffle -- instead of four 2-byte stores
+// (measured 1.5% faster for the single pass on the 7.5B shard and 3% on the
+// Llama-3-8B shard; for d == 2 the shuffle was 0.5% slower than the two
+// 4-byte stores). Only a lane whose neighbour is missing (the wave's first and
+// last lanes, and the last group of the range) writes those elements one by
+// one.
+__device__ __forceinline__ void store_bf16_odd(uint16_t* out, int64_t q, uint32_t lo, uint32_t hi,
+                                               bool ok, int d) {
+  uint16_t* p = out + 4 * q;
+  const int lane = threadIdx.x & 63;
+  const uint64_t live = __ballot(ok);
+  const uint32_t nlo = __shfl_down(lo, 1, 64), nhi = __shfl_down(hi, 1, 64);
+  if (!ok) return;
+  const bool has_next = lane < 63 && ((live >> (lane + 1)) & 1u);
+  const bool has_prev = lane > 0 && ((live >> (lane - 1)) & 1u);
+  const int s = 4 - d;
+  const uint64_t own = (uint64_t)lo | ((uint64_t)hi << 32);
+  if (has_next) {
+    const uint64_t nxt = (uint64_t)nlo | ((uint64_t)nhi << 32);
+    const uint64_t w = (own >> (16 * s)) | (nxt << (16 * d));
+    st_nt(u32x2{(uint32_t)w, (uint32_t)(w >> 32)}, reinterpret_cast<u32x2*>(p + s));
+  } else {
+    for (int e = s; e < 4; ++e) st_nt((uint16_t)(own >> (16 * e)), p + e);
+  }
+  if (!has_prev)
+    for (int e = 0; e < s; ++e) st_nt((uint16_t)(own >> (16 * e)), p + e);
+}
+
+// Host: the `d` of store_bf16_even / store_bf16_odd for an output pointer
+// (2-byte aligned).
 inline int bf16_out_mode(const void* out) {
-  const uintptr_t a = reinterpret_cast<uintptr_t>(out);
-  return (a & 7u) == 0 ? 0 : ((a & 3u) == 0 ? 1 : 2);
+  return (int)((reinterpret_cast<uintptr_t>(out) & 7u) >> 1);
 }
 
 // ---- gradient contributions ----------------------------------------------------

@@ -55,8 +55,10 @@
  *   - Alignment: any element-aligned pointer is accepted. Inputs and fp32
  *     state on 16-byte boundaries (8-byte for bf16 contributions) take the
  *     vector path, whatever the alignment of a bf16 output (its 4-element
- *     groups are stored as one 8-byte, two 4-byte or four 2-byte writes);
- *     others take an element-wise path with the same results.
+ *     groups are stored as one 8-byte or two 4-byte writes, or, when the
+ *     output is 2 or 6 bytes past an 8-byte boundary, as aligned 8-byte
+ *     words that straddle neighbouring groups); others take an element-wise
+ *     path with the same results.
  */
 #ifndef ZS_H_
 #define ZS_H_

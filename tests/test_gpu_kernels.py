@@ -148,17 +148,23 @@ def test_adamw_misaligned_and_8byte_slot():
     _adamw(50001, 2, hparams(), seed=323, out_offset=2)      # bf16 slot on a 4-byte boundary
 
 
-@pytest.mark.parametrize("world", [4, 64])
-def test_bf16_slot_at_every_alignment_is_bitwise_the_aligned_one(world):
+# every launch shape of the single pass: one-wave (4, 8), group-major 4-wave
+# (33), rank-major 8-wave (64; 16 with fp32 rows); the sizes leave the last
+# wave of every shape with 1 or 37 live lanes, so the bf16 words that straddle
+# two lanes' groups meet a missing neighbour mid-wave as well as at lane 63
+@pytest.mark.parametrize("world,dtype,n", [(4, "bf16", 262144 * 3 + 5), (8, "bf16", 262144 * 3 + 4 * 37 + 3),
+                                           (33, "bf16", 262144 * 3 + 4 * 37 + 3), (64, "bf16", 262144 * 3 + 5),
+                                           (16, "f32", 262144 * 3 + 4 * 37 + 3)])
+def test_bf16_slot_at_every_alignment_is_bitwise_the_aligned_one(world, dtype, n):
     # a rank's slot of the all-gather buffer starts at element r*S, so it can sit
-    # on an 8-, 4- or 2-byte boundary; the vector kernels split their bf16 stores
-    # to match, and every result must equal the 16-byte-aligned slot's bit for
-    # bit, with the elements around the slot left untouched
-    n = 262144 * 3 + 5
-    rows = device_rows(600 + world, world, n, "bf16")
+    # 2, 4 or 6 bytes past an 8-byte boundary; the vector kernels then store
+    # aligned 8-byte words that straddle neighbouring lanes' groups, and every
+    # result must equal the 16-byte-aligned slot's bit for bit, with the
+    # elements around the slot left untouched
+    rows = device_rows(600 + world, world, n, dtype)
     base_state = device_state(610 + world, n)
     results = {}
-    for off in (8, 1, 2, 3, 4):  # 8 elements = a 16-byte boundary, the reference
+    for off in (8, 1, 2, 3, 4, 5, 7):  # 8 elements = a 16-byte boundary, the reference
         buf = torch.full((n + 16,), float("nan"), device="cuda", dtype=torch.bfloat16)
         slot = buf[off:off + n]
         st = [t.clone() for t in base_state]
