@@ -637,6 +637,7 @@ def run(args, cpu) -> int:
     # same way (settle, W warm-up steps, K steps), right after the first so that
     # both run on the device in the same state (the 7.5B shard stays allocated:
     # together they hold about 75 GB)
+    llama_entry = None
     if args.workload == "7p5b" and not args.no_parts and not args.calibrate_copy:
         ll = make_shard("llama8b", dev)
         settle(ll["step"], args.settle_ms * 1e-3)
@@ -662,7 +663,8 @@ def run(args, cpu) -> int:
         runtime_copy_gbs = 2 * src.numel() * 2 / (t_copy * 1e-3) / 1e9
         del src, dst, one
         parts["fused_step"] = gbs_entry(ms_step, fused_bpe, S)
-        parts["llama8b_step"] = llama_entry
+        if llama_entry is not None:
+            parts["llama8b_step"] = llama_entry
         measure_parts(sh, dev, stream, max(10, args.steps), parts)
         if "torch_composed_step" in parts:
             parts["torch_composed_step"]["fused_step_speedup"] = round(parts["torch_composed_step"]["ms"] / ms_step, 3)
