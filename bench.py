@@ -195,18 +195,28 @@ def gbs_entry(ms: float, bpe: int, elems: int, **extra) -> dict:
 # ---------------------------------------------------------------- CPU oracle leg
 
 def cpu_model() -> str:
+    """The host CPU as the machine reports it: lscpu's model name, with the
+    family / model / stepping numbers from /proc/cpuinfo (a virtual machine may
+    report only a brand string such as "AMD EPYC")."""
+    name = None
     try:
         out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
-        for line in out.splitlines():
-            if line.startswith("Model name:"):
-                return line.split(":", 1)[1].strip()
+        name = next((ln.split(":", 1)[1].strip() for ln in out.splitlines() if ln.startswith("Model name:")), None)
     except (OSError, subprocess.SubprocessError):
         pass
+    ids = {}
     try:
         with open("/proc/cpuinfo") as f:
-            return next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "unknown")
+            for ln in f:
+                if not ln.strip():
+                    break  # the first processor's block
+                k, _, v = ln.partition(":")
+                ids[k.strip()] = v.strip()
     except OSError:
-        return "unknown"
+        pass
+    name = name or ids.get("model name", "unknown")
+    nums = [f"{k} {ids[k]}" for k in ("cpu family", "model", "stepping") if k in ids]
+    return f"{name} ({', '.join(nums)})" if nums else name
 
 
 def cpu_workers() -> int:

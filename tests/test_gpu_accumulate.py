@@ -25,12 +25,14 @@ def _zero2(mbs, n, scale, sumsq=False, offset=0):
 
 
 # world sizes of each launch shape: one-wave (3, 8), rank-major 8-wave (16, 64,
-# 100; 30 with fp32 rows), group-major 4-wave (30 with bf16 rows, 33)
+# 100; 30 with fp32 rows), group-major 4-wave (30 with bf16 rows, 33, 65)
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("world", [3, 8, 16, 30, 33, 64, 100])
+@pytest.mark.parametrize("world", [3, 8, 16, 30, 33, 64, 65, 100])
 def test_zero2_accumulation_matches_oracle(dtype, world):
-    k, n = 4, 262144 + 5
-    for scale in (1.0 / 4, 1.0 / 3, 1.0):
+    n = 262144 + 5
+    # four micro-batches (the sum of squares with the last), and one alone
+    # (the sum of squares with the first call)
+    for k, scale in ((4, 1.0 / 4), (4, 1.0 / 3), (4, 1.0), (1, 1.0 / 3), (1, 1.0)):
         mbs = [device_rows(900 + 10 * world + j, world, n, dtype) for j in range(k)]
         acc, ss = _zero2(mbs, n, scale, sumsq=True)
         want = oacc.zero2_accumulate([np.stack([host(r) for r in rows]) for rows in mbs], scale)

@@ -32,7 +32,7 @@ def _reduce(rows, n, sumsq=False):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("world", [1, 2, 3, 4, 7, 8, 16, 30, 33, 64, 100])
+@pytest.mark.parametrize("world", [1, 2, 3, 4, 7, 8, 16, 30, 32, 33, 48, 64, 65, 100])
 def test_reduce_matches_oracle(dtype, world):
     for i, n in enumerate(SIZES):
         rows = device_rows(100 + world * 10 + i, world, n, dtype)
@@ -251,12 +251,14 @@ def test_cast_at_every_offset_in_a_cache_line():
             assert np.all(b[:8 + off] == nan16) and np.all(b[8 + off + n:] == nan16), (off, n)
 
 
-# world sizes: the one-wave shape (< 16), the rank-major 8-wave shape (16, 32,
-# 64, 100 and 30 with fp32 rows), and the group-major 4-wave shape that takes
-# over when the rank-major chunk does not divide N (30 and 33 with bf16 rows,
-# 33 with fp32 rows); sizes span several tiles of each and a ragged tail
+# world sizes: the one-wave shape (< 16; 2, 4 and 8 have kernels of their
+# own), the rank-major 8-wave shape (16, 32, 64, and 48 and 100 through the
+# kernels for any N up to 64 and up to 256; 30 with fp32 rows), and the
+# group-major 4-wave shape that takes over when the rank-major chunk does not
+# divide N (30 and 33 with bf16 rows, 33 with fp32 rows, 65 above 64); sizes
+# span several tiles of each and a ragged tail
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("world", [1, 3, 4, 8, 16, 30, 32, 33, 64, 100])
+@pytest.mark.parametrize("world", [1, 2, 3, 4, 8, 16, 30, 32, 33, 48, 64, 65, 100])
 def test_fused_step_is_bitwise_the_two_call_path(dtype, world):
     for i, n in enumerate([5, 4096 + 3, 262144 + 7, 3 * 131072 + 4096 + 3]):
         rows = device_rows(500 + world + i, world, n, dtype)
@@ -267,10 +269,12 @@ def test_fused_step_is_bitwise_the_two_call_path(dtype, world):
         g = torch.empty(n, device="cuda")
         hp = hparams()
         sc = torch.tensor([0.5], device="cuda")
-        for step, scale in ((1, None), (2, sc)):
+        # with and without the gradient scale, with and without the bf16 copy
+        # (the slots keep the copies of step 2)
+        for step, scale, cast in ((1, None, True), (2, sc, True), (3, None, False), (4, sc, False)):
             zs.zs_reduce_grads(rows, g)
-            zs.zs_adamw_step(*a, g, step=step, grad_scale=scale, bf16_out=oa, **hp)
-            zs.zs_sharded_step(rows, *b, step=step, grad_scale=scale, bf16_out=ob, **hp)
+            zs.zs_adamw_step(*a, g, step=step, grad_scale=scale, bf16_out=oa if cast else None, **hp)
+            zs.zs_sharded_step(rows, *b, step=step, grad_scale=scale, bf16_out=ob if cast else None, **hp)
         torch.cuda.synchronize()
         for x, y in zip(a, b):
             assert np.array_equal(bits32(host(x)), bits32(host(y)))
