@@ -39,11 +39,11 @@ class AdamWHParams(C.Structure):
 # name -> (restype, argtypes), mirroring include/zs.h
 _I64P = C.POINTER(C.c_int64)
 SIGNATURES = {
-    "zs_flat_layout": (C.c_int32, [_I64P, C.c_int32, C.c_int32, _I64P, _I64P, _I64P, _I64P]),
+    "zs_flat_layout": (C.c_int32, [_I64P, C.c_int32, C.c_int32, C.c_int64, _I64P, _I64P, _I64P, _I64P]),
     "zs_check_layout": (C.c_int32, [C.POINTER(ParamDesc), C.c_int32, C.c_int64, C.c_int32]),
     "zs_pack_shard": (C.c_int32, [C.c_void_p, C.c_int32, C.c_int64, C.c_int32, C.c_int32,
-                                  C.c_int32, C.c_int64, C.c_void_p, C.c_void_p, C.c_void_p,
-                                  C.c_void_p]),
+                                  C.c_int32, C.c_int64, C.c_int64, C.c_void_p, C.c_void_p,
+                                  C.c_void_p, C.c_void_p]),
     "zs_reduce_grads": (C.c_int32, [C.POINTER(C.c_void_p), C.c_int32, C.c_int32, C.c_int64,
                                     C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
     "zs_reduce_grads_noalloc": (C.c_int32, [C.POINTER(C.c_void_p), C.c_int32, C.c_int32, C.c_int64,

@@ -55,14 +55,15 @@ def _hparams(lr, beta1, beta2, eps, weight_decay, step) -> L.AdamWHParams:
 
 # ---------------------------------------------------------------- layout
 
-def zs_flat_layout(numels, world: int):
-    """(offsets, total T, padded P, shard S) of a FlatParameter over `world` ranks."""
+def zs_flat_layout(numels, world: int, align: int = 1):
+    """(offsets, total T, padded P, shard S) of a FlatParameter over `world`
+    ranks, S rounded up to a multiple of `align` elements (1: no rounding)."""
     n = len(numels)
     arr = (C.c_int64 * max(n, 1))(*[int(x) for x in numels])
     offs = (C.c_int64 * max(n, 1))()
     total, padded, shard = C.c_int64(), C.c_int64(), C.c_int64()
     L.check("zs_flat_layout", _lib().zs_flat_layout(
-        arr, n, int(world), offs, C.byref(total), C.byref(padded), C.byref(shard)))
+        arr, n, int(world), int(align), offs, C.byref(total), C.byref(padded), C.byref(shard)))
     return list(offs[:n]), total.value, padded.value, shard.value
 
 
@@ -105,7 +106,7 @@ class ParamTable:
 # ---------------------------------------------------------------- pack / copy-out
 
 def zs_pack_shard(table: ParamTable, world: int, rank: int, master, exp_avg=None, exp_avg_sq=None,
-                  stream=None):
+                  stream=None, align: int = 1):
     _dev(master, "master", torch.float32)
     for name, t in (("exp_avg", exp_avg), ("exp_avg_sq", exp_avg_sq)):
         if t is not None:
@@ -114,7 +115,7 @@ def zs_pack_shard(table: ParamTable, world: int, rank: int, master, exp_avg=None
                 raise ValueError(f"{name} must have the master's size")
     L.check("zs_pack_shard", _lib().zs_pack_shard(
         table.ptr, table.nparams, table.total, _DTYPES[table.dtype], int(world), int(rank),
-        master.numel(), _ptr(master), _ptr(exp_avg), _ptr(exp_avg_sq),
+        int(align), master.numel(), _ptr(master), _ptr(exp_avg), _ptr(exp_avg_sq),
         _stream(stream, master.device)))
 
 

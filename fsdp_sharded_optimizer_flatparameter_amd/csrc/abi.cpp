@@ -98,10 +98,23 @@ const char* zs_status_string(zs_status s) {
   }
 }
 
-zs_status zs_flat_layout(const int64_t* numels, int32_t nparams, int32_t world,
+// S of a unit of t elements over `world` ranks: ceil(t / world) rounded up to a
+// multiple of `align`; ZS_ERR_SIZE when it or S * world overflows int64.
+static zs_status shard_length(int64_t t, int32_t world, int64_t align, int64_t* s_out) {
+  int64_t s = t / world + (t % world != 0);
+  if (align > 1) {
+    if (s > INT64_MAX - (align - 1)) return ZS_ERR_SIZE;
+    s = (s + align - 1) / align * align;
+  }
+  if (s > INT64_MAX / world) return ZS_ERR_SIZE;
+  *s_out = s;
+  return ZS_OK;
+}
+
+zs_status zs_flat_layout(const int64_t* numels, int32_t nparams, int32_t world, int64_t align,
                          int64_t* offsets_out, int64_t* total_out, int64_t* padded_out,
                          int64_t* shard_out) {
-  if (nparams < 0) return ZS_ERR_SIZE;
+  if (nparams < 0 || align < 1) return ZS_ERR_SIZE;
   if (world < 1) return ZS_ERR_WORLD;
   if (nparams > 0 && !numels) return ZS_ERR_NULL;
   int64_t t = 0;
@@ -110,8 +123,8 @@ zs_status zs_flat_layout(const int64_t* numels, int32_t nparams, int32_t world,
     if (numels[i] > INT64_MAX - t) return ZS_ERR_SIZE;
     t += numels[i];
   }
-  const int64_t s = t / world + (t % world != 0);
-  if (s > INT64_MAX / world) return ZS_ERR_SIZE;
+  int64_t s = 0;
+  if (const zs_status st = shard_length(t, world, align, &s)) return st;
   if (offsets_out) {
     int64_t run = 0;
     for (int32_t i = 0; i < nparams; ++i) {
@@ -150,14 +163,16 @@ size_t zs_workspace_bytes(int64_t n) {
 }
 
 zs_status zs_pack_shard(const zs_param_desc* d_desc, int32_t nparams, int64_t total_numel,
-                        int32_t src_dtype, int32_t world, int32_t rank, int64_t shard_numel,
-                        float* master, float* exp_avg, float* exp_avg_sq, hipStream_t stream) {
-  if (nparams < 0 || total_numel < 0 || shard_numel < 0) return ZS_ERR_SIZE;
+                        int32_t src_dtype, int32_t world, int32_t rank, int64_t align,
+                        int64_t shard_numel, float* master, float* exp_avg, float* exp_avg_sq,
+                        hipStream_t stream) {
+  if (nparams < 0 || total_numel < 0 || shard_numel < 0 || align < 1) return ZS_ERR_SIZE;
   if (nparams == 0 && total_numel != 0) return ZS_ERR_SIZE;
   if (world < 1) return ZS_ERR_WORLD;
   if (rank < 0 || rank >= world) return ZS_ERR_RANK;
   if (src_dtype != ZS_F32 && src_dtype != ZS_BF16) return ZS_ERR_DTYPE;
-  const int64_t s = total_numel / world + (total_numel % world != 0);
+  int64_t s = 0;
+  if (const zs_status st = shard_length(total_numel, world, align, &s)) return st;
   if (shard_numel != s) return ZS_ERR_SHARD;
   if (shard_numel == 0) return ZS_OK;
   if (!master || (nparams > 0 && !d_desc)) return ZS_ERR_NULL;

@@ -131,16 +131,26 @@ typedef struct zs_adamw_hparams {
  * [L5] s7.1 points 1 and 3; [LAF] s5.1; [DPZ] s4.2 (contiguous split).
  *   numels[nparams]      element count of each parameter, in registration order
  *   world                data-parallel world size N (>= 1)
+ *   align                S is rounded up to a multiple of `align` elements
+ *                        (>= 1). 1 gives the pages' layout, P = ceil(T / N) * N.
+ *                        64 puts every rank's slice of a bf16 gather buffer,
+ *                        and every row of a bf16 [N, S] receive buffer, on a
+ *                        128-byte line: slices and rows off it cost the single
+ *                        pass up to 3% (slices, at n = 1,003,782,656, N = 8)
+ *                        and 10% (rows, at n = 117,187,500, N = 64). The extra
+ *                        padding is at the tail; parameter offsets do not move.
  *   offsets_out[nparams] receives flat_offset of each parameter (exclusive
  *                        prefix sum of numels); may be NULL
  *   total_out            receives T = sum(numels)
- *   padded_out           receives P = ceil(T / N) * N (tail padding only)
- *   shard_out            receives S = P / N, the per-rank slice length
+ *   padded_out           receives P = S * N (tail padding only)
+ *   shard_out            receives S = ceil(T / N) rounded up to a multiple of
+ *                        align, the per-rank slice length
  * All pointers are host pointers. Output pointers other than offsets_out may
  * be NULL. Errors: ZS_ERR_NULL (numels NULL with nparams > 0), ZS_ERR_SIZE
- * (nparams < 0, a negative numel, or T overflowing int64), ZS_ERR_WORLD.
+ * (nparams < 0, align < 1, a negative numel, or T or P overflowing int64),
+ * ZS_ERR_WORLD.
  */
-zs_status zs_flat_layout(const int64_t* numels, int32_t nparams, int32_t world,
+zs_status zs_flat_layout(const int64_t* numels, int32_t nparams, int32_t world, int64_t align,
                          int64_t* offsets_out, int64_t* total_out, int64_t* padded_out,
                          int64_t* shard_out);
 
@@ -162,7 +172,11 @@ zs_status zs_check_layout(const zs_param_desc* host_desc, int32_t nparams, int64
  *   d_desc[nparams]  DEVICE table describing the unit (see zs_param_desc);
  *                    parameters hold `src_dtype` elements (ZS_F32 or ZS_BF16)
  *   total_numel      T of the unit (the table must tile [0, T))
- *   world, rank      N and r; shard_numel must equal ceil(T / N)
+ *   world, rank      N and r
+ *   align, shard_numel
+ *                    the layout's rounding and S: shard_numel must equal the S
+ *                    that zs_flat_layout gives for (T, N, align), otherwise
+ *                    ZS_ERR_SHARD
  *   master[S]        receives flat[r*S + k] for k < S, as fp32 (bf16 sources
  *                    are widened exactly); positions at or past T are +0.0
  *   exp_avg[S], exp_avg_sq[S]
@@ -172,8 +186,9 @@ zs_status zs_check_layout(const zs_param_desc* host_desc, int32_t nparams, int64
  * ZS_ERR_WORLD, ZS_ERR_RANK, ZS_ERR_DTYPE, ZS_ERR_SHARD, ZS_ERR_HIP.
  */
 zs_status zs_pack_shard(const zs_param_desc* d_desc, int32_t nparams, int64_t total_numel,
-                        int32_t src_dtype, int32_t world, int32_t rank, int64_t shard_numel,
-                        float* master, float* exp_avg, float* exp_avg_sq, hipStream_t stream);
+                        int32_t src_dtype, int32_t world, int32_t rank, int64_t align,
+                        int64_t shard_numel, float* master, float* exp_avg, float* exp_avg_sq,
+                        hipStream_t stream);
 
 /*
  * zs_reduce_grads -- mean of N gradient contributions for this rank's slice.

@@ -17,6 +17,11 @@ Readings where the pages are silent:
   * no alignment padding between parameters, only the tail pad;
   * pad value +0.0;
   * the rank shard of an empty unit is empty.
+
+Beyond the pages: `align` (default 1, the pages' layout) rounds the per-rank
+slice S up to a multiple of `align` elements. The extra padding also sits at
+the tail of the unit, so parameter offsets and every real element's value
+are unchanged; only S, P and the rank boundaries r*S move.
 """
 from __future__ import annotations
 
@@ -29,16 +34,18 @@ import numpy as np
 class Layout:
     offsets: tuple  # offset of parameter i inside the flat buffer
     total: int      # T = sum of element counts
-    padded: int     # P = ceil(T / N) * N
-    shard: int      # S = P / N
-    pad: int        # P - T, always in [0, N)
+    padded: int     # P = S * N
+    shard: int      # S = ceil(T / N) rounded up to a multiple of align
+    pad: int        # P - T, always in [0, N * align)
     world: int
 
 
-def flat_layout(numels, world: int) -> Layout:
+def flat_layout(numels, world: int, align: int = 1) -> Layout:
     """Offsets are the exclusive prefix sum of element counts in list order."""
     if world < 1:
         raise ValueError("world size must be >= 1")
+    if align < 1:
+        raise ValueError("align must be >= 1")
     offsets = []
     t = 0
     for n in numels:
@@ -48,13 +55,14 @@ def flat_layout(numels, world: int) -> Layout:
         offsets.append(t)
         t += n
     s = -(-t // world)  # ceil(T / N)
+    s = -(-s // align) * align  # up to a multiple of align
     p = s * world
     return Layout(tuple(offsets), t, p, s, p - t, world)
 
 
-def flatten(params, world: int, dtype=None) -> np.ndarray:
+def flatten(params, world: int, dtype=None, align: int = 1) -> np.ndarray:
     """Concatenate C-order ravels of `params` and append zero padding up to P."""
-    lay = flat_layout([np.asarray(p).size for p in params], world)
+    lay = flat_layout([np.asarray(p).size for p in params], world, align)
     if dtype is None:
         dtype = np.asarray(params[0]).dtype if params else np.float32
     flat = np.zeros(lay.padded, dtype=dtype)
@@ -74,7 +82,7 @@ def shard_of(flat: np.ndarray, world: int, rank: int) -> np.ndarray:
     return flat[rank * s:(rank + 1) * s]
 
 
-def pack_shard(params, world: int, rank: int):
+def pack_shard(params, world: int, rank: int, align: int = 1):
     """The rank's fp32 master shard plus zeroed Adam moments.
 
     Parameters may be fp32 arrays or bf16 patterns given as uint16 arrays; the
@@ -86,7 +94,7 @@ def pack_shard(params, world: int, rank: int):
         if a.dtype == np.uint16:
             a = (a.astype(np.uint32) << np.uint32(16)).view(np.float32)
         decoded.append(a.astype(np.float32, copy=False))
-    flat = flatten(decoded, world, dtype=np.float32)
+    flat = flatten(decoded, world, dtype=np.float32, align=align)
     master = shard_of(flat, world, rank).copy()
     return master, np.zeros_like(master), np.zeros_like(master)
 

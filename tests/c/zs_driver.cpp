@@ -120,7 +120,7 @@ int main(int argc, char** argv) {
   // theta (split the same way) as a world-1 shard
   std::vector<int64_t> offsets(nparams);
   int64_t total = 0, padded = 0, shard = 0;
-  ZS_OK_OR_EXIT(zs_flat_layout(numel.data(), nparams, 1, offsets.data(), &total, &padded, &shard));
+  ZS_OK_OR_EXIT(zs_flat_layout(numel.data(), nparams, 1, 1, offsets.data(), &total, &padded, &shard));
   if (total != n) return 2;
   std::vector<zs_param_desc> out_desc(nparams), src_desc(nparams);
   std::vector<uint16_t*> outs(nparams);
@@ -137,7 +137,7 @@ int main(int argc, char** argv) {
   zs_param_desc* d_src_desc = dev_copy(src_desc.data(), nparams);
   ZS_OK_OR_EXIT(zs_copy_out(d_out, n, d_out_desc, nparams, total, s));
   float* d_master = dev_copy<float>(nullptr, n);
-  ZS_OK_OR_EXIT(zs_pack_shard(d_src_desc, nparams, total, ZS_F32, 1, 0, shard, d_master, nullptr,
+  ZS_OK_OR_EXIT(zs_pack_shard(d_src_desc, nparams, total, ZS_F32, 1, 0, 1, shard, d_master, nullptr,
                               nullptr, s));
   // bf16 cast alone of the two-call theta'
   uint16_t* c_out = dev_copy<uint16_t>(nullptr, n);

@@ -57,12 +57,12 @@ def test_status_codes_match_header(lib):
     assert lib.zs_version() >= 100
 
 
-def _layout_c(lib, numels, world):
+def _layout_c(lib, numels, world, align=1):
     n = len(numels)
     arr = (C.c_int64 * max(n, 1))(*numels)
     offs = (C.c_int64 * max(n, 1))()
     t, p, s = C.c_int64(), C.c_int64(), C.c_int64()
-    st = lib.zs_flat_layout(arr, n, world, offs, C.byref(t), C.byref(p), C.byref(s))
+    st = lib.zs_flat_layout(arr, n, world, align, offs, C.byref(t), C.byref(p), C.byref(s))
     return st, list(offs[:n]), t.value, p.value, s.value
 
 
@@ -74,19 +74,23 @@ def test_flat_layout_matches_oracle(lib):
     cases += [[0], [1], [0, 0, 5, 0]]
     for numels in cases:
         for world in (1, 2, 3, 4, 5, 7, 8, 9, 64, 256):
-            st, offs, t, p, s = _layout_c(lib, numels, world)
-            ref = olayout.flat_layout(numels, world)
-            assert st == 0
-            assert (offs, t, p, s) == (list(ref.offsets), ref.total, ref.padded, ref.shard)
+            for align in (1, 3, 64):
+                st, offs, t, p, s = _layout_c(lib, numels, world, align)
+                ref = olayout.flat_layout(numels, world, align)
+                assert st == 0
+                assert (offs, t, p, s) == (list(ref.offsets), ref.total, ref.padded, ref.shard)
 
 
 def test_flat_layout_errors(lib):
     assert _layout_c(lib, [4, 4], 0)[0] == -3
     assert _layout_c(lib, [4, -1], 2)[0] == -2
+    assert _layout_c(lib, [4, 4], 2, 0)[0] == -2  # align < 1
     assert _layout_c(lib, [2 ** 62, 2 ** 62], 1)[0] == -2  # int64 overflow
+    assert _layout_c(lib, [2 ** 62], 1, 2 ** 62 + 3)[0] == -2  # the rounded S overflows
+    assert _layout_c(lib, [2 ** 62], 2, 2 ** 62 + 1)[0] == -2  # S * N overflows
     t = C.c_int64()
-    assert lib.zs_flat_layout(None, 2, 2, None, C.byref(t), None, None) == -1
-    assert lib.zs_flat_layout(None, 0, 2, None, C.byref(t), None, None) == 0 and t.value == 0
+    assert lib.zs_flat_layout(None, 2, 2, 1, None, C.byref(t), None, None) == -1
+    assert lib.zs_flat_layout(None, 0, 2, 1, None, C.byref(t), None, None) == 0 and t.value == 0
 
 
 def _table(entries):
@@ -233,16 +237,19 @@ def test_cast_copy_out_pack_errors(lib):
 
     p = lib.zs_pack_shard
     mm = C.c_void_p(FAKE + (1 << 38))
-    assert p(d, 2, 10, 0, 0, 0, 10, mm, None, None, None) == -3
-    assert p(d, 2, 10, 0, 4, 4, 3, mm, None, None, None) == -4
-    assert p(d, 2, 10, 0, 4, -1, 3, mm, None, None, None) == -4
-    assert p(d, 2, 10, 9, 4, 0, 3, mm, None, None, None) == -5
-    assert p(d, 2, 10, 0, 4, 0, 2, mm, None, None, None) == -7   # S must be ceil(10/4) = 3
-    assert p(d, 2, 10, 0, 4, 0, 3, None, None, None, None) == -1
-    assert p(None, 2, 10, 0, 4, 0, 3, mm, None, None, None) == -1
-    assert p(d, 0, 10, 0, 4, 0, 3, mm, None, None, None) == -2
-    assert p(d, 2, 10, 0, 4, 0, 3, mm, C.c_void_p(FAKE + (1 << 38) + 4), None, None) == -11
-    assert p(d, 0, 0, 0, 4, 0, 0, None, None, None, None) == 0
+    assert p(d, 2, 10, 0, 0, 0, 1, 10, mm, None, None, None) == -3
+    assert p(d, 2, 10, 0, 4, 4, 1, 3, mm, None, None, None) == -4
+    assert p(d, 2, 10, 0, 4, -1, 1, 3, mm, None, None, None) == -4
+    assert p(d, 2, 10, 9, 4, 0, 1, 3, mm, None, None, None) == -5
+    assert p(d, 2, 10, 0, 4, 0, 1, 2, mm, None, None, None) == -7   # S must be ceil(10/4) = 3
+    assert p(d, 2, 10, 0, 4, 0, 4, 3, mm, None, None, None) == -7   # with align 4, S = 4
+    assert p(d, 2, 10, 0, 4, 0, 0, 3, mm, None, None, None) == -2   # align < 1
+    assert p(d, 2, 10, 0, 4, 0, 1, 3, None, None, None, None) == -1
+    assert p(None, 2, 10, 0, 4, 0, 1, 3, mm, None, None, None) == -1
+    assert p(d, 0, 10, 0, 4, 0, 1, 3, mm, None, None, None) == -2
+    assert p(d, 2, 10, 0, 4, 0, 1, 3, mm, C.c_void_p(FAKE + (1 << 38) + 4), None, None) == -11
+    assert p(d, 2, 10, 0, 4, 0, 4, 4, mm, C.c_void_p(FAKE + (1 << 38) + 12), None, None) == -11
+    assert p(d, 0, 0, 0, 4, 0, 1, 0, None, None, None, None) == 0
 
 
 def test_sharded_step_argument_errors(lib):

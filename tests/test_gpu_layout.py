@@ -18,13 +18,13 @@ def _params(shape_list, seed, dtype=torch.float32):
             for _, s in shape_list]
 
 
-def _pack(params, world, rank):
+def _pack(params, world, rank, align=1):
     table = zs.ParamTable(params)
-    _, total, padded, shard = zs.zs_flat_layout([p.numel() for p in params], world)
+    _, total, padded, shard = zs.zs_flat_layout([p.numel() for p in params], world, align)
     master = torch.full((shard,), float("nan"), device="cuda")
     m = torch.full_like(master, 3.0)
     v = torch.full_like(master, 3.0)
-    zs.zs_pack_shard(table, world, rank, master, m, v)
+    zs.zs_pack_shard(table, world, rank, master, m, v, align=align)
     torch.cuda.synchronize()
     return host(master), host(m), host(v)
 
@@ -40,6 +40,23 @@ def test_pack_matches_oracle_every_rank(name, world):
         master, m, v = _pack(params, world, r)
         want, _, _ = olayout.pack_shard(host_params, world, r)
         assert np.array_equal(bits32(master), bits32(want)), (name, world, r)
+        assert not bits32(m).any() and not bits32(v).any()
+
+
+@pytest.mark.parametrize("name,world,align", [("tiny_ragged", 3, 3), ("tiny_ragged", 7, 64), ("gpt2", 5, 64),
+                                              ("gpt2", 8, 1000)])
+def test_pack_with_aligned_slices_matches_oracle_every_rank(name, world, align):
+    # slices rounded up to a multiple of `align` elements: each rank's master
+    # is the oracle's, the padding past the unit +0
+    shp = shapes.WORKLOADS[name][0]()
+    params = _params(shp, seed=sum(map(ord, name)) + world + align)
+    host_params = [host(p).ravel() for p in params]
+    ranks = range(world) if name != "gpt2" else (0, world // 2, world - 1)
+    for r in ranks:
+        master, m, v = _pack(params, world, r, align)
+        want, _, _ = olayout.pack_shard(host_params, world, r, align)
+        assert master.size % align == 0
+        assert np.array_equal(bits32(master), bits32(want)), (name, world, align, r)
         assert not bits32(m).any() and not bits32(v).any()
 
 
@@ -114,21 +131,26 @@ def test_copy_out_70b_block_full():
     _copy_out_case(shapes.llama_70b_block(), seed=24, world=64)
 
 
-def test_roundtrip_pack_cast_gather_copy_out():
+@pytest.mark.parametrize("align", [1, 64])
+def test_roundtrip_pack_cast_gather_copy_out(align):
     # with lr = wd = 0, theta is unchanged, so the unsharded parameters come back
-    # as the bf16 rounding of the originals, bit for bit
+    # as the bf16 rounding of the originals, bit for bit; with slices rounded to
+    # 64 elements every rank's slot starts on a 128-byte line (S = 24,887,962
+    # by the pages' rule puts odd ranks' slots 4 bytes off an 8-byte boundary)
     shp = shapes.gpt2_small()
     world = 5
     params = _params(shp, seed=31)
     numels = [p.numel() for p in params]
-    _, total, padded, shard = zs.zs_flat_layout(numels, world)
+    _, total, padded, shard = zs.zs_flat_layout(numels, world, align)
     table = zs.ParamTable(params)
     gather = torch.empty(padded, device="cuda", dtype=torch.bfloat16)
+    if align == 64:
+        assert all((gather.data_ptr() + 2 * r * shard) % 128 == 0 for r in range(world))
     for r in range(world):
         master = torch.empty(shard, device="cuda")
         m = torch.empty_like(master)
         v = torch.empty_like(master)
-        zs.zs_pack_shard(table, world, r, master, m, v)
+        zs.zs_pack_shard(table, world, r, master, m, v, align=align)
         zero_g = torch.zeros(shard, device="cuda")
         zs.zs_adamw_step(master, m, v, zero_g, step=1, lr=0.0, beta1=0.9, beta2=0.999, eps=1e-8,
                          weight_decay=0.0, bf16_out=gather[r * shard:(r + 1) * shard])

@@ -13,14 +13,14 @@ from oracle import layout
 from synth import shapes
 
 
-def _brute_flat(params, world):
+def _brute_flat(params, world, align=1):
     elems = []
     for p in params:
         for x in np.asarray(p).ravel(order="C"):
             elems.append(x)
     t = len(elems)
-    s = 0
-    while s * world < t:
+    s = 0  # the smallest multiple of align whose N copies hold every element
+    while s * world < t or s % align:
         s += 1
     while len(elems) < s * world:
         elems.append(0.0)
@@ -160,7 +160,47 @@ def test_copy_out_shapes_and_pad_dropped():
     assert outs[2].ravel().tolist() == list(range(10, 15))
 
 
+def test_brute_force_small_with_aligned_slices():
+    # S rounded up to a multiple of align: found by counting, the padding at
+    # the tail, the parameter offsets and real elements those of align = 1
+    for numels in list(_lists_up_to(40))[::3]:
+        params = [np.arange(1, n + 1, dtype=np.float32) * (i + 1) * 1000 + np.float32(0.5)
+                  for i, n in enumerate(numels)]
+        for world in range(1, 7):
+            base = layout.flat_layout(numels, world)
+            for align in (1, 2, 3, 8, 64):
+                want_flat, want_s = _brute_flat(params, world, align)
+                lay = layout.flat_layout(numels, world, align)
+                assert lay.shard == want_s and lay.padded == want_s * world
+                assert lay.offsets == base.offsets and lay.total == base.total
+                assert base.shard <= lay.shard < base.shard + align
+                if not params:
+                    continue
+                flat = layout.flatten(params, world, dtype=np.float32, align=align)
+                assert np.array_equal(flat.view(np.uint32), want_flat.view(np.uint32))
+                for r in range(world):
+                    master, m, v = layout.pack_shard(params, world, r, align)
+                    assert np.array_equal(master, want_flat[r * want_s:(r + 1) * want_s])
+                    assert not m.any() and not v.any()
+                outs = layout.copy_out(flat, [(n,) for n in numels])
+                for o, p in zip(outs, params):
+                    assert np.array_equal(o, p)
+
+
+def test_aligned_slices_by_hand():
+    # six elements over three ranks: S = 2 by the pages' rule; with slices
+    # rounded up to 4 elements the ranks hold [1 2 3 4], [5 6 0 0], [0 0 0 0]
+    flat = layout.flatten([np.array([1, 2, 3, 4, 5, 6], np.float32)], 3, align=4)
+    assert [layout.shard_of(flat, 3, r).tolist() for r in range(3)] == [[1, 2, 3, 4], [5, 6, 0, 0], [0, 0, 0, 0]]
+    lay = layout.flat_layout([6], 3, 4)
+    assert (lay.shard, lay.padded, lay.pad) == (4, 12, 6)
+    # a slice that is already a multiple keeps its size
+    assert layout.flat_layout([128], 2, 64).shard == 64
+
+
 def test_errors():
+    with pytest.raises(ValueError):
+        layout.flat_layout([3], 2, 0)
     with pytest.raises(ValueError):
         layout.flat_layout([3], 0)
     with pytest.raises(ValueError):

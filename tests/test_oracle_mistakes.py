@@ -175,8 +175,8 @@ def _shard_shifted(flat, world, rank):  # starts one element late
     return out
 
 
-def _flatten_front_pad(params, world, dtype=None):  # the pad at the front
-    lay = layout.flat_layout([np.asarray(p).size for p in params], world)
+def _flatten_front_pad(params, world, dtype=None, align=1):  # the pad at the front
+    lay = layout.flat_layout([np.asarray(p).size for p in params], world, align)
     if dtype is None:
         dtype = np.asarray(params[0]).dtype if params else np.float32
     flat = np.zeros(lay.padded, dtype=dtype)
@@ -186,8 +186,8 @@ def _flatten_front_pad(params, world, dtype=None):  # the pad at the front
     return flat
 
 
-def _flatten_fortran(params, world, dtype=None):  # each tensor in column-major order
-    lay = layout.flat_layout([np.asarray(p).size for p in params], world)
+def _flatten_fortran(params, world, dtype=None, align=1):  # each tensor in column-major order
+    lay = layout.flat_layout([np.asarray(p).size for p in params], world, align)
     if dtype is None:
         dtype = np.asarray(params[0]).dtype if params else np.float32
     flat = np.zeros(lay.padded, dtype=dtype)
@@ -197,13 +197,28 @@ def _flatten_fortran(params, world, dtype=None):  # each tensor in column-major 
     return flat
 
 
-def _layout_floor(numels, world):  # P rounded down instead of up
-    offsets, t = [], 0
-    for n in numels:
-        offsets.append(t)
-        t += int(n)
-    s = t // world
-    return layout.Layout(tuple(offsets), t, s * world, s, s * world - t, world)
+def _layout_with(shard_rule):
+    def flat_layout(numels, world, align=1):
+        offsets, t = [], 0
+        for n in numels:
+            offsets.append(t)
+            t += int(n)
+        s = shard_rule(t, world, align)
+        return layout.Layout(tuple(offsets), t, s * world, s, s * world - t, world)
+    flat_layout.__name__ = shard_rule.__name__
+    return flat_layout
+
+
+def _layout_floor(t, world, align):  # S = T / N rounded down instead of up
+    return -(-(t // world) // align) * align
+
+
+def _layout_align_floor(t, world, align):  # ceil(T / N) rounded down to a multiple of align
+    return (-(-t // world) // align) * align
+
+
+def _layout_align_total(t, world, align):  # T rounded up to a multiple of align, then split
+    return -(-(-(-t // align) * align) // world)
 
 
 LAYOUT_PINS = [pins_layout.test_brute_force_small, pins_layout.test_tiny_shard_is_param,
@@ -211,11 +226,16 @@ LAYOUT_PINS = [pins_layout.test_brute_force_small, pins_layout.test_tiny_shard_i
                pins_layout.test_contiguous_assignment_matches_illustration,
                pins_layout.test_flat_window_equals_slices_of_flatten,
                pins_layout.test_copy_out_shapes_and_pad_dropped,
-               pins_layout.test_multidim_params_flatten_row_major]
+               pins_layout.test_multidim_params_flatten_row_major,
+               pins_layout.test_brute_force_small_with_aligned_slices,
+               pins_layout.test_aligned_slices_by_hand]
 
 
 @pytest.mark.parametrize("name,fn", [("shard_of", _shard_shifted), ("flatten", _flatten_front_pad),
-                                     ("flatten", _flatten_fortran), ("flat_layout", _layout_floor)])
+                                     ("flatten", _flatten_fortran),
+                                     ("flat_layout", _layout_with(_layout_floor)),
+                                     ("flat_layout", _layout_with(_layout_align_floor)),
+                                     ("flat_layout", _layout_with(_layout_align_total))])
 def test_layout_pins_catch(monkeypatch, name, fn):
     monkeypatch.setattr(layout, name, fn)
     assert _fails(LAYOUT_PINS), fn.__name__
