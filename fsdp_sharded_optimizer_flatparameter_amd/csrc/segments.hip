@@ -12,24 +12,39 @@
 // all-gather result is copied out per parameter).
 //
 // Every kernel walks a contiguous range -- the flat buffer, the rank's shard,
-// or the rank-major gather buffer -- in chunks of kChunk elements, one chunk
-// per workgroup iteration. The workgroup finds the parameters that overlap its
-// chunk by binary search over the parameter offsets (staged in LDS when the
-// table is small), then copies each overlap with 16-byte vectors. A bf16 copy
-// whose source and destination sit at different offsets from the 16-byte grid
-// is realigned in registers (each destination vector is funnel-shifted from
-// two source vectors, the second taken from the neighbour lane); the pack's
-// fp32-widening copy falls back to lane-contiguous element accesses there
-// (still coalesced: 64 lanes touch 64 consecutive elements). Every access lies
-// inside the parameter's own [0, numel) range, inside the flat or gather
-// buffer, or inside the shard.
+// or the rank-major gather buffer -- in chunks, one chunk per workgroup
+// iteration. The workgroup finds the parameters that overlap its chunk by
+// binary search over the parameter offsets (the packs: 4-wave workgroups with
+// the offsets staged in LDS; the copy-outs: one-wave workgroups searching the
+// device table with wave-uniform scalar loads), then copies each overlap with
+// 16-byte vectors. A bf16 copy whose source and destination sit at different
+// offsets from the 16-byte grid is realigned in registers (each destination
+// vector is funnel-shifted from two source vectors, the second taken from the
+// neighbour lane), and the copy-outs move each chunk edge inside a piece to
+// the destination's 16-byte grid so that only a piece's own ends go element by
+// element; the pack's fp32-widening copy falls back to lane-contiguous element
+// accesses there (still coalesced: 64 lanes touch 64 consecutive elements).
+// Every access lies inside the parameter's own [0, numel) range, inside the
+// flat or gather buffer, or inside the shard.
 #include "zs_device.hpp"
 #include "zs_launch.hpp"
 
 namespace zs {
 namespace {
 
-constexpr int64_t kChunk = 8192;   // elements per workgroup iteration
+constexpr int64_t kChunk = 8192;   // elements per workgroup iteration (the packs)
+// The copy-outs run one-wave workgroups over short chunks: many small
+// workgroups keep more of the chip's memory pipeline busy than fewer large
+// ones (a plain 2 GiB bf16 copy: 83% of peak with one 16-byte vector per lane
+// and 1 KiB per workgroup, 77% with 256 lanes and 16 KiB), and in one wave the
+// chunk's first parameter is found without LDS or barriers. Measured against
+// 256 lanes over 8192 elements, in alternating rounds: the flat copy-out 2-4%
+// faster with 2048-element chunks (a 2 GiB parameter, the Llama-3-8B and 70B
+// blocks); the dim-0 copy-out 7% (Llama-3-8B block, N = 8), 12% (GPT-2,
+// N = 8) and 1% (GPT-2, N = 5) faster with 1024-element chunks.
+constexpr int kCopyBS = 64;
+constexpr int64_t kCopyChunk = 2048;
+constexpr int64_t kCopyDim0Chunk = 1024;
 constexpr int kLdsParams = 1024;   // offsets cached in LDS up to this many parameters
 // LDS reserved (beyond the offset table) by each pack workgroup: it holds the
 // write-heavy pack to 4 workgroups per CU, measured 3-11% faster than the 8
@@ -89,26 +104,26 @@ __device__ void seg_to_f32(const Src* __restrict__ src, float* __restrict__ dst,
 // wave loads it itself), then funnel-shifts the pair into one aligned store.
 // Each lane keeps 4 source vectors in flight: with one at a time the realigning
 // copy was bound by load latency.
-// The caller keeps every loaded vector inside the copied range: k_begin >= 1
-// and k_end <= nv - 1 for nv destination vectors, so sa[k_begin] starts after
-// the range's first element and sa[k_end] ends before its last.
-template <int SH>
+// The caller keeps every loaded vector, sa[k_begin] .. sa[k_end], inside
+// memory the copy may read: the copied range itself, or the same piece's
+// elements around it (see seg_bf16).
+template <int SH, int BS>
 __device__ void realign_bf16(const u32x4* __restrict__ sa, u32x4* __restrict__ da, int64_t k_begin,
                              int64_t k_end) {
   constexpr int q = SH / 2;          // whole 32-bit words to skip
   constexpr bool half = (SH & 1) != 0;  // plus one bf16
   constexpr int U = 4;               // source vectors in flight per lane
   const int lane = threadIdx.x & 63;
-  for (int64_t kb = k_begin; kb < k_end; kb += U * kThreads) {  // uniform across the workgroup
+  for (int64_t kb = k_begin; kb < k_end; kb += U * BS) {  // uniform across the workgroup
     u32x4 lo[U];
 #pragma unroll
     for (int j = 0; j < U; ++j) {
-      const int64_t k = kb + (int64_t)j * kThreads + threadIdx.x;
+      const int64_t k = kb + (int64_t)j * BS + threadIdx.x;
       lo[j] = k < k_end ? ld_nt(sa + k) : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int j = 0; j < U; ++j) {
-      const int64_t k = kb + (int64_t)j * kThreads + threadIdx.x;
+      const int64_t k = kb + (int64_t)j * BS + threadIdx.x;
       u32x4 hi;  // sa[k + 1]: the next lane's vector of the same round
       hi.x = __shfl_down(lo[j].x, 1, 64);
       hi.y = __shfl_down(lo[j].y, 1, 64);
@@ -131,50 +146,61 @@ __device__ void realign_bf16(const u32x4* __restrict__ sa, u32x4* __restrict__ d
 // loads before their stores (32 bytes in flight per lane instead of 16:
 // measured 2.5% faster for both copy-outs; four or more were no better, and
 // the fp32-widening copy above is fastest one vector at a time). Otherwise the
-// middle of the range goes through realign_bf16 and only the ends are copied
-// element by element.
+// destination vectors go through realign_bf16 and only the ends are copied
+// element by element. Destination vector k reads the aligned source vectors
+// that hold source elements head + 8k - sh .. head + 8k + 8; the first and the
+// last destination vectors need one that reaches up to 7 elements before or
+// after the range, which they read only when that stays inside the range or
+// the caller allows it: `lead` / `trail` promise that at least 8 elements of
+// the same piece precede src / follow src + len (an interior edge of a piece
+// that a workgroup's chunk cuts). Otherwise those two vectors go element by
+// element.
+template <int BS>
 __device__ void seg_bf16(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst,
-                         int64_t len) {
+                         int64_t len, bool lead = false, bool trail = false) {
   const uintptr_t da = reinterpret_cast<uintptr_t>(dst);
   int64_t head = (int64_t)(((16u - (da & 15u)) & 15u) / 2u);
   if (head > len) head = len;
   const int sh = (int)((reinterpret_cast<uintptr_t>(src + head) & 15u) / 2u);
   if (sh != 0) {
     const int64_t nv = (len - head) / 8;  // destination vectors
-    if (nv < 3) {
-      for (int64_t i = threadIdx.x; i < len; i += kThreads) dst[i] = src[i];
+    const int64_t kb = (lead || head >= sh) ? 0 : 1;                  // first realigned vector
+    const int64_t ke = (trail || len - head - 8 * nv >= 8 - sh) ? nv : nv - 1;  // one past the last
+    if (ke - kb < 1) {
+      for (int64_t i = threadIdx.x; i < len; i += BS) dst[i] = src[i];
       return;
     }
-    // element by element: the head and destination vector 0, then the last
-    // destination vector and the tail
-    const int64_t e0 = head + 8, e1 = head + 8 * (nv - 1);
-    for (int64_t i = threadIdx.x; i < e0; i += kThreads) dst[i] = src[i];
-    for (int64_t i = e1 + threadIdx.x; i < len; i += kThreads) dst[i] = src[i];
+    // element by element: the head (and destination vector 0 unless it is
+    // realigned), then the last destination vector unless it is realigned,
+    // and the tail
+    const int64_t e0 = head + 8 * kb, e1 = head + 8 * ke;
+    for (int64_t i = threadIdx.x; i < e0; i += BS) dst[i] = src[i];
+    for (int64_t i = e1 + threadIdx.x; i < len; i += BS) dst[i] = src[i];
     const u32x4* sa = reinterpret_cast<const u32x4*>(src + head - sh);
     u32x4* dv = reinterpret_cast<u32x4*>(dst + head);
     switch (sh) {
-      case 1: realign_bf16<1>(sa, dv, 1, nv - 1); break;
-      case 2: realign_bf16<2>(sa, dv, 1, nv - 1); break;
-      case 3: realign_bf16<3>(sa, dv, 1, nv - 1); break;
-      case 4: realign_bf16<4>(sa, dv, 1, nv - 1); break;
-      case 5: realign_bf16<5>(sa, dv, 1, nv - 1); break;
-      case 6: realign_bf16<6>(sa, dv, 1, nv - 1); break;
-      default: realign_bf16<7>(sa, dv, 1, nv - 1); break;
+      case 1: realign_bf16<1, BS>(sa, dv, kb, ke); break;
+      case 2: realign_bf16<2, BS>(sa, dv, kb, ke); break;
+      case 3: realign_bf16<3, BS>(sa, dv, kb, ke); break;
+      case 4: realign_bf16<4, BS>(sa, dv, kb, ke); break;
+      case 5: realign_bf16<5, BS>(sa, dv, kb, ke); break;
+      case 6: realign_bf16<6, BS>(sa, dv, kb, ke); break;
+      default: realign_bf16<7, BS>(sa, dv, kb, ke); break;
     }
     return;
   }
-  for (int64_t i = threadIdx.x; i < head; i += kThreads) dst[i] = src[i];
+  for (int64_t i = threadIdx.x; i < head; i += BS) dst[i] = src[i];
   const int64_t nv = (len - head) / 8;
   const u32x4* s = reinterpret_cast<const u32x4*>(src + head);
   u32x4* d = reinterpret_cast<u32x4*>(dst + head);
   int64_t i = threadIdx.x;
-  for (; i + kThreads < nv; i += 2 * kThreads) {
-    const u32x4 a = ld_nt(s + i), b = ld_nt(s + i + kThreads);
+  for (; i + BS < nv; i += 2 * BS) {
+    const u32x4 a = ld_nt(s + i), b = ld_nt(s + i + BS);
     st_nt(a, d + i);
-    st_nt(b, d + i + kThreads);
+    st_nt(b, d + i + BS);
   }
   if (i < nv) st_nt(ld_nt(s + i), d + i);
-  for (int64_t i = head + 8 * nv + threadIdx.x; i < len; i += kThreads) dst[i] = src[i];
+  for (int64_t i = head + 8 * nv + threadIdx.x; i < len; i += BS) dst[i] = src[i];
 }
 
 __device__ void zero_f32(float* __restrict__ p, int64_t len) {
@@ -188,11 +214,12 @@ __device__ void zero_f32(float* __restrict__ p, int64_t len) {
   for (int64_t i = head + 4 * nv + threadIdx.x; i < len; i += kThreads) p[i] = 0.0f;
 }
 
-// Stage parameter offsets in LDS when the table fits.
+// Stage parameter offsets in LDS when the table fits (BS: the workgroup size).
+template <int BS = kThreads>
 __device__ bool stage_offsets(int64_t* off_lds, const zs_param_desc* desc, int nparams) {
   const bool use = nparams <= kLdsParams;
   if (use)
-    for (int i = threadIdx.x; i < nparams; i += kThreads) off_lds[i] = desc[i].flat_offset;
+    for (int i = threadIdx.x; i < nparams; i += BS) off_lds[i] = desc[i].flat_offset;
   __syncthreads();
   return use;
 }
@@ -239,21 +266,76 @@ __global__ __launch_bounds__(kThreads) void k_pack(const zs_param_desc* __restri
   }
 }
 
-__global__ __launch_bounds__(kThreads) void k_copy_out(const uint16_t* __restrict__ gathered,
-                                                       const zs_param_desc* __restrict__ desc,
-                                                       int nparams, int64_t total) {
-  __shared__ int64_t off_lds[kLdsParams];
-  const bool use_lds = stage_offsets(off_lds, desc, nparams);
-  for (int64_t f0 = (int64_t)blockIdx.x * kChunk; f0 < total; f0 += (int64_t)gridDim.x * kChunk) {
-    const int64_t fe = f0 + kChunk < total ? f0 + kChunk : total;
-    int lo, hi;
-    chunk_params(off_lds, desc, nparams, use_lds, f0, fe, &lo, &hi);
-    for (int p = lo; p <= hi; ++p) {
-      const int64_t off = desc[p].flat_offset, cnt = desc[p].numel;
-      const int64_t a = f0 > off ? f0 : off;
-      const int64_t b = fe < off + cnt ? fe : off + cnt;
-      if (a >= b) continue;
-      seg_bf16(gathered + a, static_cast<uint16_t*>(desc[p].ptr) + (a - off), b - a);
+// An edge f of a workgroup's part of a piece n elements long (in the piece's
+// coordinates; destination element f at dst + f): an interior edge moves
+// forward to the next element whose destination lies on the 16-byte grid, at
+// most to n. The two workgroups that meet at f compute the same edge, so their
+// parts still tile the piece, and neither writes half of a destination vector
+// or copies elements one by one there.
+__device__ __forceinline__ int64_t dst_edge(const uint16_t* dst, int64_t f, int64_t n) {
+  if (f <= 0 || f >= n) return f;
+  const int64_t adv = (int64_t)(((16u - (reinterpret_cast<uintptr_t>(dst + f) & 15u)) & 15u) / 2u);
+  return f + adv < n ? f + adv : n;
+}
+
+// The part [a, b) (flat coordinates) of parameter p that a workgroup copies,
+// its edges moved by dst_edge.
+template <int BS>
+__device__ __forceinline__ void copy_param_part(const uint16_t* __restrict__ gathered,
+                                                const zs_param_desc& d, int64_t a, int64_t b) {
+  uint16_t* dp = static_cast<uint16_t*>(d.ptr);
+  const int64_t xa = dst_edge(dp, a - d.flat_offset, d.numel), xb = dst_edge(dp, b - d.flat_offset, d.numel);
+  if (xa < xb)
+    seg_bf16<BS>(gathered + d.flat_offset + xa, dp + xa, xb - xa, xa >= 8, d.numel - xb >= 8);
+}
+
+// Largest p with key(p) <= f, every lane computing the same search: in a
+// one-wave workgroup the indices are wave-uniform, so the table is read with
+// scalar loads and no LDS staging or barrier is needed.
+template <typename Key>
+__device__ __forceinline__ int find_uniform(int nparams, int64_t f, Key key) {
+  int lo = 0, hi = nparams - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (key(mid) <= f) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+// BS lanes copy chunks of CH elements of the flat range. One-wave workgroups
+// (BS == 64) find the chunk's first parameter by a wave-uniform search and walk
+// forward; larger ones stage the offsets in LDS and search behind barriers.
+template <int BS, int64_t CH>
+__global__ __launch_bounds__(BS) void k_copy_out(const uint16_t* __restrict__ gathered,
+                                                 const zs_param_desc* __restrict__ desc,
+                                                 int nparams, int64_t total) {
+  if constexpr (BS == 64) {
+    for (int64_t f0 = (int64_t)blockIdx.x * CH; f0 < total; f0 += (int64_t)gridDim.x * CH) {
+      const int64_t fe = f0 + CH < total ? f0 + CH : total;
+      const int lo = find_uniform(nparams, f0, [&](int i) { return desc[i].flat_offset; });
+      for (int p = lo; p < nparams; ++p) {
+        const zs_param_desc d = desc[p];
+        if (d.flat_offset >= fe) break;
+        const int64_t a = f0 > d.flat_offset ? f0 : d.flat_offset;
+        const int64_t b = fe < d.flat_offset + d.numel ? fe : d.flat_offset + d.numel;
+        if (a < b) copy_param_part<BS>(gathered, d, a, b);
+      }
+    }
+  } else {
+    static_assert(BS >= 128, "chunk_params searches on threads 0 and 64");
+    __shared__ int64_t off_lds[kLdsParams];
+    const bool use_lds = stage_offsets<BS>(off_lds, desc, nparams);
+    for (int64_t f0 = (int64_t)blockIdx.x * CH; f0 < total; f0 += (int64_t)gridDim.x * CH) {
+      const int64_t fe = f0 + CH < total ? f0 + CH : total;
+      int lo, hi;
+      chunk_params(off_lds, desc, nparams, use_lds, f0, fe, &lo, &hi);
+      for (int p = lo; p <= hi; ++p) {
+        const zs_param_desc d = desc[p];
+        const int64_t a = f0 > d.flat_offset ? f0 : d.flat_offset;
+        const int64_t b = fe < d.flat_offset + d.numel ? fe : d.flat_offset + d.numel;
+        if (a < b) copy_param_part<BS>(gathered, d, a, b);
+      }
     }
   }
 }
@@ -323,43 +405,65 @@ __global__ __launch_bounds__(kThreads) void k_pack_dim0(const zs_dim0_desc* __re
 // parameters in order instead reads N windows at once and measured 2-9%
 // slower) and scatter each piece -- rank r's part of one parameter's chunk --
 // to that parameter's rows [r*c, r*c + valid). Padding rows are not copied.
-__global__ __launch_bounds__(kThreads) void k_copy_out_dim0(const uint16_t* __restrict__ gathered,
-                                                            const zs_dim0_desc* __restrict__ desc,
-                                                            int nparams, int world,
-                                                            int64_t local_total) {
-  __shared__ int64_t key[kLdsParams];
-  __shared__ int s_lo, s_hi;
-  const bool use_lds = nparams <= kLdsParams;
-  if (use_lds)
-    for (int i = threadIdx.x; i < nparams; i += kThreads) key[i] = desc[i].local_offset;
-  __syncthreads();
-  auto lkey = [&](int i) { return desc[i].local_offset; };
+// Workgroup shapes as in k_copy_out.
+template <int BS, int64_t CH>
+__global__ __launch_bounds__(BS) void k_copy_out_dim0(const uint16_t* __restrict__ gathered,
+                                                      const zs_dim0_desc* __restrict__ desc,
+                                                      int nparams, int world,
+                                                      int64_t local_total) {
+  auto piece = [&](int p, int64_t r, int64_t j0, int64_t j1) {  // rank r's [j0, j1) of parameter p
+    const zs_dim0_desc d = desc[p];
+    const int64_t a = j0 > d.local_offset ? j0 : d.local_offset;
+    const int64_t b = j1 < d.local_offset + d.chunk ? j1 : d.local_offset + d.chunk;
+    if (a >= b) return;
+    const int64_t ja = a - d.local_offset, jb = b - d.local_offset;  // within the chunk
+    const int64_t val = valid_part(d, (int)r);
+    const int64_t je = jb < val ? jb : val;  // real rows end
+    if (ja >= je) return;
+    uint16_t* dp = static_cast<uint16_t*>(d.ptr) + r * d.chunk;  // the piece: val elements
+    const int64_t xa = dst_edge(dp, ja, val), xb = dst_edge(dp, je, val);
+    if (xa < xb)
+      seg_bf16<BS>(gathered + r * local_total + d.local_offset + xa, dp + xa, xb - xa, xa >= 8,
+                   val - xb >= 8);
+  };
   const int64_t src_total = (int64_t)world * local_total;
-  for (int64_t g0 = (int64_t)blockIdx.x * kChunk; g0 < src_total; g0 += (int64_t)gridDim.x * kChunk) {
-    const int64_t ge = g0 + kChunk < src_total ? g0 + kChunk : src_total;
-    int64_t gp = g0;
-    while (gp < ge) {  // the chunk's pieces inside one rank's shard (uniform loop)
-      const int64_t r = gp / local_total;
-      const int64_t rend = (r + 1) * local_total < ge ? (r + 1) * local_total : ge;
-      const int64_t j0 = gp - r * local_total, j1 = rend - r * local_total;
-      if (threadIdx.x == 0) s_lo = find_by(key, use_lds, nparams, j0, lkey);
-      if (threadIdx.x == 64) s_hi = find_by(key, use_lds, nparams, j1 - 1, lkey);
-      __syncthreads();
-      const int lo = __builtin_amdgcn_readfirstlane(s_lo), hi = __builtin_amdgcn_readfirstlane(s_hi);
-      __syncthreads();
-      for (int p = lo; p <= hi; ++p) {
-        const zs_dim0_desc d = desc[p];
-        const int64_t a = j0 > d.local_offset ? j0 : d.local_offset;
-        const int64_t b = j1 < d.local_offset + d.chunk ? j1 : d.local_offset + d.chunk;
-        if (a >= b) continue;
-        const int64_t ja = a - d.local_offset, jb = b - d.local_offset;  // within the chunk
-        const int64_t val = valid_part(d, (int)r);
-        const int64_t je = jb < val ? jb : val;  // real rows end
-        if (ja < je)
-          seg_bf16(gathered + r * local_total + a, static_cast<uint16_t*>(d.ptr) + r * d.chunk + ja,
-                   je - ja);
+  if constexpr (BS == 64) {
+    auto lkey = [&](int i) { return desc[i].local_offset; };
+    for (int64_t g0 = (int64_t)blockIdx.x * CH; g0 < src_total; g0 += (int64_t)gridDim.x * CH) {
+      const int64_t ge = g0 + CH < src_total ? g0 + CH : src_total;
+      for (int64_t gp = g0; gp < ge;) {  // the chunk's pieces inside one rank's shard
+        const int64_t r = gp / local_total;
+        const int64_t rend = (r + 1) * local_total < ge ? (r + 1) * local_total : ge;
+        const int64_t j0 = gp - r * local_total, j1 = rend - r * local_total;
+        for (int p = find_uniform(nparams, j0, lkey); p < nparams && desc[p].local_offset < j1; ++p)
+          piece(p, r, j0, j1);
+        gp = rend;
       }
-      gp = rend;
+    }
+  } else {
+    static_assert(BS >= 128, "the piece search runs on threads 0 and 64");
+    __shared__ int64_t key[kLdsParams];
+    __shared__ int s_lo, s_hi;
+    const bool use_lds = nparams <= kLdsParams;
+    if (use_lds)
+      for (int i = threadIdx.x; i < nparams; i += BS) key[i] = desc[i].local_offset;
+    __syncthreads();
+    auto lkey = [&](int i) { return desc[i].local_offset; };
+    for (int64_t g0 = (int64_t)blockIdx.x * CH; g0 < src_total; g0 += (int64_t)gridDim.x * CH) {
+      const int64_t ge = g0 + CH < src_total ? g0 + CH : src_total;
+      int64_t gp = g0;
+      while (gp < ge) {  // the chunk's pieces inside one rank's shard (uniform loop)
+        const int64_t r = gp / local_total;
+        const int64_t rend = (r + 1) * local_total < ge ? (r + 1) * local_total : ge;
+        const int64_t j0 = gp - r * local_total, j1 = rend - r * local_total;
+        if (threadIdx.x == 0) s_lo = find_by(key, use_lds, nparams, j0, lkey);
+        if (threadIdx.x == 64) s_hi = find_by(key, use_lds, nparams, j1 - 1, lkey);
+        __syncthreads();
+        const int lo = __builtin_amdgcn_readfirstlane(s_lo), hi = __builtin_amdgcn_readfirstlane(s_hi);
+        __syncthreads();
+        for (int p = lo; p <= hi; ++p) piece(p, r, j0, j1);
+        gp = rend;
+      }
     }
   }
 }
@@ -396,16 +500,20 @@ hipError_t launch_pack_dim0(const zs_dim0_desc* d_desc, int nparams, int src_dty
 hipError_t launch_copy_out_dim0(const uint16_t* gathered, const zs_dim0_desc* d_desc, int nparams,
                                 int world, int64_t total, int64_t local_total, hipStream_t s) {
   if (total == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_copy_out_dim0, dim3((unsigned)chunk_grid((int64_t)world * local_total)),
-                     dim3(kThreads), 0, s, gathered, d_desc, nparams, world, local_total);
+  constexpr int BS = kCopyBS;
+  constexpr int64_t CH = kCopyDim0Chunk;
+  hipLaunchKernelGGL((k_copy_out_dim0<BS, CH>), dim3((unsigned)grid_for((int64_t)world * local_total, CH, BS)),
+                     dim3(BS), 0, s, gathered, d_desc, nparams, world, local_total);
   return hipGetLastError();
 }
 
 hipError_t launch_copy_out(const uint16_t* gathered, const zs_param_desc* d_desc, int nparams,
                            int64_t total, hipStream_t s) {
   if (total == 0 || nparams == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_copy_out, dim3((unsigned)chunk_grid(total)), dim3(kThreads), 0, s, gathered,
-                     d_desc, nparams, total);
+  constexpr int BS = kCopyBS;
+  constexpr int64_t CH = kCopyChunk;
+  hipLaunchKernelGGL((k_copy_out<BS, CH>), dim3((unsigned)grid_for(total, CH, BS)), dim3(BS), 0, s,
+                     gathered, d_desc, nparams, total);
   return hipGetLastError();
 }
 
