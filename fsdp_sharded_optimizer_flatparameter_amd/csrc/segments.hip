@@ -14,10 +14,10 @@
 // Every kernel walks a contiguous range -- the flat buffer, the rank's shard,
 // or the rank-major gather buffer -- in chunks, one chunk per workgroup
 // iteration. The workgroup finds the parameters that overlap its chunk by
-// binary search over the parameter offsets (the packs: 4-wave workgroups with
-// the offsets staged in LDS; the copy-outs: one-wave workgroups searching the
-// device table with wave-uniform scalar loads), then copies each overlap with
-// 16-byte vectors. A bf16 copy whose source and destination sit at different
+// binary search over the parameter offsets -- one-wave workgroups search the
+// device table with wave-uniform scalar loads; wider ones, which every kernel
+// can also be built for, stage the offsets in LDS -- then copies each overlap
+// with 16-byte vectors. A bf16 copy whose source and destination sit at different
 // offsets from the 16-byte grid is realigned in registers (each destination
 // vector is funnel-shifted from two source vectors, the second taken from the
 // neighbour lane), and the copy-outs move each chunk edge inside a piece to
@@ -32,7 +32,6 @@
 namespace zs {
 namespace {
 
-constexpr int64_t kChunk = 8192;   // elements per workgroup iteration (the packs)
 // The copy-outs run one-wave workgroups over short chunks: many small
 // workgroups keep more of the chip's memory pipeline busy than fewer large
 // ones (a plain 2 GiB bf16 copy: 83% of peak with one 16-byte vector per lane
@@ -46,10 +45,17 @@ constexpr int kCopyBS = 64;
 constexpr int64_t kCopyChunk = 2048;
 constexpr int64_t kCopyDim0Chunk = 1024;
 constexpr int kLdsParams = 1024;   // offsets cached in LDS up to this many parameters
-// LDS reserved (beyond the offset table) by each pack workgroup: it holds the
-// write-heavy pack to 4 workgroups per CU, measured 3-11% faster than the 8
-// that fit otherwise. The copy-outs keep full residency (capping them was slower).
-constexpr unsigned kPackLds = 32768;
+// The packs take one-wave workgroups as well (fp32 writes, 12 of their 16
+// bytes per element). The flat pack works 1024-element chunks under a 12 KiB
+// LDS reservation that holds it to 13 workgroups per CU: 6% faster than 256
+// lanes over 8192 elements with 4 workgroups per CU on the 7.5B shard, 8% on
+// GPT-2's shard at N = 5. The dim-0 pack works 256-element chunks at full
+// residency: 13% faster on the Llama-3-8B block at N = 8 and on the 70B block
+// at N = 64.
+constexpr int kPackBS = 64;
+constexpr int64_t kPackChunk = 1024;
+constexpr unsigned kPackLds = 12288;
+constexpr int64_t kPackDim0Chunk = 256;
 
 // Largest p with off[p] <= f (off ascending, off[0] == 0 <= f).
 __device__ __forceinline__ int find_param(const int64_t* off_lds, const zs_param_desc* desc,
@@ -77,23 +83,23 @@ __device__ __forceinline__ f32x4 load4(const uint16_t* p) {
 }
 
 // Workgroup-cooperative copy of len elements src -> dst (fp32 destination).
-template <typename Src>
+template <typename Src, int BS = kThreads>
 __device__ void seg_to_f32(const Src* __restrict__ src, float* __restrict__ dst, int64_t len) {
   const uintptr_t da = reinterpret_cast<uintptr_t>(dst);
   int64_t head = (int64_t)(((16u - (da & 15u)) & 15u) / 4u);
   if (head > len) head = len;
   const bool vec = (reinterpret_cast<uintptr_t>(src + head) & (4 * sizeof(Src) - 1)) == 0;
   if (!vec) {
-    for (int64_t i = threadIdx.x; i < len; i += kThreads) dst[i] = widen(src[i]);
+    for (int64_t i = threadIdx.x; i < len; i += BS) dst[i] = widen(src[i]);
     return;
   }
-  for (int64_t i = threadIdx.x; i < head; i += kThreads) dst[i] = widen(src[i]);
+  for (int64_t i = threadIdx.x; i < head; i += BS) dst[i] = widen(src[i]);
   const int64_t nv = (len - head) / 4;
   const Src* s = src + head;
   float* d = dst + head;
-  for (int64_t i = threadIdx.x; i < nv; i += kThreads)
+  for (int64_t i = threadIdx.x; i < nv; i += BS)
     st_nt(load4(s + 4 * i), reinterpret_cast<f32x4*>(d + 4 * i));
-  for (int64_t i = head + 4 * nv + threadIdx.x; i < len; i += kThreads) dst[i] = widen(src[i]);
+  for (int64_t i = head + 4 * nv + threadIdx.x; i < len; i += BS) dst[i] = widen(src[i]);
 }
 
 // Destination vectors [k_begin, k_end) of a bf16 copy whose source runs SH
@@ -203,15 +209,16 @@ __device__ void seg_bf16(const uint16_t* __restrict__ src, uint16_t* __restrict_
   for (int64_t i = head + 8 * nv + threadIdx.x; i < len; i += BS) dst[i] = src[i];
 }
 
+template <int BS = kThreads>
 __device__ void zero_f32(float* __restrict__ p, int64_t len) {
   const uintptr_t a = reinterpret_cast<uintptr_t>(p);
   int64_t head = (int64_t)(((16u - (a & 15u)) & 15u) / 4u);
   if (head > len) head = len;
-  for (int64_t i = threadIdx.x; i < head; i += kThreads) p[i] = 0.0f;
+  for (int64_t i = threadIdx.x; i < head; i += BS) p[i] = 0.0f;
   const int64_t nv = (len - head) / 4;
   f32x4* d = reinterpret_cast<f32x4*>(p + head);
-  for (int64_t i = threadIdx.x; i < nv; i += kThreads) st_nt(f32x4{0.f, 0.f, 0.f, 0.f}, d + i);
-  for (int64_t i = head + 4 * nv + threadIdx.x; i < len; i += kThreads) p[i] = 0.0f;
+  for (int64_t i = threadIdx.x; i < nv; i += BS) st_nt(f32x4{0.f, 0.f, 0.f, 0.f}, d + i);
+  for (int64_t i = head + 4 * nv + threadIdx.x; i < len; i += BS) p[i] = 0.0f;
 }
 
 // Stage parameter offsets in LDS when the table fits (BS: the workgroup size).
@@ -236,33 +243,59 @@ __device__ void chunk_params(const int64_t* off_lds, const zs_param_desc* desc, 
   __syncthreads();  // s_lo / s_hi are rewritten by the next chunk
 }
 
-template <typename Src>
-__global__ __launch_bounds__(kThreads) void k_pack(const zs_param_desc* __restrict__ desc,
-                                                   int nparams, int64_t total, int64_t flat_begin,
-                                                   int64_t shard, float* __restrict__ master,
-                                                   float* __restrict__ m, float* __restrict__ v) {
-  __shared__ int64_t off_lds[kLdsParams];
-  const bool use_lds = nparams > 0 ? stage_offsets(off_lds, desc, nparams) : false;
-  for (int64_t k0 = (int64_t)blockIdx.x * kChunk; k0 < shard; k0 += (int64_t)gridDim.x * kChunk) {
-    const int64_t k1 = k0 + kChunk < shard ? k0 + kChunk : shard;
+// Largest p with key(p) <= f, every lane computing the same search: in a
+// one-wave workgroup the indices are wave-uniform, so the table is read with
+// scalar loads and no LDS staging or barrier is needed.
+template <typename Key>
+__device__ __forceinline__ int find_uniform(int nparams, int64_t f, Key key) {
+  int lo = 0, hi = nparams - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (key(mid) <= f) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+// The rank's slice [flat_begin, flat_begin + shard) of the padded flat unit,
+// CH elements per workgroup iteration. One-wave workgroups (BS == 64) find the
+// chunk's first parameter by a wave-uniform search (find_uniform); larger ones
+// stage the offsets in LDS.
+template <typename Src, int BS, int64_t CH>
+__global__ __launch_bounds__(BS) void k_pack(const zs_param_desc* __restrict__ desc,
+                                             int nparams, int64_t total, int64_t flat_begin,
+                                             int64_t shard, float* __restrict__ master,
+                                             float* __restrict__ m, float* __restrict__ v) {
+  [[maybe_unused]] __shared__ int64_t off_lds[BS == 64 ? 1 : kLdsParams];
+  bool use_lds = false;
+  if constexpr (BS != 64) use_lds = nparams > 0 ? stage_offsets<BS>(off_lds, desc, nparams) : false;
+  for (int64_t k0 = (int64_t)blockIdx.x * CH; k0 < shard; k0 += (int64_t)gridDim.x * CH) {
+    const int64_t k1 = k0 + CH < shard ? k0 + CH : shard;
     const int64_t f0 = flat_begin + k0, f1 = flat_begin + k1;
     const int64_t fe = f1 < total ? f1 : total;  // end of real data inside the chunk
-    if (m) zero_f32(m + k0, k1 - k0);
-    if (v) zero_f32(v + k0, k1 - k0);
+    if (m) zero_f32<BS>(m + k0, k1 - k0);
+    if (v) zero_f32<BS>(v + k0, k1 - k0);
+    auto part = [&](int p) {
+      const int64_t off = desc[p].flat_offset, cnt = desc[p].numel;
+      const int64_t a = f0 > off ? f0 : off;
+      const int64_t b = fe < off + cnt ? fe : off + cnt;
+      if (a >= b) return;
+      const Src* src = static_cast<const Src*>(desc[p].ptr) + (a - off);
+      seg_to_f32<Src, BS>(src, master + (a - flat_begin), b - a);
+    };
     if (f0 < fe) {
-      int lo, hi;
-      chunk_params(off_lds, desc, nparams, use_lds, f0, fe, &lo, &hi);
-      for (int p = lo; p <= hi; ++p) {
-        const int64_t off = desc[p].flat_offset, cnt = desc[p].numel;
-        const int64_t a = f0 > off ? f0 : off;
-        const int64_t b = fe < off + cnt ? fe : off + cnt;
-        if (a >= b) continue;
-        const Src* src = static_cast<const Src*>(desc[p].ptr) + (a - off);
-        seg_to_f32<Src>(src, master + (a - flat_begin), b - a);
+      if constexpr (BS == 64) {
+        for (int p = find_uniform(nparams, f0, [&](int i) { return desc[i].flat_offset; });
+             p < nparams && desc[p].flat_offset < fe; ++p)
+          part(p);
+      } else {
+        int lo, hi;
+        chunk_params(off_lds, desc, nparams, use_lds, f0, fe, &lo, &hi);
+        for (int p = lo; p <= hi; ++p) part(p);
       }
     }
     const int64_t z0 = f0 > total ? f0 : total;  // tail padding -> +0.0
-    if (z0 < f1) zero_f32(master + (z0 - flat_begin), f1 - z0);
+    if (z0 < f1) zero_f32<BS>(master + (z0 - flat_begin), f1 - z0);
   }
 }
 
@@ -287,20 +320,6 @@ __device__ __forceinline__ void copy_param_part(const uint16_t* __restrict__ gat
   const int64_t xa = dst_edge(dp, a - d.flat_offset, d.numel), xb = dst_edge(dp, b - d.flat_offset, d.numel);
   if (xa < xb)
     seg_bf16<BS>(gathered + d.flat_offset + xa, dp + xa, xb - xa, xa >= 8, d.numel - xb >= 8);
-}
-
-// Largest p with key(p) <= f, every lane computing the same search: in a
-// one-wave workgroup the indices are wave-uniform, so the table is read with
-// scalar loads and no LDS staging or barrier is needed.
-template <typename Key>
-__device__ __forceinline__ int find_uniform(int nparams, int64_t f, Key key) {
-  int lo = 0, hi = nparams - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (key(mid) <= f) lo = mid;
-    else hi = mid - 1;
-  }
-  return lo;
 }
 
 // BS lanes copy chunks of CH elements of the flat range. One-wave workgroups
@@ -362,40 +381,50 @@ __device__ __forceinline__ int64_t valid_part(const zs_dim0_desc& d, int rank) {
 }
 
 // Rank r's shard: for each parameter its rows [r*c, (r+1)*c), zero past dim 0.
-template <typename Src>
-__global__ __launch_bounds__(kThreads) void k_pack_dim0(const zs_dim0_desc* __restrict__ desc,
-                                                        int nparams, int rank, int64_t local_total,
-                                                        float* __restrict__ master,
-                                                        float* __restrict__ m,
-                                                        float* __restrict__ v) {
-  __shared__ int64_t key[kLdsParams];
-  __shared__ int s_lo, s_hi;
-  const bool use_lds = nparams <= kLdsParams;
-  if (use_lds)
-    for (int i = threadIdx.x; i < nparams; i += kThreads) key[i] = desc[i].local_offset;
-  __syncthreads();
+// Workgroup shapes as in k_pack.
+template <typename Src, int BS, int64_t CH>
+__global__ __launch_bounds__(BS) void k_pack_dim0(const zs_dim0_desc* __restrict__ desc,
+                                                  int nparams, int rank, int64_t local_total,
+                                                  float* __restrict__ master,
+                                                  float* __restrict__ m,
+                                                  float* __restrict__ v) {
   auto lkey = [&](int i) { return desc[i].local_offset; };
-  for (int64_t k0 = (int64_t)blockIdx.x * kChunk; k0 < local_total; k0 += (int64_t)gridDim.x * kChunk) {
-    const int64_t k1 = k0 + kChunk < local_total ? k0 + kChunk : local_total;
-    if (m) zero_f32(m + k0, k1 - k0);
-    if (v) zero_f32(v + k0, k1 - k0);
-    if (threadIdx.x == 0) s_lo = find_by(key, use_lds, nparams, k0, lkey);
-    if (threadIdx.x == 64) s_hi = find_by(key, use_lds, nparams, k1 - 1, lkey);
+  [[maybe_unused]] __shared__ int64_t key[BS == 64 ? 1 : kLdsParams];
+  [[maybe_unused]] __shared__ int s_lo, s_hi;
+  const bool use_lds = BS != 64 && nparams <= kLdsParams;
+  if constexpr (BS != 64) {
+    if (use_lds)
+      for (int i = threadIdx.x; i < nparams; i += BS) key[i] = desc[i].local_offset;
     __syncthreads();
-    const int lo = __builtin_amdgcn_readfirstlane(s_lo), hi = __builtin_amdgcn_readfirstlane(s_hi);
-    __syncthreads();
-    for (int p = lo; p <= hi; ++p) {
+  }
+  for (int64_t k0 = (int64_t)blockIdx.x * CH; k0 < local_total; k0 += (int64_t)gridDim.x * CH) {
+    const int64_t k1 = k0 + CH < local_total ? k0 + CH : local_total;
+    if (m) zero_f32<BS>(m + k0, k1 - k0);
+    if (v) zero_f32<BS>(v + k0, k1 - k0);
+    auto part = [&](int p) {
       const zs_dim0_desc d = desc[p];
       const int64_t a = k0 > d.local_offset ? k0 : d.local_offset;
       const int64_t b = k1 < d.local_offset + d.chunk ? k1 : d.local_offset + d.chunk;
-      if (a >= b) continue;
+      if (a >= b) return;
       const int64_t ja = a - d.local_offset, jb = b - d.local_offset;  // within the chunk
       const int64_t val = valid_part(d, rank);
       const int64_t je = jb < val ? jb : val;  // real rows end
       if (ja < je)
-        seg_to_f32<Src>(static_cast<const Src*>(d.ptr) + (int64_t)rank * d.chunk + ja, master + a, je - ja);
+        seg_to_f32<Src, BS>(static_cast<const Src*>(d.ptr) + (int64_t)rank * d.chunk + ja, master + a,
+                            je - ja);
       const int64_t z0 = ja > val ? ja : val;  // padding rows
-      if (z0 < jb) zero_f32(master + d.local_offset + z0, jb - z0);
+      if (z0 < jb) zero_f32<BS>(master + d.local_offset + z0, jb - z0);
+    };
+    if constexpr (BS == 64) {
+      for (int p = find_uniform(nparams, k0, lkey); p < nparams && desc[p].local_offset < k1; ++p) part(p);
+    } else {
+      static_assert(BS >= 128, "the piece search runs on threads 0 and 64");
+      if (threadIdx.x == 0) s_lo = find_by(key, use_lds, nparams, k0, lkey);
+      if (threadIdx.x == 64) s_hi = find_by(key, use_lds, nparams, k1 - 1, lkey);
+      __syncthreads();
+      const int lo = __builtin_amdgcn_readfirstlane(s_lo), hi = __builtin_amdgcn_readfirstlane(s_hi);
+      __syncthreads();
+      for (int p = lo; p <= hi; ++p) part(p);
     }
   }
 }
@@ -468,32 +497,36 @@ __global__ __launch_bounds__(BS) void k_copy_out_dim0(const uint16_t* __restrict
   }
 }
 
-int64_t chunk_grid(int64_t elems) { return grid_for(elems, kChunk); }
-
 }  // namespace
 
 hipError_t launch_pack(const zs_param_desc* d_desc, int nparams, int64_t total, int src_dtype,
                        int64_t flat_begin, int64_t shard, float* master, float* m, float* v,
                        hipStream_t s) {
   if (shard == 0) return hipSuccess;
-  const dim3 gd((unsigned)chunk_grid(shard)), bd(kThreads);
+  constexpr int BS = kPackBS;
+  constexpr int64_t CH = kPackChunk;
+  const dim3 gd((unsigned)grid_for(shard, CH, BS)), bd(BS);
   if (src_dtype == ZS_BF16)
-    hipLaunchKernelGGL((k_pack<uint16_t>), gd, bd, kPackLds, s, d_desc, nparams, total, flat_begin,
-                       shard, master, m, v);
+    hipLaunchKernelGGL((k_pack<uint16_t, BS, CH>), gd, bd, kPackLds, s, d_desc, nparams, total,
+                       flat_begin, shard, master, m, v);
   else
-    hipLaunchKernelGGL((k_pack<float>), gd, bd, kPackLds, s, d_desc, nparams, total, flat_begin,
-                       shard, master, m, v);
+    hipLaunchKernelGGL((k_pack<float, BS, CH>), gd, bd, kPackLds, s, d_desc, nparams, total,
+                       flat_begin, shard, master, m, v);
   return hipGetLastError();
 }
 
 hipError_t launch_pack_dim0(const zs_dim0_desc* d_desc, int nparams, int src_dtype, int rank,
                             int64_t local_total, float* master, float* m, float* v, hipStream_t s) {
   if (local_total == 0) return hipSuccess;
-  const dim3 gd((unsigned)chunk_grid(local_total)), bd(kThreads);
+  constexpr int BS = kPackBS;
+  constexpr int64_t CH = kPackDim0Chunk;
+  const dim3 gd((unsigned)grid_for(local_total, CH, BS)), bd(BS);
   if (src_dtype == ZS_BF16)
-    hipLaunchKernelGGL((k_pack_dim0<uint16_t>), gd, bd, 0, s, d_desc, nparams, rank, local_total, master, m, v);
+    hipLaunchKernelGGL((k_pack_dim0<uint16_t, BS, CH>), gd, bd, 0, s, d_desc, nparams, rank,
+                       local_total, master, m, v);
   else
-    hipLaunchKernelGGL((k_pack_dim0<float>), gd, bd, 0, s, d_desc, nparams, rank, local_total, master, m, v);
+    hipLaunchKernelGGL((k_pack_dim0<float, BS, CH>), gd, bd, 0, s, d_desc, nparams, rank,
+                       local_total, master, m, v);
   return hipGetLastError();
 }
 
