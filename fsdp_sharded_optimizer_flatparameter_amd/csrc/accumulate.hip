@@ -152,15 +152,14 @@ __global__ __launch_bounds__(kThreads) void k_accum_scalar(RowTable<ZS_MAX_WORLD
   }
 }
 
-template <typename In, bool FIRST>
-__global__ __launch_bounds__(kThreads) void k_accum_local(const In* __restrict__ g, int64_t ngroups,
-                                                          int64_t n, float* __restrict__ acc,
-                                                          int vec) {
+template <typename In, bool FIRST, int BS = kThreads>
+__global__ __launch_bounds__(BS) void k_accum_local(const In* __restrict__ g, int64_t ngroups,
+                                                    int64_t n, float* __restrict__ acc, int vec) {
   using L = Lanes<In>;
   using Vec = typename L::Vec;
   if (vec) {
-    for (int64_t q = (int64_t)blockIdx.x * kThreads + threadIdx.x; q < ngroups;
-         q += (int64_t)gridDim.x * kThreads) {
+    for (int64_t q = (int64_t)blockIdx.x * BS + threadIdx.x; q < ngroups;
+         q += (int64_t)gridDim.x * BS) {
       const Vec w = ld_nt(reinterpret_cast<const Vec*>(g) + q);
       float x[4] = {-0.0f, -0.0f, -0.0f, -0.0f};
       L::add(w, x);  // -0 + g == g exactly: the widened gradient
@@ -175,8 +174,8 @@ __global__ __launch_bounds__(kThreads) void k_accum_local(const In* __restrict__
     }
   }
   const int64_t start = vec ? ngroups * 4 : 0;
-  for (int64_t i = start + (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n;
-       i += (int64_t)gridDim.x * kThreads) {
+  for (int64_t i = start + (int64_t)blockIdx.x * BS + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * BS) {
     const float x = L::scalar(g, i);
     acc[i] = FIRST ? x : acc[i] + x;
   }
@@ -292,13 +291,17 @@ hipError_t launch_accumulate_local(const void* g, int dtype, int64_t n, float* a
   if (n == 0) return hipSuccess;
   const bool vec = aligned_to(acc, 16) && aligned_to(g, dtype == ZS_BF16 ? 8 : 16);
   const int64_t ngroups = n / 4;
-  const dim3 gd((unsigned)grid_for(vec ? ngroups : n, kThreads)), bd(kThreads);
+  // one-wave workgroups, one 4-element group per lane, full residency: 4.5%
+  // faster than 4-wave workgroups on the 7.5B shard's size (a 12 KiB or 32 KiB
+  // reservation, or two groups per lane, were slower)
+  constexpr int BS = 64;
+  const dim3 gd((unsigned)grid_for(vec ? ngroups : n, BS, BS)), bd(BS);
   if (dtype == ZS_BF16) {
-    if (first) hipLaunchKernelGGL((k_accum_local<uint16_t, true>), gd, bd, 0, s, static_cast<const uint16_t*>(g), ngroups, n, acc, (int)vec);
-    else hipLaunchKernelGGL((k_accum_local<uint16_t, false>), gd, bd, 0, s, static_cast<const uint16_t*>(g), ngroups, n, acc, (int)vec);
+    if (first) hipLaunchKernelGGL((k_accum_local<uint16_t, true, BS>), gd, bd, 0, s, static_cast<const uint16_t*>(g), ngroups, n, acc, (int)vec);
+    else hipLaunchKernelGGL((k_accum_local<uint16_t, false, BS>), gd, bd, 0, s, static_cast<const uint16_t*>(g), ngroups, n, acc, (int)vec);
   } else {
-    if (first) hipLaunchKernelGGL((k_accum_local<float, true>), gd, bd, 0, s, static_cast<const float*>(g), ngroups, n, acc, (int)vec);
-    else hipLaunchKernelGGL((k_accum_local<float, false>), gd, bd, 0, s, static_cast<const float*>(g), ngroups, n, acc, (int)vec);
+    if (first) hipLaunchKernelGGL((k_accum_local<float, true, BS>), gd, bd, 0, s, static_cast<const float*>(g), ngroups, n, acc, (int)vec);
+    else hipLaunchKernelGGL((k_accum_local<float, false, BS>), gd, bd, 0, s, static_cast<const float*>(g), ngroups, n, acc, (int)vec);
   }
   return hipGetLastError();
 }
