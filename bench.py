@@ -151,13 +151,14 @@ def alternating_ms(fns: dict, iters: int, stream, rounds: int = 5) -> dict:
     return {k: sorted(t)[len(t) // 2] for k, t in times.items()}
 
 
-def settle(step, seconds: float) -> int:
-    """Run `step` until `seconds` of wall time have passed (synchronising every
-    few steps); returns the number of steps run."""
+def settle(step, seconds: float, min_steps: int = 0) -> int:
+    """Run `step` until `seconds` of wall time have passed and at least
+    `min_steps` steps have run (synchronising every few steps); returns the
+    number of steps run."""
     import torch
 
     n, t0 = 0, time.perf_counter()
-    while time.perf_counter() - t0 < seconds:
+    while time.perf_counter() - t0 < seconds or n < min_steps:
         for _ in range(4):
             step(n)
             n += 1
@@ -580,6 +581,8 @@ def main() -> int:
     ap.add_argument("--workload", default="7p5b", choices=sorted(WORKLOADS))
     ap.add_argument("--settle-ms", type=float, default=300.0,
                     help="wall time the step runs before the W warm-up steps (device settle)")
+    ap.add_argument("--settle-steps", type=int, default=40,
+                    help="the least number of steps the settle runs, whatever its wall time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parts", action="store_true", help="time only the step")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -634,7 +637,7 @@ def run(args, cpu) -> int:
         del src, dst
 
     # ---- the step: settle, W warm-up steps, then exactly K timed steps
-    settle_steps = settle(sh["step"], args.settle_ms * 1e-3)
+    settle_steps = settle(sh["step"], args.settle_ms * 1e-3, args.settle_steps if args.settle_ms > 0 else 0)
     ms_step, spread = timed_steps(sh["step"], stream, args.warmup, args.steps)
     gelem = S / (ms_step * 1e-3) / 1e9
     fused_bpe = sh["fused_bpe"]
@@ -650,7 +653,7 @@ def run(args, cpu) -> int:
     llama_entry = None
     if args.workload == "7p5b" and not args.no_parts and not args.calibrate_copy:
         ll = make_shard("llama8b", dev)
-        settle(ll["step"], args.settle_ms * 1e-3)
+        settle(ll["step"], args.settle_ms * 1e-3, args.settle_steps if args.settle_ms > 0 else 0)
         ms_ll, spread_ll = timed_steps(ll["step"], stream, args.warmup, args.steps)
         llama_entry = gbs_entry(ms_ll, ll["fused_bpe"], ll["S"], kernel=kernel_name,
                                 workload=ll["wl"]["desc"],
