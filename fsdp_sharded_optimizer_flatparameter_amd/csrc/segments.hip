@@ -289,6 +289,7 @@ __global__ __launch_bounds__(BS) void k_pack(const zs_param_desc* __restrict__ d
              p < nparams && desc[p].flat_offset < fe; ++p)
           part(p);
       } else {
+        static_assert(BS >= 128, "chunk_params searches on threads 0 and 64");
         int lo, hi;
         chunk_params(off_lds, desc, nparams, use_lds, f0, fe, &lo, &hi);
         for (int p = lo; p <= hi; ++p) part(p);
