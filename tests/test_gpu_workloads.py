@@ -148,10 +148,12 @@ def _full_size_case(n, world, dtype, step, moments, slot_offset, seed, windows=6
     assert torch.equal(slot.view(torch.int16), fslot.view(torch.int16))
 
 
-@pytest.mark.parametrize("world", [8, 7, 5])
-def test_gpt2_shard_end_to_end_every_element(world):
+@pytest.mark.parametrize("world,align", [(8, 1), (7, 1), (5, 1), (7, 64), (5, 64)])
+def test_gpt2_shard_end_to_end_every_element(world, align):
     # GPT-2's 148 parameters (124,439,808 elements) as one FlatParameter over N
-    # ranks (tail pad 0, 4 and 2 elements). The last rank's shard, which holds
+    # ranks (tail pad 0, 4 and 2 elements; with slices rounded to 64 elements,
+    # which puts every rank's slot on a 128-byte line, 256 and 192). The last
+    # rank's shard, which holds
     # the pad when there is one, is packed from the parameters and takes two
     # single-pass steps from N bf16 contributions into its slot of the gather
     # buffer; the other ranks' slots are the cast of their packed shards; the
@@ -163,16 +165,16 @@ def test_gpt2_shard_end_to_end_every_element(world):
     params = [gen.device_normal(g0, shapes.numel(s), gen.THETA_SIGMA).reshape(s) for _, s in shp]
     params_h = [host(p).ravel() for p in params]
     table = zs.ParamTable(params)
-    _, total, padded, S = zs.zs_flat_layout([p.numel() for p in params], world)
+    _, total, padded, S = zs.zs_flat_layout([p.numel() for p in params], world, align)
     gather = torch.empty(padded, device="cuda", dtype=torch.bfloat16)
     for r in range(world - 1):
         t = torch.empty(S, device="cuda")
-        zs.zs_pack_shard(table, world, r, t)
+        zs.zs_pack_shard(table, world, r, t, align=align)
         zs.zs_cast_for_gather(t, gather[r * S:(r + 1) * S])
     th, m, v = (torch.empty(S, device="cuda") for _ in range(3))
-    zs.zs_pack_shard(table, world, rank, th, m, v)
+    zs.zs_pack_shard(table, world, rank, th, m, v, align=align)
     torch.cuda.synchronize()
-    want = olayout.pack_shard(params_h, world, rank)
+    want = olayout.pack_shard(params_h, world, rank, align)
     for got, w in zip((th, m, v), want):
         assert np.array_equal(bits32(host(got)), bits32(w))
     slot = gather[rank * S:(rank + 1) * S]
