@@ -12,6 +12,8 @@
 //   k_clip         coefficient = min(1, max_norm / (sqrt(sum of partials) + 1e-6))
 #include <cmath>
 
+#include <type_traits>
+
 #include "zs_device.hpp"
 #include "zs_launch.hpp"
 
@@ -31,83 +33,110 @@ template <int NW, int CAP, int G, int BS, typename In, bool SUMSQ, bool FIRST, b
           bool RM = false>
 __global__ __launch_bounds__(BS) void k_accum(RowTable<CAP> rows, int world, MeanDiv div,
                                                     float scale, int64_t ngroups, int64_t n,
-                                                    float* __restrict__ acc,
+                                                    TilePlan plan, float* __restrict__ acc,
                                                     double* __restrict__ partials) {
   using L = Lanes<In>;
   extern __shared__ f32x4 slot[];  // G * BS lane-private slots
   const int nw = NW > 0 ? NW : world;
-  const int64_t span = (int64_t)BS * G;
   double ss = 0.0;
-  for (int64_t base = (int64_t)blockIdx.x * span; base < ngroups; base += (int64_t)gridDim.x * span) {
-    if constexpr (RM) {
-      constexpr int C = sizeof(In) == 2 ? 4 : 2;
-      rank_sums_rank_major<In, C, G, CAP, BS>(rows, nw, base, ngroups, slot, [&](int k, const float* s) {
-        f32x4 u;
+  for (int64_t t = blockIdx.x; t < plan.count(); t += gridDim.x) {
+    int64_t base, end;  // the tile's groups; each lane takes ng of them (at most G)
+    plan.range(t, ngroups, &base, &end);
+    const int ng = G == 1 ? 1 : (int)((end - base + BS - 1) / BS);
+    // a full tile (ng == G) runs loops with compile-time trip counts
+    auto tile = [&](auto full) {
+      constexpr bool FULL = decltype(full)::value;
+      const int NG = FULL ? G : ng;
+      if constexpr (RM) {
+        constexpr int C = sizeof(In) == 2 ? 4 : 2;
+        rank_sums_rank_major<In, C, G, CAP, BS, FULL>(rows, nw, base, end, ng, slot, [&](int k, const float* s) {
+          f32x4 u;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          u[e] = div(s[e]);
-          if (SCALE) u[e] *= scale;
+          for (int e = 0; e < 4; ++e) {
+            u[e] = div(s[e]);
+            if (SCALE) u[e] *= scale;
+          }
+          slot[k * BS + threadIdx.x] = u;
+        });
+        auto qidx = [&](int k) { return base + (int64_t)k * BS + threadIdx.x; };
+        auto finish = [&](int k, const f32x4& prev) {
+          const int64_t qq = qidx(k);
+          if (qq >= end) return;
+          const f32x4 u = slot[k * BS + threadIdx.x];
+          f32x4 o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            o[e] = FIRST ? u[e] : prev[e] + u[e];
+            if (SUMSQ) ss = fma((double)o[e], (double)o[e], ss);
+          }
+          st_nt(o, reinterpret_cast<f32x4*>(acc) + qq);
+        };
+        auto prev_of = [&](int k) {
+          const int64_t q = qidx(k) < end ? qidx(k) : end - 1;
+          return ld_nt(reinterpret_cast<const f32x4*>(acc) + q);
+        };
+        if (FIRST) {
+#pragma unroll
+          for (int k = 0; k < G; ++k) finish(k, f32x4{0.f, 0.f, 0.f, 0.f});  // k >= ng: nothing
+        } else if constexpr (FULL) {
+          f32x4 p0 = prev_of(0), p1;
+#pragma unroll 1
+          for (int k = 0; k < G; k += 2) {
+            if (k + 1 < G) p1 = prev_of(k + 1);
+            finish(k, p0);
+            if (k + 1 >= G) break;
+            if (k + 2 < G) p0 = prev_of(k + 2);
+            finish(k + 1, p1);
+          }
+        } else {
+          // pairs whose two prefetches both exist, then the last one or two groups
+          f32x4 p0 = prev_of(0), p1;
+          int k = 0;
+#pragma unroll 1
+          for (; k + 2 < ng; k += 2) {
+            p1 = prev_of(k + 1);
+            finish(k, p0);
+            p0 = prev_of(k + 2);
+            finish(k + 1, p1);
+          }
+          if (k + 1 < ng) {
+            p1 = prev_of(k + 1);
+            finish(k, p0);
+            finish(k + 1, p1);
+          } else {
+            finish(k, p0);
+          }
         }
-        slot[k * BS + threadIdx.x] = u;
-      });
-      auto qidx = [&](int k) { return base + (int64_t)k * BS + threadIdx.x; };
-      auto finish = [&](int k, const f32x4& prev) {
-        const int64_t qq = qidx(k);
-        if (qq >= ngroups) return;
-        const f32x4 u = slot[k * BS + threadIdx.x];
+        return;
+      }
+      if (!FIRST) {
+#pragma unroll
+        for (int k = 0; k < G; ++k) {
+          const int64_t qq = base + (int64_t)k * BS + threadIdx.x;
+          const int64_t q = qq < end ? qq : end - 1;
+          slot[k * BS + threadIdx.x] = ld_nt(reinterpret_cast<const f32x4*>(acc) + q);
+        }
+      }
+      rank_sums_streamed<In, 8, G, CAP, BS>(rows, nw, base, end, NG, [&](int k, const float* s) {
+        const int64_t qq = base + (int64_t)k * BS + threadIdx.x;
         f32x4 o;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          o[e] = FIRST ? u[e] : prev[e] + u[e];
-          if (SUMSQ) ss = fma((double)o[e], (double)o[e], ss);
+          float u = div(s[e]);
+          if (SCALE) u *= scale;
+          o[e] = FIRST ? u : slot[k * BS + threadIdx.x][e] + u;
+          if (SUMSQ && qq < end) ss = fma((double)o[e], (double)o[e], ss);
         }
-        st_nt(o, reinterpret_cast<f32x4*>(acc) + qq);
-      };
-      auto prev_of = [&](int k) {
-        const int64_t q = qidx(k) < ngroups ? qidx(k) : ngroups - 1;
-        return ld_nt(reinterpret_cast<const f32x4*>(acc) + q);
-      };
-      if (FIRST) {
-#pragma unroll
-        for (int k = 0; k < G; ++k) finish(k, f32x4{0.f, 0.f, 0.f, 0.f});
-      } else {
-        f32x4 p0 = prev_of(0), p1;
-#pragma unroll 1
-        for (int k = 0; k < G; k += 2) {
-          if (k + 1 < G) p1 = prev_of(k + 1);
-          finish(k, p0);
-          if (k + 1 >= G) break;
-          if (k + 2 < G) p0 = prev_of(k + 2);
-          finish(k + 1, p1);
-        }
-      }
-      continue;
-    }
-    if (!FIRST) {
-#pragma unroll
-      for (int k = 0; k < G; ++k) {
+        slot[k * BS + threadIdx.x] = o;
+      });
+      for (int k = 0; k < NG; ++k) {  // each lane writes back only its own slots
         const int64_t qq = base + (int64_t)k * BS + threadIdx.x;
-        const int64_t q = qq < ngroups ? qq : ngroups - 1;
-        slot[k * BS + threadIdx.x] = ld_nt(reinterpret_cast<const f32x4*>(acc) + q);
+        if (qq >= end) break;
+        st_nt(slot[k * BS + threadIdx.x], reinterpret_cast<f32x4*>(acc) + qq);
       }
-    }
-    rank_sums_streamed<In, 8, G, CAP, BS>(rows, nw, base, ngroups, [&](int k, const float* s) {
-      const int64_t qq = base + (int64_t)k * BS + threadIdx.x;
-      f32x4 o;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float u = div(s[e]);
-        if (SCALE) u *= scale;
-        o[e] = FIRST ? u : slot[k * BS + threadIdx.x][e] + u;
-        if (SUMSQ && qq < ngroups) ss = fma((double)o[e], (double)o[e], ss);
-      }
-      slot[k * BS + threadIdx.x] = o;
-    });
-    for (int k = 0; k < G; ++k) {  // each lane writes back only its own slots
-      const int64_t qq = base + (int64_t)k * BS + threadIdx.x;
-      if (qq >= ngroups) break;
-      st_nt(slot[k * BS + threadIdx.x], reinterpret_cast<f32x4*>(acc) + qq);
-    }
+    };
+    if (ng == G) tile(std::true_type{});
+    else tile(std::false_type{});
   }
   if (blockIdx.x == 0) {  // ragged tail
     for (int64_t i = ngroups * 4 + threadIdx.x; i < n; i += BS) {
@@ -204,12 +233,17 @@ template <int G, int BS, int NW, int CAP, typename In, bool SUMSQ, bool FIRST, b
 void launch_accum_shape(const RowTable<CAP>& t, int world, int64_t n, float* acc, float scale,
                         double* partials, int64_t* grid_out, size_t lds, hipStream_t s) {
   const int64_t ngroups = n / 4;
-  int64_t grid = grid_for(ngroups, (int64_t)BS * G, BS);
+  const int64_t span = (int64_t)BS * G;
+  if (lds < (size_t)G * BS * sizeof(f32x4)) lds = (size_t)G * BS * sizeof(f32x4);
+  auto kernel = k_accum<NW, CAP, G, BS, In, SUMSQ, FIRST, SCALE, RM>;
+  const TilePlan plan =
+      span > 64 ? balanced_tiles(ngroups, span, device_slots(s, reinterpret_cast<const void*>(kernel), BS, lds))
+                : plain_tiles(ngroups, span);
+  int64_t grid = grid_for(plan.count(), 1, BS);
   if (SUMSQ && grid > max_partials(n)) grid = max_partials(n);
   *grid_out = grid;
-  if (lds < (size_t)G * BS * sizeof(f32x4)) lds = (size_t)G * BS * sizeof(f32x4);
-  hipLaunchKernelGGL((k_accum<NW, CAP, G, BS, In, SUMSQ, FIRST, SCALE, RM>), dim3((unsigned)grid),
-                     dim3(BS), lds, s, t, world, mean_div(world), scale, ngroups, n, acc, partials);
+  hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(BS), lds, s, t, world, mean_div(world), scale,
+                     ngroups, n, plan, acc, partials);
 }
 
 template <int NW, int CAP, typename In, bool SUMSQ, bool FIRST, bool SCALE>

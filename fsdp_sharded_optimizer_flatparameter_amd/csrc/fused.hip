@@ -10,6 +10,8 @@
 // Pages: "Lesson 5: ZeRO and FSDP" s3 (ZeRO-1/2 steps 1-2, reduce-scatter
 // result -> local update -> BF16), "Data parallelism and ZeRO memory
 // sharding" s3.1 and s4.2.
+#include <type_traits>
+
 #include "zs_device.hpp"
 #include "zs_launch.hpp"
 
@@ -30,7 +32,7 @@ namespace {
 // (rank_sums_streamed).
 template <int NW, int CAP, int G, int C, int BS, typename In, bool CAST, bool SCALE, bool RM>
 __global__ __launch_bounds__(BS) void k_fused(RowTable<CAP> rows, int world, MeanDiv div,
-                                                    int64_t ngroups, int64_t n,
+                                                    int64_t ngroups, int64_t n, TilePlan plan,
                                                     float* __restrict__ th, float* __restrict__ m,
                                                     float* __restrict__ v, AdamConsts c,
                                                     const float* __restrict__ scale,
@@ -39,72 +41,99 @@ __global__ __launch_bounds__(BS) void k_fused(RowTable<CAP> rows, int world, Mea
   using L = Lanes<In>;
   const int nw = NW > 0 ? NW : world;
   const float sc = SCALE ? *scale : 1.0f;
-  const int64_t span = (int64_t)BS * G;
 
-  for (int64_t base = (int64_t)blockIdx.x * span; base < ngroups; base += (int64_t)gridDim.x * span) {
-    auto sink = [&](int k, const float* acc) {
-      f32x4 gv;
+  for (int64_t t = blockIdx.x; t < plan.count(); t += gridDim.x) {
+    int64_t base, end;  // the tile's groups; each lane takes ng of them (at most G)
+    plan.range(t, ngroups, &base, &end);
+    const int ng = G == 1 ? 1 : (int)((end - base + BS - 1) / BS);
+    // a full tile (ng == G) runs loops with compile-time trip counts
+    auto tile = [&](auto full) {
+      constexpr bool FULL = decltype(full)::value;
+      auto sink = [&](int k, const float* acc) {
+        f32x4 gv;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) gv[e] = SCALE ? div(acc[e]) * sc : div(acc[e]);
-      gl[k * BS + threadIdx.x] = gv;
-    };
-    if constexpr (RM) rank_sums_rank_major<In, C, G, CAP, BS>(rows, nw, base, ngroups, gl, sink);
-    else rank_sums_streamed<In, C, G, CAP, BS>(rows, nw, base, ngroups, sink);
-    // phase 2: with bf16 contributions double-buffered (group k+1's state loads
-    // are in flight while group k is updated and stored)
-    auto qidx = [&](int k) { return base + (int64_t)k * BS + threadIdx.x; };
-    auto load = [&](int k, f32x4& T, f32x4& M, f32x4& W) {
-      const int64_t q = qidx(k) < ngroups ? qidx(k) : ngroups - 1;
-      T = ld_nt(reinterpret_cast<const f32x4*>(th) + q);
-      M = ld_nt(reinterpret_cast<const f32x4*>(m) + q);
-      W = ld_nt(reinterpret_cast<const f32x4*>(v) + q);
-    };
-    auto update = [&](int k, f32x4& T, f32x4& M, f32x4& W) {  // every lane calls it
-      const int64_t qq = qidx(k);
-      const bool ok = qq < ngroups;
-      uint32_t lo = 0, hi = 0;  // the bf16 group, packed on live lanes only
-      if (ok) {
-        const f32x4 gv = gl[k * BS + threadIdx.x];
+        for (int e = 0; e < 4; ++e) gv[e] = SCALE ? div(acc[e]) * sc : div(acc[e]);
+        gl[k * BS + threadIdx.x] = gv;
+      };
+      if constexpr (RM) rank_sums_rank_major<In, C, G, CAP, BS, FULL>(rows, nw, base, end, ng, gl, sink);
+      else rank_sums_streamed<In, C, G, CAP, BS>(rows, nw, base, end, FULL ? G : ng, sink);
+      // phase 2: with bf16 contributions double-buffered (group k+1's state
+      // loads are in flight while group k is updated and stored)
+      auto qidx = [&](int k) { return base + (int64_t)k * BS + threadIdx.x; };
+      auto load = [&](int k, f32x4& T, f32x4& M, f32x4& W) {
+        const int64_t q = qidx(k) < end ? qidx(k) : end - 1;
+        T = ld_nt(reinterpret_cast<const f32x4*>(th) + q);
+        M = ld_nt(reinterpret_cast<const f32x4*>(m) + q);
+        W = ld_nt(reinterpret_cast<const f32x4*>(v) + q);
+      };
+      auto update = [&](int k, f32x4& T, f32x4& M, f32x4& W) {  // every lane calls it
+        const int64_t qq = qidx(k);
+        const bool ok = qq < end;
+        uint32_t lo = 0, hi = 0;  // the bf16 group, packed on live lanes only
+        if (ok) {
+          const f32x4 gv = gl[k * BS + threadIdx.x];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float tt = T[e], mm = M[e], vv = W[e];
-          adamw_elem(tt, mm, vv, gv[e], c);
-          T[e] = tt;
-          M[e] = mm;
-          W[e] = vv;
+          for (int e = 0; e < 4; ++e) {
+            float tt = T[e], mm = M[e], vv = W[e];
+            adamw_elem(tt, mm, vv, gv[e], c);
+            T[e] = tt;
+            M[e] = mm;
+            W[e] = vv;
+          }
+          st_nt(T, reinterpret_cast<f32x4*>(th) + qq);
+          st_nt(M, reinterpret_cast<f32x4*>(m) + qq);
+          st_nt(W, reinterpret_cast<f32x4*>(v) + qq);
+          if (CAST) {
+            lo = pack_bf16x2(T[0], T[1]);
+            hi = pack_bf16x2(T[2], T[3]);
+            if (!(om & 1)) store_bf16_even(out, qq, lo, hi, om);
+          }
         }
-        st_nt(T, reinterpret_cast<f32x4*>(th) + qq);
-        st_nt(M, reinterpret_cast<f32x4*>(m) + qq);
-        st_nt(W, reinterpret_cast<f32x4*>(v) + qq);
-        if (CAST) {
-          lo = pack_bf16x2(T[0], T[1]);
-          hi = pack_bf16x2(T[2], T[3]);
-          if (!(om & 1)) store_bf16_even(out, qq, lo, hi, om);
-        }
-      }
-      if (CAST && (om & 1)) store_bf16_odd(out, qq, lo, hi, ok, om);
-    };
-    if constexpr (sizeof(In) == 4 && !RM) {
-      // fp32 contributions, group-major walk: all G groups' state loads are
-      // issued before the first update (measured 2% faster than two in flight
-      // at N=64)
-      f32x4 T[G], M[G], W[G];
+        if (CAST && (om & 1)) store_bf16_odd(out, qq, lo, hi, ok, om);
+      };
+      if constexpr (sizeof(In) == 4 && !RM) {
+        // fp32 contributions, group-major walk: all G groups' state loads are
+        // issued before the first update (measured 2% faster than two in
+        // flight at N=64); groups past ng load group end-1 and store nothing
+        f32x4 T[G], M[G], W[G];
 #pragma unroll
-      for (int k = 0; k < G; ++k) load(k, T[k], M[k], W[k]);
+        for (int k = 0; k < G; ++k) load(k, T[k], M[k], W[k]);
 #pragma unroll
-      for (int k = 0; k < G; ++k) update(k, T[k], M[k], W[k]);
-    } else {
-      f32x4 T0, M0, W0, T1, M1, W1;
-      load(0, T0, M0, W0);
+        for (int k = 0; k < G; ++k) update(k, T[k], M[k], W[k]);
+      } else if constexpr (FULL) {
+        f32x4 T0, M0, W0, T1, M1, W1;
+        load(0, T0, M0, W0);
 #pragma unroll 1
-      for (int k = 0; k < G; k += 2) {
-        if (k + 1 < G) load(k + 1, T1, M1, W1);
-        update(k, T0, M0, W0);
-        if (k + 1 >= G) break;
-        if (k + 2 < G) load(k + 2, T0, M0, W0);
-        update(k + 1, T1, M1, W1);
+        for (int k = 0; k < G; k += 2) {
+          if (k + 1 < G) load(k + 1, T1, M1, W1);
+          update(k, T0, M0, W0);
+          if (k + 1 >= G) break;
+          if (k + 2 < G) load(k + 2, T0, M0, W0);
+          update(k + 1, T1, M1, W1);
+        }
+      } else {
+        // pairs whose two prefetches both exist, then the last one or two groups
+        f32x4 T0, M0, W0, T1, M1, W1;
+        load(0, T0, M0, W0);
+        int k = 0;
+#pragma unroll 1
+        for (; k + 2 < ng; k += 2) {
+          load(k + 1, T1, M1, W1);
+          update(k, T0, M0, W0);
+          load(k + 2, T0, M0, W0);
+          update(k + 1, T1, M1, W1);
+        }
+        if (k + 1 < ng) {
+          load(k + 1, T1, M1, W1);
+          update(k, T0, M0, W0);
+          update(k + 1, T1, M1, W1);
+        } else {
+          update(k, T0, M0, W0);
+        }
       }
-    }
+    };
+    if (ng == G) tile(std::true_type{});
+    else tile(std::false_type{});
   }
   if (blockIdx.x == 0) {  // ragged tail (fewer than 4 elements)
     for (int64_t i = ngroups * 4 + threadIdx.x; i < n; i += BS) {
@@ -193,17 +222,19 @@ void run_fused(const void* const* rows, int world, int64_t n, float* th, float* 
   RowTable<CAP> t;
   for (int i = 0; i < CAP; ++i) t.p[i] = i < world ? rows[i] : nullptr;
   const int64_t ngroups = n / 4;
-  const dim3 gd((unsigned)grid_for(ngroups, (int64_t)BS * G, BS)), bd(BS);
   const MeanDiv d = mean_div(world);
   const int om = out ? bf16_out_mode(out) : 0;
-  if (out && scale)
-    hipLaunchKernelGGL((k_fused<NW, CAP, G, C, BS, In, true, true, RM>), gd, bd, lds, s, t, world, d, ngroups, n, th, m, v, c, scale, out, om);
-  else if (out)
-    hipLaunchKernelGGL((k_fused<NW, CAP, G, C, BS, In, true, false, RM>), gd, bd, lds, s, t, world, d, ngroups, n, th, m, v, c, scale, out, om);
-  else if (scale)
-    hipLaunchKernelGGL((k_fused<NW, CAP, G, C, BS, In, false, true, RM>), gd, bd, lds, s, t, world, d, ngroups, n, th, m, v, c, scale, out, om);
-  else
-    hipLaunchKernelGGL((k_fused<NW, CAP, G, C, BS, In, false, false, RM>), gd, bd, lds, s, t, world, d, ngroups, n, th, m, v, c, scale, out, om);
+  auto go = [&](auto kernel) {
+    const void* k = reinterpret_cast<const void*>(kernel);
+    const TilePlan plan = BS * G > 64 ? balanced_tiles(ngroups, (int64_t)BS * G, device_slots(s, k, BS, lds))
+                                      : plain_tiles(ngroups, (int64_t)BS * G);
+    const dim3 gd((unsigned)grid_for(plan.count(), 1, BS)), bd(BS);
+    hipLaunchKernelGGL(kernel, gd, bd, lds, s, t, world, d, ngroups, n, plan, th, m, v, c, scale, out, om);
+  };
+  if (out && scale) go(k_fused<NW, CAP, G, C, BS, In, true, true, RM>);
+  else if (out) go(k_fused<NW, CAP, G, C, BS, In, true, false, RM>);
+  else if (scale) go(k_fused<NW, CAP, G, C, BS, In, false, true, RM>);
+  else go(k_fused<NW, CAP, G, C, BS, In, false, false, RM>);
 }
 
 template <typename In, int G, int C, int BS>

@@ -22,6 +22,7 @@
 //     power of two), so the result is independent of the launch shape;
 //   * rows are read with the nontemporal hint (each byte is used once).
 #include <mutex>
+#include <type_traits>
 
 #include "zs_device.hpp"
 #include "zs_launch.hpp"
@@ -45,39 +46,47 @@ namespace {
 // the same LDS slots.
 template <int NW, int CAP, int G, int C, int BS, typename In, bool SUMSQ, bool RM = false>
 __global__ __launch_bounds__(BS) void k_reduce(RowTable<CAP> rows, int world, MeanDiv div,
-                                                     int64_t ngroups, int64_t n,
+                                                     int64_t ngroups, int64_t n, TilePlan plan,
                                                      float* __restrict__ g,
                                                      double* __restrict__ partials) {
   extern __shared__ f32x4 gl[];  // G * BS groups when G > 1
   using L = Lanes<In>;
   const int nw = NW > 0 ? NW : world;
-  const int64_t span = (int64_t)BS * G;
   double ss = 0.0;
 
-  for (int64_t base = (int64_t)blockIdx.x * span; base < ngroups; base += (int64_t)gridDim.x * span) {
-    auto sink = [&](int k, const float* acc) {
-      const int64_t qq = base + (int64_t)k * BS + threadIdx.x;
-      f32x4 o;
+  for (int64_t t = blockIdx.x; t < plan.count(); t += gridDim.x) {
+    int64_t base, end;  // the tile's groups; each lane takes ng of them (at most G)
+    plan.range(t, ngroups, &base, &end);
+    const int ng = G == 1 ? 1 : (int)((end - base + BS - 1) / BS);
+    // a full tile (ng == G) runs loops with compile-time trip counts
+    auto tile = [&](auto full) {
+      constexpr bool FULL = decltype(full)::value;
+      auto sink = [&](int k, const float* acc) {
+        const int64_t qq = base + (int64_t)k * BS + threadIdx.x;
+        f32x4 o;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        o[e] = div(acc[e]);
-        if (SUMSQ && qq < ngroups) ss = fma((double)o[e], (double)o[e], ss);
-      }
-      if (G == 1) {
-        if (qq < ngroups) st_nt(o, reinterpret_cast<f32x4*>(g) + qq);
-      } else {
-        gl[k * BS + threadIdx.x] = o;
+        for (int e = 0; e < 4; ++e) {
+          o[e] = div(acc[e]);
+          if (SUMSQ && qq < end) ss = fma((double)o[e], (double)o[e], ss);
+        }
+        if (G == 1) {
+          if (qq < end) st_nt(o, reinterpret_cast<f32x4*>(g) + qq);
+        } else {
+          gl[k * BS + threadIdx.x] = o;
+        }
+      };
+      if constexpr (RM) rank_sums_rank_major<In, C, G, CAP, BS, FULL>(rows, nw, base, end, ng, gl, sink);
+      else rank_sums_streamed<In, C, G, CAP, BS>(rows, nw, base, end, FULL ? G : ng, sink);
+      if (G > 1) {
+        for (int k = 0; k < (FULL ? G : ng); ++k) {  // each lane writes back only its own entries
+          const int64_t qq = base + k * BS + threadIdx.x;
+          if (qq >= end) break;
+          st_nt(gl[k * BS + threadIdx.x], reinterpret_cast<f32x4*>(g) + qq);
+        }
       }
     };
-    if constexpr (RM) rank_sums_rank_major<In, C, G, CAP, BS>(rows, nw, base, ngroups, gl, sink);
-    else rank_sums_streamed<In, C, G, CAP, BS>(rows, nw, base, ngroups, sink);
-    if (G > 1) {
-      for (int k = 0; k < G; ++k) {  // each lane writes back only its own entries
-        const int64_t qq = base + k * BS + threadIdx.x;
-        if (qq >= ngroups) break;
-        st_nt(gl[k * BS + threadIdx.x], reinterpret_cast<f32x4*>(g) + qq);
-      }
-    }
+    if (ng == G) tile(std::true_type{});
+    else tile(std::false_type{});
   }
 
   // ragged tail (fewer than 4 elements), same order of operations
@@ -150,16 +159,19 @@ hipError_t run_vec(const void* const* rows, int world, int64_t n, float* g, doub
   for (int i = 0; i < CAP; ++i) t.p[i] = i < world ? rows[i] : nullptr;
   const int64_t ngroups = n / 4;
   const int64_t span = (int64_t)BS * G;
-  int64_t grid = grid_for(ngroups, span, BS);
-  if (partials && grid > max_partials(n)) grid = max_partials(n);
-  *grid_out = grid;
   const size_t lds = G > 1 ? (size_t)G * BS * 16 : kOneWaveLds;
-  if (partials)
-    hipLaunchKernelGGL((k_reduce<NW, CAP, G, C, BS, In, true, RM>), dim3((unsigned)grid), dim3(BS), lds,
-                       s, t, world, mean_div(world), ngroups, n, g, partials);
-  else
-    hipLaunchKernelGGL((k_reduce<NW, CAP, G, C, BS, In, false, RM>), dim3((unsigned)grid), dim3(BS), lds,
-                       s, t, world, mean_div(world), ngroups, n, g, partials);
+  auto go = [&](auto kernel) {
+    const void* k = reinterpret_cast<const void*>(kernel);
+    const TilePlan plan = span > 64 ? balanced_tiles(ngroups, span, device_slots(s, k, BS, lds))
+                                    : plain_tiles(ngroups, span);
+    int64_t grid = grid_for(plan.count(), 1, BS);
+    if (partials && grid > max_partials(n)) grid = max_partials(n);
+    *grid_out = grid;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(BS), lds, s, t, world, mean_div(world), ngroups, n,
+                       plan, g, partials);
+  };
+  if (partials) go(k_reduce<NW, CAP, G, C, BS, In, true, RM>);
+  else go(k_reduce<NW, CAP, G, C, BS, In, false, RM>);
   return hipGetLastError();
 }
 

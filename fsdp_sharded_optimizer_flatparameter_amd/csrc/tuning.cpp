@@ -1,7 +1,9 @@
-// Launch-shape knobs of the streaming kernels and the sum-of-squares workspace
-// bound. Host code only.
+// Launch-shape knobs of the streaming kernels, the sum-of-squares workspace
+// bound and the per-device residency lookup. Host code only.
 #include <cstdint>
 #include <cstdlib>
+#include <mutex>
+#include <vector>
 
 #include "zs_launch.hpp"
 
@@ -49,6 +51,39 @@ int64_t max_partials(int64_t n) {
   const int64_t b = (n + 255) / 256;
   const int64_t kMax = (int64_t(1) << 24) - 1;  // x 256 lanes stays a 32-bit dispatch
   return b < 1 ? 1 : (b > kMax ? kMax : b);
+}
+
+int64_t device_slots(hipStream_t s, const void* kernel, int bs, size_t lds) {
+  struct Entry {
+    const void* kernel;
+    int dev;
+    int bs;
+    size_t lds;
+    int64_t slots;
+  };
+  static std::mutex mu;
+  static std::vector<Entry> known;
+  int dev = 0;
+  if ((s ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev)) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  for (const Entry& e : known)
+    if (e.kernel == kernel && e.dev == dev && e.bs == bs && e.lds == lds) return e.slots;
+  int cus = 0, per_cu = 0, cur = 0;
+  int64_t slots = 0;
+  // the occupancy query answers for the current device
+  if (hipGetDevice(&cur) == hipSuccess && (cur == dev || hipSetDevice(dev) == hipSuccess)) {
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, bs, lds) == hipSuccess &&
+        cus > 0 && per_cu > 0)
+      slots = (int64_t)cus * per_cu;
+    if (cur != dev) (void)hipSetDevice(cur);
+  }
+  // the entry points return before launching while an error is pending, so
+  // an error left here is this lookup's own: clear it (the launch then uses
+  // plain tiles)
+  if (slots == 0) (void)hipGetLastError();
+  known.push_back(Entry{kernel, dev, bs, lds, slots});
+  return slots;
 }
 
 }  // namespace zs

@@ -163,9 +163,10 @@ struct Lanes<float> {
   }
 };
 
-// Rank sums of G groups per lane -- group k at index base + k*BS + lane, BS the
-// workgroup size --
-// streamed as one double-buffered sequence of rank chunks that runs across
+// Rank sums of the first `ng` (at most G) groups per lane -- group k at index
+// base + k*BS + lane, BS the workgroup size, lanes past `end` loading group
+// end-1 and discarding it -- streamed as one double-buffered sequence of rank
+// chunks that runs across
 // group boundaries: while chunk i is added, chunk i+1 (the next ranks of the
 // same group, or the first ranks of the next group) is already in flight, so a
 // lane never waits a full memory round trip between two groups. Each group's
@@ -175,16 +176,16 @@ struct Lanes<float> {
 // sink(k, acc) receives group k's finished sums.
 template <typename In, int C, int G, int CAP, int BS = kThreads, typename Sink>
 __device__ __forceinline__ void rank_sums_streamed(const RowTable<CAP>& rows, int nw, int64_t base,
-                                                   int64_t ngroups, Sink&& sink) {
+                                                   int64_t end, int ng, Sink&& sink) {
   using L = Lanes<In>;
   using Vec = typename L::Vec;
   const int nch = (nw + C - 1) / C;  // chunks per group
-  const int total = G * nch;
+  const int total = (G == 1 ? 1 : ng) * nch;
   auto load = [&](int idx, Vec* buf) {
     const int k = idx / nch;
     const int r0 = (idx - k * nch) * C;
     const int64_t qq = base + (int64_t)k * BS + threadIdx.x;
-    const int64_t q = qq < ngroups ? qq : ngroups - 1;  // clamped: loads stay in bounds
+    const int64_t q = qq < end ? qq : end - 1;  // clamped: loads stay in bounds
 #pragma unroll
     for (int u = 0; u < C; ++u)
       if (r0 + u < nw) buf[u] = ld_nt(static_cast<const Vec*>(rows.p[r0 + u]) + q);
@@ -223,26 +224,33 @@ __device__ __forceinline__ void rank_sums_streamed(const RowTable<CAP>& rows, in
 // -0.0 here; each element still adds c_0, c_1, ..., c_{N-1} in that order in
 // fp32, so the result is bit-identical to rank_sums_streamed. The loads of
 // step i+1 (C rows of one group) are in flight while step i is added.
-// nw must be a multiple of C. sink(k, acc) receives group k's finished sums
-// after the last chunk.
-template <typename In, int C, int G, int CAP, int BS, typename Sink>
+// Only the first `ng` (at most G) groups per lane are walked, lanes past `end`
+// loading group end-1 and discarding it; FULL (ng == G) takes the loop with a
+// compile-time step count. nw must be a multiple of C. sink(k, acc) receives
+// group k's finished sums after the last chunk.
+//
+// The full-tile loop prefetches across the first step of each pair only: its
+// second prefetch is conditional, so the wave waits for all outstanding loads
+// before the pair's second add. That half-pipelined loop measured faster for
+// bf16 rows at N=64 than prefetching both steps of every pair (3% for the
+// single pass and the reduce on the 7.5B shard) and much faster than no
+// prefetch (23-31%); with fp32 rows the two prefetching loops measured within
+// 1.2% of each other.
+template <typename In, int C, int G, int CAP, int BS, bool FULL, typename Sink>
 __device__ __forceinline__ void rank_sums_rank_major(const RowTable<CAP>& rows, int nw, int64_t base,
-                                                     int64_t ngroups, f32x4* sums, Sink&& sink) {
+                                                     int64_t end, int ng, f32x4* sums, Sink&& sink) {
   using L = Lanes<In>;
   using Vec = typename L::Vec;
   const int nch = nw / C;
-  const int total = nch * G;
 #pragma unroll
   for (int k = 0; k < G; ++k) sums[k * BS + threadIdx.x] = f32x4{-0.0f, -0.0f, -0.0f, -0.0f};
-  auto load = [&](int idx, Vec* buf) {
-    const int c = idx / G, k = idx - c * G;
+  auto load = [&](int c, int k, Vec* buf) {
     const int64_t qq = base + (int64_t)k * BS + threadIdx.x;
-    const int64_t q = qq < ngroups ? qq : ngroups - 1;  // clamped: loads stay in bounds
+    const int64_t q = qq < end ? qq : end - 1;  // clamped: loads stay in bounds
 #pragma unroll
     for (int u = 0; u < C; ++u) buf[u] = ld_nt(static_cast<const Vec*>(rows.p[c * C + u]) + q);
   };
-  auto consume = [&](int idx, const Vec* buf) {
-    const int c = idx / G, k = idx - c * G;
+  auto consume = [&](int c, int k, const Vec* buf) {
     const f32x4 s = sums[k * BS + threadIdx.x];
     float acc[4] = {s[0], s[1], s[2], s[3]};
 #pragma unroll
@@ -251,14 +259,54 @@ __device__ __forceinline__ void rank_sums_rank_major(const RowTable<CAP>& rows, 
     else sums[k * BS + threadIdx.x] = f32x4{acc[0], acc[1], acc[2], acc[3]};
   };
   Vec a[C], b[C];
-  load(0, a);
+  if constexpr (FULL) {
+    // step idx reads chunk idx / G of group idx % G
+    const int total = nch * G;
+    load(0, 0, a);
 #pragma unroll 1
-  for (int idx = 0; idx < total; idx += 2) {
-    if (idx + 1 < total) load(idx + 1, b);
-    consume(idx, a);
-    if (idx + 1 >= total) break;
-    if (idx + 2 < total) load(idx + 2, a);
-    consume(idx + 1, b);
+    for (int idx = 0; idx < total; idx += 2) {
+      if (idx + 1 < total) load((idx + 1) / G, (idx + 1) % G, b);
+      consume(idx / G, idx % G, a);
+      if (idx + 1 >= total) break;
+      if (idx + 2 < total) load((idx + 2) / G, (idx + 2) % G, a);
+      consume((idx + 1) / G, (idx + 1) % G, b);
+    }
+  } else {
+    // (c, k) advance group-fastest over ng groups; pairs whose two prefetches
+    // both exist run in the loop, the last one or two steps after it
+    const int total = nch * ng;
+    auto next = [&](int& c, int& k) {
+      if (++k == ng) {
+        k = 0;
+        ++c;
+      }
+    };
+    int c0 = 0, k0 = 0, c1 = 0, k1 = 0;
+    load(c0, k0, a);
+    int idx = 0;
+#pragma unroll 1
+    for (; idx + 2 < total; idx += 2) {
+      c1 = c0;
+      k1 = k0;
+      next(c1, k1);
+      load(c1, k1, b);
+      consume(c0, k0, a);
+      c0 = c1;
+      k0 = k1;
+      next(c0, k0);
+      load(c0, k0, a);
+      consume(c1, k1, b);
+    }
+    if (idx + 1 < total) {
+      c1 = c0;
+      k1 = k0;
+      next(c1, k1);
+      load(c1, k1, b);
+      consume(c0, k0, a);
+      consume(c1, k1, b);
+    } else {
+      consume(c0, k0, a);
+    }
   }
 }
 

@@ -214,7 +214,10 @@ zs_status zs_pack_shard(const zs_param_desc* d_desc, int32_t nparams, int64_t to
  *                 one IEEE division by N (bit-identical for any launch shape)
  *   sumsq_out     optional DEVICE double: receives sum_k g[k]^2 (this
  *                 shard's partial of a global gradient norm, [DPZ] s6),
- *                 accumulated in fp64 in a fixed order (deterministic)
+ *                 accumulated in fp64 in a fixed order: the same bits on
+ *                 every call with the same n, N and dtype on devices with
+ *                 the same number of compute units (the launch's tiles, and
+ *                 so the order of the partial sums, follow the CU count)
  *   workspace     DEVICE scratch of at least zs_workspace_bytes(n) bytes,
  *                 required only when sumsq_out != NULL
  * grad_out may not overlap any row; sumsq_out and workspace may not overlap
