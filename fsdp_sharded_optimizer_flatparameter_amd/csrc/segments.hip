@@ -90,26 +90,30 @@ __device__ void seg_to_f32(const Src* __restrict__ src, float* __restrict__ dst,
   if (head > len) head = len;
   const bool vec = (reinterpret_cast<uintptr_t>(src + head) & (4 * sizeof(Src) - 1)) == 0;
   if (!vec) {
-    for (int64_t i = threadIdx.x; i < len; i += BS) dst[i] = widen(src[i]);
+    for (int64_t i = threadIdx.x; i < len; i += BS) st_g(widen(ld_g(src + i)), dst + i);
     return;
   }
-  for (int64_t i = threadIdx.x; i < head; i += BS) dst[i] = widen(src[i]);
+  for (int64_t i = threadIdx.x; i < head; i += BS) st_g(widen(ld_g(src + i)), dst + i);
   const int64_t nv = (len - head) / 4;
   const Src* s = src + head;
   float* d = dst + head;
   for (int64_t i = threadIdx.x; i < nv; i += BS)
     st_nt(load4(s + 4 * i), reinterpret_cast<f32x4*>(d + 4 * i));
-  for (int64_t i = head + 4 * nv + threadIdx.x; i < len; i += BS) dst[i] = widen(src[i]);
+  for (int64_t i = head + 4 * nv + threadIdx.x; i < len; i += BS) st_g(widen(ld_g(src + i)), dst + i);
 }
 
 // Destination vectors [k_begin, k_end) of a bf16 copy whose source runs SH
 // elements (1..7) past a 16-byte boundary when the destination sits on one:
 // destination vector k takes elements SH + 8k .. SH + 8k + 7 of the aligned
 // source vectors sa[k] and sa[k + 1]. Each lane loads its own sa[k] and gets
-// sa[k + 1] from the next lane by a wave shuffle (the last active lane of a
-// wave loads it itself), then funnel-shifts the pair into one aligned store.
-// Each lane keeps 4 source vectors in flight: with one at a time the realigning
-// copy was bound by load latency.
+// sa[k + 1] from the next lane by a wave shuffle, then funnel-shifts the pair
+// into one aligned store. Each lane keeps 4 source vectors in flight: with one
+// at a time the realigning copy was bound by load latency.
+// In one-wave workgroups lane 63's neighbour is lane 0 of the next group of
+// 64 vectors, which the wave already holds, and the one vector after the last
+// of a round is loaded together with the round by the lane that needs it, so a
+// round costs one memory round trip. (Loading that vector after the shuffle,
+// as wider workgroups still do, made every round wait for memory twice.)
 // The caller keeps every loaded vector, sa[k_begin] .. sa[k_end], inside
 // memory the copy may read: the copied range itself, or the same piece's
 // elements around it (see seg_bf16).
@@ -120,29 +124,59 @@ __device__ void realign_bf16(const u32x4* __restrict__ sa, u32x4* __restrict__ d
   constexpr bool half = (SH & 1) != 0;  // plus one bf16
   constexpr int U = 4;               // source vectors in flight per lane
   const int lane = threadIdx.x & 63;
-  for (int64_t kb = k_begin; kb < k_end; kb += U * BS) {  // uniform across the workgroup
-    u32x4 lo[U];
+  auto emit = [&](const u32x4& lo, const u32x4& hi, int64_t k) {
+    const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    u32x4 o;
 #pragma unroll
-    for (int j = 0; j < U; ++j) {
-      const int64_t k = kb + (int64_t)j * BS + threadIdx.x;
-      lo[j] = k < k_end ? ld_nt(sa + k) : u32x4{0u, 0u, 0u, 0u};
+    for (int t = 0; t < 4; ++t) o[t] = half ? (w[q + t] >> 16) | (w[q + t + 1] << 16) : w[q + t];
+    st_nt(o, da + k);
+  };
+  auto next_lane = [](const u32x4& x) {  // lane i receives lane i+1's vector
+    return u32x4{(uint32_t)__shfl_down(x.x, 1, 64), (uint32_t)__shfl_down(x.y, 1, 64),
+                 (uint32_t)__shfl_down(x.z, 1, 64), (uint32_t)__shfl_down(x.w, 1, 64)};
+  };
+  if constexpr (BS == 64) {
+    for (int64_t kb = k_begin; kb < k_end; kb += U * 64) {
+      const int64_t kx = kb + U * 64 < k_end ? kb + U * 64 : k_end;  // this round: [kb, kx)
+      u32x4 lo[U];
+#pragma unroll
+      for (int j = 0; j < U; ++j) {
+        const int64_t k = kb + (int64_t)j * 64 + lane;
+        lo[j] = k < kx ? ld_nt(sa + k) : u32x4{0u, 0u, 0u, 0u};
+      }
+      // sa[kx], the neighbour of the round's last vector, by the lane holding it
+      u32x4 ext{0u, 0u, 0u, 0u};
+      if (lane == (int)((kx - 1 - kb) & 63)) ext = ld_nt(sa + kx);
+#pragma unroll
+      for (int j = 0; j < U; ++j) {
+        const int64_t k = kb + (int64_t)j * 64 + lane;
+        u32x4 hi = next_lane(lo[j]);
+        if (j + 1 < U) {
+          const u32x4 nx{(uint32_t)__shfl(lo[j + 1].x, 0, 64), (uint32_t)__shfl(lo[j + 1].y, 0, 64),
+                         (uint32_t)__shfl(lo[j + 1].z, 0, 64), (uint32_t)__shfl(lo[j + 1].w, 0, 64)};
+          if (lane == 63) hi = nx;
+        }
+        if (k >= kx) continue;
+        if (k + 1 == kx) hi = ext;
+        emit(lo[j], hi, k);
+      }
     }
+  } else {
+    for (int64_t kb = k_begin; kb < k_end; kb += U * BS) {  // uniform across the workgroup
+      u32x4 lo[U];
 #pragma unroll
-    for (int j = 0; j < U; ++j) {
-      const int64_t k = kb + (int64_t)j * BS + threadIdx.x;
-      u32x4 hi;  // sa[k + 1]: the next lane's vector of the same round
-      hi.x = __shfl_down(lo[j].x, 1, 64);
-      hi.y = __shfl_down(lo[j].y, 1, 64);
-      hi.z = __shfl_down(lo[j].z, 1, 64);
-      hi.w = __shfl_down(lo[j].w, 1, 64);
-      if (k >= k_end) continue;
-      if (lane == 63 || k + 1 >= k_end) hi = ld_nt(sa + k + 1);
-      const uint32_t w[8] = {lo[j].x, lo[j].y, lo[j].z, lo[j].w, hi.x, hi.y, hi.z, hi.w};
-      u32x4 o;
+      for (int j = 0; j < U; ++j) {
+        const int64_t k = kb + (int64_t)j * BS + threadIdx.x;
+        lo[j] = k < k_end ? ld_nt(sa + k) : u32x4{0u, 0u, 0u, 0u};
+      }
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-        o[t] = half ? (w[q + t] >> 16) | (w[q + t + 1] << 16) : w[q + t];
-      st_nt(o, da + k);
+      for (int j = 0; j < U; ++j) {
+        const int64_t k = kb + (int64_t)j * BS + threadIdx.x;
+        u32x4 hi = next_lane(lo[j]);  // sa[k + 1]: the next lane's vector of the same round
+        if (k >= k_end) continue;
+        if (lane == 63 || k + 1 >= k_end) hi = ld_nt(sa + k + 1);
+        emit(lo[j], hi, k);
+      }
     }
   }
 }
@@ -164,49 +198,62 @@ __device__ void realign_bf16(const u32x4* __restrict__ sa, u32x4* __restrict__ d
 template <int BS>
 __device__ void seg_bf16(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst,
                          int64_t len, bool lead = false, bool trail = false) {
+  static_assert(BS >= 16, "each lane copies at most one element of each end");
   const uintptr_t da = reinterpret_cast<uintptr_t>(dst);
   int64_t head = (int64_t)(((16u - (da & 15u)) & 15u) / 2u);
   if (head > len) head = len;
   const int sh = (int)((reinterpret_cast<uintptr_t>(src + head) & 15u) / 2u);
+  // The ends that go element by element ([0, e0) and [e1, len), at most 15
+  // elements each) are loaded before the vectors and stored after them, so
+  // that their loads share the vectors' round trip to memory.
+  auto ends = [&](int64_t e0, int64_t e1, auto&& vectors) {
+    const int64_t t = threadIdx.x;
+    const bool hl = t < e0, tl = e1 + t < len;
+    uint16_t hv = 0, tv = 0;
+    if (hl) hv = ld_g(src + t);
+    if (tl) tv = ld_g(src + e1 + t);
+    vectors();
+    if (hl) st_g(hv, dst + t);
+    if (tl) st_g(tv, dst + e1 + t);
+  };
   if (sh != 0) {
     const int64_t nv = (len - head) / 8;  // destination vectors
     const int64_t kb = (lead || head >= sh) ? 0 : 1;                  // first realigned vector
     const int64_t ke = (trail || len - head - 8 * nv >= 8 - sh) ? nv : nv - 1;  // one past the last
     if (ke - kb < 1) {
-      for (int64_t i = threadIdx.x; i < len; i += BS) dst[i] = src[i];
+      for (int64_t i = threadIdx.x; i < len; i += BS) st_g(ld_g(src + i), dst + i);
       return;
     }
     // element by element: the head (and destination vector 0 unless it is
     // realigned), then the last destination vector unless it is realigned,
     // and the tail
-    const int64_t e0 = head + 8 * kb, e1 = head + 8 * ke;
-    for (int64_t i = threadIdx.x; i < e0; i += BS) dst[i] = src[i];
-    for (int64_t i = e1 + threadIdx.x; i < len; i += BS) dst[i] = src[i];
     const u32x4* sa = reinterpret_cast<const u32x4*>(src + head - sh);
     u32x4* dv = reinterpret_cast<u32x4*>(dst + head);
-    switch (sh) {
-      case 1: realign_bf16<1, BS>(sa, dv, kb, ke); break;
-      case 2: realign_bf16<2, BS>(sa, dv, kb, ke); break;
-      case 3: realign_bf16<3, BS>(sa, dv, kb, ke); break;
-      case 4: realign_bf16<4, BS>(sa, dv, kb, ke); break;
-      case 5: realign_bf16<5, BS>(sa, dv, kb, ke); break;
-      case 6: realign_bf16<6, BS>(sa, dv, kb, ke); break;
-      default: realign_bf16<7, BS>(sa, dv, kb, ke); break;
-    }
+    ends(head + 8 * kb, head + 8 * ke, [&] {
+      switch (sh) {
+        case 1: realign_bf16<1, BS>(sa, dv, kb, ke); break;
+        case 2: realign_bf16<2, BS>(sa, dv, kb, ke); break;
+        case 3: realign_bf16<3, BS>(sa, dv, kb, ke); break;
+        case 4: realign_bf16<4, BS>(sa, dv, kb, ke); break;
+        case 5: realign_bf16<5, BS>(sa, dv, kb, ke); break;
+        case 6: realign_bf16<6, BS>(sa, dv, kb, ke); break;
+        default: realign_bf16<7, BS>(sa, dv, kb, ke); break;
+      }
+    });
     return;
   }
-  for (int64_t i = threadIdx.x; i < head; i += BS) dst[i] = src[i];
   const int64_t nv = (len - head) / 8;
   const u32x4* s = reinterpret_cast<const u32x4*>(src + head);
   u32x4* d = reinterpret_cast<u32x4*>(dst + head);
-  int64_t i = threadIdx.x;
-  for (; i + BS < nv; i += 2 * BS) {
-    const u32x4 a = ld_nt(s + i), b = ld_nt(s + i + BS);
-    st_nt(a, d + i);
-    st_nt(b, d + i + BS);
-  }
-  if (i < nv) st_nt(ld_nt(s + i), d + i);
-  for (int64_t i = head + 8 * nv + threadIdx.x; i < len; i += BS) dst[i] = src[i];
+  ends(head, head + 8 * nv, [&] {
+    int64_t i = threadIdx.x;
+    for (; i + BS < nv; i += 2 * BS) {
+      const u32x4 a = ld_nt(s + i), b = ld_nt(s + i + BS);
+      st_nt(a, d + i);
+      st_nt(b, d + i + BS);
+    }
+    if (i < nv) st_nt(ld_nt(s + i), d + i);
+  });
 }
 
 template <int BS = kThreads>
@@ -214,11 +261,11 @@ __device__ void zero_f32(float* __restrict__ p, int64_t len) {
   const uintptr_t a = reinterpret_cast<uintptr_t>(p);
   int64_t head = (int64_t)(((16u - (a & 15u)) & 15u) / 4u);
   if (head > len) head = len;
-  for (int64_t i = threadIdx.x; i < head; i += BS) p[i] = 0.0f;
+  for (int64_t i = threadIdx.x; i < head; i += BS) st_g(0.0f, p + i);
   const int64_t nv = (len - head) / 4;
   f32x4* d = reinterpret_cast<f32x4*>(p + head);
   for (int64_t i = threadIdx.x; i < nv; i += BS) st_nt(f32x4{0.f, 0.f, 0.f, 0.f}, d + i);
-  for (int64_t i = head + 4 * nv + threadIdx.x; i < len; i += BS) p[i] = 0.0f;
+  for (int64_t i = head + 4 * nv + threadIdx.x; i < len; i += BS) st_g(0.0f, p + i);
 }
 
 // Stage parameter offsets in LDS when the table fits (BS: the workgroup size).

@@ -22,15 +22,24 @@ constexpr int kThreads = 256;  // 4 wave64 per workgroup
 
 // ---- streaming memory access -------------------------------------------------
 
+// Every pointer these helpers take is device (global) memory. Pointers that
+// come out of a table in memory (the parameter descriptors) are generic to the
+// compiler, which would access them with FLAT instructions; a FLAT store counts
+// on the LDS/scalar-load counter as well, so every wait for a shuffle or a
+// descriptor load would also wait for the stores in flight. The casts below
+// give the compiler the global address space.
+template <typename T>
+using gptr = __attribute__((address_space(1))) T*;
+
 #ifndef ZS_NT_LOADS
 #define ZS_NT_LOADS 1
 #endif
 template <typename T>
 __device__ __forceinline__ T ld_nt(const T* p) {
 #if ZS_NT_LOADS
-  return __builtin_nontemporal_load(p);
+  return __builtin_nontemporal_load((const __attribute__((address_space(1))) T*)p);
 #else
-  return *p;
+  return *(const __attribute__((address_space(1))) T*)p;
 #endif
 }
 #ifndef ZS_NT_STORES
@@ -39,10 +48,19 @@ __device__ __forceinline__ T ld_nt(const T* p) {
 template <typename T>
 __device__ __forceinline__ void st_nt(T v, T* p) {
 #if ZS_NT_STORES
-  __builtin_nontemporal_store(v, p);
+  __builtin_nontemporal_store(v, (gptr<T>)p);
 #else
-  *p = v;
+  *(gptr<T>)p = v;
 #endif
+}
+// Plain (cached) element accesses to global memory.
+template <typename T>
+__device__ __forceinline__ T ld_g(const T* p) {
+  return *(const __attribute__((address_space(1))) T*)p;
+}
+template <typename T>
+__device__ __forceinline__ void st_g(T v, T* p) {
+  *(gptr<T>)p = v;
 }
 
 // ---- bf16 <-> fp32 -----------------------------------------------------------
