@@ -40,9 +40,12 @@ namespace {
 // 256 lanes over 8192 elements, in alternating rounds: the flat copy-out 2-4%
 // faster with 2048-element chunks (a 2 GiB parameter, the Llama-3-8B and 70B
 // blocks); the dim-0 copy-out 7% (Llama-3-8B block, N = 8), 12% (GPT-2,
-// N = 8) and 1% (GPT-2, N = 5) faster with 1024-element chunks.
+// N = 8) and 1% (GPT-2, N = 5) faster with 1024-element chunks. Since the
+// stores go out as global (not FLAT) stores, 1024-element chunks are also the
+// best for the flat copy-out: 2.2-3.9% faster than 2048 on those blocks, the
+// 2 GiB parameter and GPT-2's unit (512 elements: 6-35% slower).
 constexpr int kCopyBS = 64;
-constexpr int64_t kCopyChunk = 2048;
+constexpr int64_t kCopyChunk = 1024;
 constexpr int64_t kCopyDim0Chunk = 1024;
 constexpr int kLdsParams = 1024;   // offsets cached in LDS up to this many parameters
 // The packs take one-wave workgroups as well (fp32 writes, 12 of their 16
