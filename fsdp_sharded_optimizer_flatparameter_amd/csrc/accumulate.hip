@@ -58,11 +58,13 @@ __global__ __launch_bounds__(BS) void k_accum(RowTable<CAP> rows, int world, Mea
           }
           slot[k * BS + threadIdx.x] = u;
         });
-        auto qidx = [&](int k) { return base + (int64_t)k * BS + threadIdx.x; };
+        // each wave finishes its own run of groups
+        __syncthreads();
+        auto qidx = [&](int k) { return base + (int64_t)wave_run_index(NG, k); };
         auto finish = [&](int k, const f32x4& prev) {
           const int64_t qq = qidx(k);
           if (qq >= end) return;
-          const f32x4 u = slot[k * BS + threadIdx.x];
+          const f32x4 u = slot[wave_run_index(NG, k)];
           f32x4 o;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -77,7 +79,7 @@ __global__ __launch_bounds__(BS) void k_accum(RowTable<CAP> rows, int world, Mea
         };
         if (FIRST) {
 #pragma unroll
-          for (int k = 0; k < G; ++k) finish(k, f32x4{0.f, 0.f, 0.f, 0.f});  // k >= ng: nothing
+          for (int k = 0; k < NG; ++k) finish(k, f32x4{0.f, 0.f, 0.f, 0.f});
         } else if constexpr (FULL) {
           f32x4 p0 = prev_of(0), p1;
 #pragma unroll 1
@@ -107,6 +109,7 @@ __global__ __launch_bounds__(BS) void k_accum(RowTable<CAP> rows, int world, Mea
             finish(k, p0);
           }
         }
+        __syncthreads();  // the next tile's walk rewrites slots other waves read
         return;
       }
       if (!FIRST) {

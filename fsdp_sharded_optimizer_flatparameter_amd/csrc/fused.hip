@@ -58,8 +58,15 @@ __global__ __launch_bounds__(BS) void k_fused(RowTable<CAP> rows, int world, Mea
       if constexpr (RM) rank_sums_rank_major<In, C, G, CAP, BS, FULL>(rows, nw, base, end, ng, gl, sink);
       else rank_sums_streamed<In, C, G, CAP, BS>(rows, nw, base, end, FULL ? G : ng, sink);
       // phase 2: with bf16 contributions double-buffered (group k+1's state
-      // loads are in flight while group k is updated and stored)
-      auto qidx = [&](int k) { return base + (int64_t)k * BS + threadIdx.x; };
+      // loads are in flight while group k is updated and stored); after the
+      // rank-major walk each wave updates its own run of groups
+      [[maybe_unused]] const int NG = FULL ? G : ng;
+      if constexpr (RM) __syncthreads();
+      auto ridx = [&](int k) -> int {
+        if constexpr (RM) return wave_run_index(NG, k);
+        else return k * BS + (int)threadIdx.x;
+      };
+      auto qidx = [&](int k) { return base + (int64_t)ridx(k); };
       auto load = [&](int k, f32x4& T, f32x4& M, f32x4& W) {
         const int64_t q = qidx(k) < end ? qidx(k) : end - 1;
         T = ld_nt(reinterpret_cast<const f32x4*>(th) + q);
@@ -71,7 +78,7 @@ __global__ __launch_bounds__(BS) void k_fused(RowTable<CAP> rows, int world, Mea
         const bool ok = qq < end;
         uint32_t lo = 0, hi = 0;  // the bf16 group, packed on live lanes only
         if (ok) {
-          const f32x4 gv = gl[k * BS + threadIdx.x];
+          const f32x4 gv = gl[ridx(k)];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             float tt = T[e], mm = M[e], vv = W[e];
@@ -131,6 +138,7 @@ __global__ __launch_bounds__(BS) void k_fused(RowTable<CAP> rows, int world, Mea
           update(k, T0, M0, W0);
         }
       }
+      if constexpr (RM) __syncthreads();  // the next tile's walk rewrites entries other waves read
     };
     if (ng == G) tile(std::true_type{});
     else tile(std::false_type{});

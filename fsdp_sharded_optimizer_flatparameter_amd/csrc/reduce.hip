@@ -78,11 +78,17 @@ __global__ __launch_bounds__(BS) void k_reduce(RowTable<CAP> rows, int world, Me
       if constexpr (RM) rank_sums_rank_major<In, C, G, CAP, BS, FULL>(rows, nw, base, end, ng, gl, sink);
       else rank_sums_streamed<In, C, G, CAP, BS>(rows, nw, base, end, FULL ? G : ng, sink);
       if (G > 1) {
-        for (int k = 0; k < (FULL ? G : ng); ++k) {  // each lane writes back only its own entries
-          const int64_t qq = base + k * BS + threadIdx.x;
+        // group-major: each lane writes back its own entries; rank-major: each
+        // wave writes its own run of groups
+        const int NG = FULL ? G : ng;
+        if constexpr (RM) __syncthreads();
+        for (int k = 0; k < NG; ++k) {
+          const int r = RM ? wave_run_index(NG, k) : k * BS + (int)threadIdx.x;
+          const int64_t qq = base + r;
           if (qq >= end) break;
-          st_nt(gl[k * BS + threadIdx.x], reinterpret_cast<f32x4*>(g) + qq);
+          st_nt(gl[r], reinterpret_cast<f32x4*>(g) + qq);
         }
+        if constexpr (RM) __syncthreads();
       }
     };
     if (ng == G) tile(std::true_type{});
