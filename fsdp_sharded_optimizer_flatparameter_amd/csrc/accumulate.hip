@@ -27,8 +27,9 @@ namespace {
 // runs without a write stream beside it, and the LDS reservation caps the
 // workgroups resident per CU. With RM the ranks are walked rank-major
 // (rank_sums_rank_major), the slots holding the running sums and then the
-// scaled means; the previous sums are read after the walk, two groups in
-// flight, as the single pass reads its state.
+// scaled means; after the walk and a barrier each wave reads the previous sums
+// of its own run of groups, two groups in flight, and writes the new ones, as
+// the single pass updates its state.
 template <int NW, int CAP, int G, int BS, typename In, bool SUMSQ, bool FIRST, bool SCALE,
           bool RM = false>
 __global__ __launch_bounds__(BS) void k_accum(RowTable<CAP> rows, int world, MeanDiv div,

@@ -20,9 +20,11 @@ namespace {
 
 // Two phases per workgroup over G groups per lane (G*BS*4 consecutive elements):
 //   1. the rank walk only -- the mean gradient of each group is parked in LDS;
-//   2. AdamW over the fp32 state of the same groups, each lane reading back its
-//      own LDS entries (no barrier), the state read and written as 16-byte
-//      vectors per group.
+//   2. AdamW over the fp32 state of the same groups, the state read and
+//      written as 16-byte vectors per group: after the group-major walk each
+//      lane reads back its own LDS entries (no barrier); after the rank-major
+//      walk a barrier lets each wave take its own run of groups
+//      (wave_run_index).
 // Keeping the row streams and the state read-modify-write apart in time, and
 // the LDS reservation (which caps the workgroups resident per CU), keeps fewer
 // DRAM pages open at once; both were measured to raise HBM throughput.
