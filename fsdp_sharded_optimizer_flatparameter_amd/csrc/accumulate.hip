@@ -31,7 +31,7 @@ namespace {
 // of its own run of groups, two groups in flight, and writes the new ones, as
 // the single pass updates its state.
 template <int NW, int CAP, int G, int BS, typename In, bool SUMSQ, bool FIRST, bool SCALE,
-          bool RM = false>
+          bool RM = false, bool RAGGED = false>
 __global__ __launch_bounds__(BS) void k_accum(RowTable<CAP> rows, int world, MeanDiv div,
                                                     float scale, int64_t ngroups, int64_t n,
                                                     TilePlan plan, float* __restrict__ acc,
@@ -50,7 +50,7 @@ __global__ __launch_bounds__(BS) void k_accum(RowTable<CAP> rows, int world, Mea
       const int NG = FULL ? G : ng;
       if constexpr (RM) {
         constexpr int C = sizeof(In) == 2 ? 4 : 2;
-        rank_sums_rank_major<In, C, G, CAP, BS, FULL>(rows, nw, base, end, ng, slot, [&](int k, const float* s) {
+        rank_sums_rank_major<In, C, G, CAP, BS, FULL, RAGGED>(rows, nw, base, end, ng, slot, [&](int k, const float* s) {
           f32x4 u;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -228,18 +228,19 @@ __global__ void k_clip(const double* __restrict__ partials, int count, double ma
 
 
 // Measured on MI355X: with many contributions the rank-major shape of the
-// single pass (16 groups per lane in 8-wave workgroups, 128 KiB of LDS), or
-// 16 groups in 4-wave workgroups (64 KiB, two per CU) where its chunk does not
-// divide the world size; with few, the shape of the single pass.
+// single pass (16 groups per lane in 8-wave workgroups, 128 KiB of LDS; the
+// last chunk of ranks short where the chunk does not divide the world size);
+// with few, the shape of the single pass.
 // ZS_ACCUM_SHAPE=1 selects the earlier shapes for comparison (4-wave
 // workgroups of 16 groups with many contributions, of 4 with few).
-template <int G, int BS, int NW, int CAP, typename In, bool SUMSQ, bool FIRST, bool SCALE, bool RM = false>
+template <int G, int BS, int NW, int CAP, typename In, bool SUMSQ, bool FIRST, bool SCALE, bool RM = false,
+          bool RAGGED = false>
 void launch_accum_shape(const RowTable<CAP>& t, int world, int64_t n, float* acc, float scale,
                         double* partials, int64_t* grid_out, size_t lds, hipStream_t s) {
   const int64_t ngroups = n / 4;
   const int64_t span = (int64_t)BS * G;
   if (lds < (size_t)G * BS * sizeof(f32x4)) lds = (size_t)G * BS * sizeof(f32x4);
-  auto kernel = k_accum<NW, CAP, G, BS, In, SUMSQ, FIRST, SCALE, RM>;
+  auto kernel = k_accum<NW, CAP, G, BS, In, SUMSQ, FIRST, SCALE, RM, RAGGED>;
   const TilePlan plan =
       span > 64 ? balanced_tiles(ngroups, span, device_slots(s, reinterpret_cast<const void*>(kernel), BS, lds))
                 : plain_tiles(ngroups, span);
@@ -256,9 +257,18 @@ void run_accum(const void* const* rows, int world, int64_t n, float* acc, float 
   RowTable<CAP> t;
   for (int i = 0; i < CAP; ++i) t.p[i] = i < world ? rows[i] : nullptr;
   constexpr int rm_c = sizeof(In) == 2 ? 4 : 2;
-  if (world >= 16 && world % rm_c == 0 && tuning().accum_shape == 0)
+  bool ragged = false;  // a short last chunk of ranks (world sizes the chunk does not divide)
+  if constexpr (NW == 0) ragged = world % rm_c != 0;
+  if (world >= 16 && tuning().accum_shape == 0) {
+    if constexpr (NW == 0) {
+      if (ragged) {
+        launch_accum_shape<16, 512, NW, CAP, In, SUMSQ, FIRST, SCALE, true, true>(t, world, n, acc, scale, partials,
+                                                                                  grid_out, 0, s);
+        return;
+      }
+    }
     launch_accum_shape<16, 512, NW, CAP, In, SUMSQ, FIRST, SCALE, true>(t, world, n, acc, scale, partials, grid_out, 0, s);
-  else if (world >= 16)
+  } else if (world >= 16)
     launch_accum_shape<16, 256, NW, CAP, In, SUMSQ, FIRST, SCALE>(t, world, n, acc, scale, partials, grid_out, 0, s);
   else if (tuning().accum_shape == 1)
     launch_accum_shape<4, 256, NW, CAP, In, SUMSQ, FIRST, SCALE>(t, world, n, acc, scale, partials, grid_out, 0, s);

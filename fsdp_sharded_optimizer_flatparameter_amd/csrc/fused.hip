@@ -32,7 +32,8 @@ namespace {
 // is added into all G groups before the next chunk is read, so every row is
 // read as one long run per chunk), otherwise the group-major one
 // (rank_sums_streamed).
-template <int NW, int CAP, int G, int C, int BS, typename In, bool CAST, bool SCALE, bool RM>
+template <int NW, int CAP, int G, int C, int BS, typename In, bool CAST, bool SCALE, bool RM,
+          bool RAGGED = false>
 __global__ __launch_bounds__(BS) void k_fused(RowTable<CAP> rows, int world, MeanDiv div,
                                                     int64_t ngroups, int64_t n, TilePlan plan,
                                                     float* __restrict__ th, float* __restrict__ m,
@@ -57,7 +58,8 @@ __global__ __launch_bounds__(BS) void k_fused(RowTable<CAP> rows, int world, Mea
         for (int e = 0; e < 4; ++e) gv[e] = SCALE ? div(acc[e]) * sc : div(acc[e]);
         gl[k * BS + threadIdx.x] = gv;
       };
-      if constexpr (RM) rank_sums_rank_major<In, C, G, CAP, BS, FULL>(rows, nw, base, end, ng, gl, sink);
+      if constexpr (RM)
+        rank_sums_rank_major<In, C, G, CAP, BS, FULL, RAGGED>(rows, nw, base, end, ng, gl, sink);
       else rank_sums_streamed<In, C, G, CAP, BS>(rows, nw, base, end, FULL ? G : ng, sink);
       // phase 2: with bf16 contributions double-buffered (group k+1's state
       // loads are in flight while group k is updated and stored); after the
@@ -204,18 +206,19 @@ constexpr int rm_chunk() { return sizeof(In) == 2 ? 4 : 2; }
 // workgroups walking the ranks rank-major over 16 staged groups (128 KiB of
 // LDS, one workgroup per CU) read every row in 64 KiB runs and ran the 7.5B
 // shard at N=64 3.5% faster, and the 70B chunk with fp32 rows 10% faster, than
-// 4-wave workgroups walking group-major over 16 groups (64 KiB, two per CU),
-// which remain for world sizes the chunk width does not divide. With few
+// 4-wave workgroups walking group-major over 16 groups (64 KiB, two per CU).
+// World sizes the chunk width does not divide take the same walk, the last
+// 1-3 ranks added by a short second walk: at N = 33 and 30 with bf16 rows the
+// group-major shape had run at 34-35% of peak, this one at 76-78%. With few
 // contributions the state read-modify-write dominates: one-wave workgroups
 // of a single group each, with a 16 KiB reservation (10 waves per CU), ran
 // the Llama-3-8B shard at N=8 11% faster than 4-wave workgroups (which were
 // best with 2 groups and 64 KiB); residency matters sharply there (5 waves
 // per CU ran 35% slower, 20 waves 8% slower).
-Shape fused_shape(int world, int chunk) {
+Shape fused_shape(int world) {
   Shape sh;
   const bool many = world >= 16;
   sh.bs = tuning().fused_bs > 0 ? tuning().fused_bs : (many ? 512 : 64);
-  if (sh.bs == 512 && world % chunk != 0) sh.bs = 256;  // the rank-major walk takes whole chunks
   sh.rm = sh.bs == 512;
   sh.g = tuning().fused_g > 0 ? tuning().fused_g : (many ? 16 : 1);
   if (sh.bs == 64 && sh.g > 4) sh.g = 4;  // one-wave workgroups are built for 1, 2 or 4 groups
@@ -226,7 +229,7 @@ Shape fused_shape(int world, int chunk) {
   return sh;
 }
 
-template <int NW, int CAP, int G, int C, int BS, typename In, bool RM = false>
+template <int NW, int CAP, int G, int C, int BS, typename In, bool RM = false, bool RAGGED = false>
 void run_fused(const void* const* rows, int world, int64_t n, float* th, float* m, float* v,
                const AdamConsts& c, const float* scale, uint16_t* out, size_t lds, hipStream_t s) {
   RowTable<CAP> t;
@@ -241,10 +244,10 @@ void run_fused(const void* const* rows, int world, int64_t n, float* th, float* 
     const dim3 gd((unsigned)grid_for(plan.count(), 1, BS)), bd(BS);
     hipLaunchKernelGGL(kernel, gd, bd, lds, s, t, world, d, ngroups, n, plan, th, m, v, c, scale, out, om);
   };
-  if (out && scale) go(k_fused<NW, CAP, G, C, BS, In, true, true, RM>);
-  else if (out) go(k_fused<NW, CAP, G, C, BS, In, true, false, RM>);
-  else if (scale) go(k_fused<NW, CAP, G, C, BS, In, false, true, RM>);
-  else go(k_fused<NW, CAP, G, C, BS, In, false, false, RM>);
+  if (out && scale) go(k_fused<NW, CAP, G, C, BS, In, true, true, RM, RAGGED>);
+  else if (out) go(k_fused<NW, CAP, G, C, BS, In, true, false, RM, RAGGED>);
+  else if (scale) go(k_fused<NW, CAP, G, C, BS, In, false, true, RM, RAGGED>);
+  else go(k_fused<NW, CAP, G, C, BS, In, false, false, RM, RAGGED>);
 }
 
 template <typename In, int G, int C, int BS>
@@ -292,15 +295,21 @@ void dispatch_world_rm(const void* const* rows, int world, int64_t n, float* th,
     case 32: run_fused<32, 32, 16, C, 512, In, true>(rows, world, n, th, m, v, c, scale, out, lds, s); break;
     case 64: run_fused<64, 64, 16, C, 512, In, true>(rows, world, n, th, m, v, c, scale, out, lds, s); break;
     default:
-      if (world <= 64) run_fused<0, 64, 16, C, 512, In, true>(rows, world, n, th, m, v, c, scale, out, lds, s);
-      else run_fused<0, ZS_MAX_WORLD, 16, C, 512, In, true>(rows, world, n, th, m, v, c, scale, out, lds, s);
+      if (world % C != 0) {  // a short last chunk
+        if (world <= 64) run_fused<0, 64, 16, C, 512, In, true, true>(rows, world, n, th, m, v, c, scale, out, lds, s);
+        else run_fused<0, ZS_MAX_WORLD, 16, C, 512, In, true, true>(rows, world, n, th, m, v, c, scale, out, lds, s);
+      } else if (world <= 64) {
+        run_fused<0, 64, 16, C, 512, In, true>(rows, world, n, th, m, v, c, scale, out, lds, s);
+      } else {
+        run_fused<0, ZS_MAX_WORLD, 16, C, 512, In, true>(rows, world, n, th, m, v, c, scale, out, lds, s);
+      }
   }
 }
 
 template <typename In>
 void dispatch(const void* const* rows, int world, int64_t n, float* th, float* m, float* v,
               const AdamConsts& c, const float* scale, uint16_t* out, hipStream_t s) {
-  const Shape sh = fused_shape(world, rm_chunk<In>());
+  const Shape sh = fused_shape(world);
   if (sh.rm) dispatch_world_rm<In>(rows, world, n, th, m, v, c, scale, out, sh.lds, s);
   else if (tuning().rank_chunk == 4) dispatch_g<In, 4>(sh, rows, world, n, th, m, v, c, scale, out, s);
   else dispatch_g<In, 8>(sh, rows, world, n, th, m, v, c, scale, out, s);

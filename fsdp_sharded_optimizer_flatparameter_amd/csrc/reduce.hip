@@ -44,7 +44,8 @@ namespace {
 // resident per CU); with G == 1 each group is stored as soon as it is summed.
 // RM walks the ranks rank-major (rank_sums_rank_major), its running sums in
 // the same LDS slots.
-template <int NW, int CAP, int G, int C, int BS, typename In, bool SUMSQ, bool RM = false>
+template <int NW, int CAP, int G, int C, int BS, typename In, bool SUMSQ, bool RM = false,
+          bool RAGGED = false>
 __global__ __launch_bounds__(BS) void k_reduce(RowTable<CAP> rows, int world, MeanDiv div,
                                                      int64_t ngroups, int64_t n, TilePlan plan,
                                                      float* __restrict__ g,
@@ -75,7 +76,8 @@ __global__ __launch_bounds__(BS) void k_reduce(RowTable<CAP> rows, int world, Me
           gl[k * BS + threadIdx.x] = o;
         }
       };
-      if constexpr (RM) rank_sums_rank_major<In, C, G, CAP, BS, FULL>(rows, nw, base, end, ng, gl, sink);
+      if constexpr (RM)
+        rank_sums_rank_major<In, C, G, CAP, BS, FULL, RAGGED>(rows, nw, base, end, ng, gl, sink);
       else rank_sums_streamed<In, C, G, CAP, BS>(rows, nw, base, end, FULL ? G : ng, sink);
       if (G > 1) {
         // group-major: each lane writes back its own entries; rank-major: each
@@ -157,7 +159,7 @@ __global__ __launch_bounds__(kThreads) void k_sumsq_finalize(const double* __res
 // without the sum of squares), where 10 or 20 per CU gained less.
 constexpr size_t kOneWaveLds = 11264;
 
-template <int NW, int CAP, int G, int C, typename In, bool RM = false>
+template <int NW, int CAP, int G, int C, typename In, bool RM = false, bool RAGGED = false>
 hipError_t run_vec(const void* const* rows, int world, int64_t n, float* g, double* partials,
                    int64_t* grid_out, hipStream_t s) {
   constexpr int BS = RM ? 512 : (G == 1 ? 64 : kThreads);
@@ -176,8 +178,8 @@ hipError_t run_vec(const void* const* rows, int world, int64_t n, float* g, doub
     hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(BS), lds, s, t, world, mean_div(world), ngroups, n,
                        plan, g, partials);
   };
-  if (partials) go(k_reduce<NW, CAP, G, C, BS, In, true, RM>);
-  else go(k_reduce<NW, CAP, G, C, BS, In, false, RM>);
+  if (partials) go(k_reduce<NW, CAP, G, C, BS, In, true, RM, RAGGED>);
+  else go(k_reduce<NW, CAP, G, C, BS, In, false, RM, RAGGED>);
   return hipGetLastError();
 }
 
@@ -198,7 +200,8 @@ hipError_t dispatch_world(const void* const* rows, int world, int64_t n, float* 
 }
 
 // The rank-major shape of the single pass: 16 groups per lane in 8-wave
-// workgroups, 128 KiB of LDS, the ranks walked in chunks of C.
+// workgroups, 128 KiB of LDS, the ranks walked in chunks of C (the last one
+// short when C does not divide the world size).
 template <typename In>
 hipError_t dispatch_world_rm(const void* const* rows, int world, int64_t n, float* g,
                              double* partials, int64_t* grid, hipStream_t s) {
@@ -208,6 +211,10 @@ hipError_t dispatch_world_rm(const void* const* rows, int world, int64_t n, floa
     case 32: return run_vec<32, 32, 16, C, In, true>(rows, world, n, g, partials, grid, s);
     case 64: return run_vec<64, 64, 16, C, In, true>(rows, world, n, g, partials, grid, s);
     default:
+      if (world % C != 0) {
+        if (world <= 64) return run_vec<0, 64, 16, C, In, true, true>(rows, world, n, g, partials, grid, s);
+        return run_vec<0, ZS_MAX_WORLD, 16, C, In, true, true>(rows, world, n, g, partials, grid, s);
+      }
       if (world <= 64) return run_vec<0, 64, 16, C, In, true>(rows, world, n, g, partials, grid, s);
       return run_vec<0, ZS_MAX_WORLD, 16, C, In, true>(rows, world, n, g, partials, grid, s);
   }
@@ -215,16 +222,14 @@ hipError_t dispatch_world_rm(const void* const* rows, int world, int64_t n, floa
 
 // Measured on MI355X: deep staging (16 groups, 64 KiB) pays off when the
 // rank walk is long, and the rank-major walk in 8-wave workgroups more so
-// (where its chunk divides the world size); with few contributions direct
-// stores are faster.
+// (at N = 33 and 30 the group-major shape ran at 30% of peak); with few
+// contributions direct stores are faster.
 template <typename In>
 hipError_t dispatch_shape(const void* const* rows, int world, int64_t n, float* g,
                           double* partials, int64_t* grid, hipStream_t s) {
   const int gsel = tuning().reduce_g > 0 ? tuning().reduce_g : (world >= 16 ? 16 : 1);
   const bool c4 = tuning().rank_chunk == 4;
-  const int rm_c = sizeof(In) == 2 ? 4 : 2;
-  if (tuning().reduce_g == 0 && world >= 16 && world % rm_c == 0)
-    return dispatch_world_rm<In>(rows, world, n, g, partials, grid, s);
+  if (tuning().reduce_g == 0 && world >= 16) return dispatch_world_rm<In>(rows, world, n, g, partials, grid, s);
   switch (gsel) {
     case 16:
       return c4 ? dispatch_world<16, 4, In>(rows, world, n, g, partials, grid, s)

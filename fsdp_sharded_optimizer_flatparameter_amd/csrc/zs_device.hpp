@@ -8,6 +8,8 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 #include <stdint.h>
 
 #include "zs.h"
@@ -244,8 +246,13 @@ __device__ __forceinline__ void rank_sums_streamed(const RowTable<CAP>& rows, in
 // step i+1 (C rows of one group) are in flight while step i is added.
 // Only the first `ng` (at most G) groups per lane are walked, lanes past `end`
 // loading group end-1 and discarding it; FULL (ng == G) takes the loop with a
-// compile-time step count. nw must be a multiple of C. sink(k, acc) receives
-// group k's finished sums after the last chunk.
+// compile-time step count. Without RAGGED nw must be a multiple of C; with it
+// the nw % C (1..C-1) ranks after the last whole chunk are added by a second,
+// shorter walk over the groups whose rank count is a compile-time constant, so
+// that no load of either walk is conditional (predicated row loads made the
+// wave wait for every load in flight at each step: 50-54% of peak at N = 33
+// against 83-87% at N = 48). sink(k, acc) receives group k's finished sums
+// after its last rank.
 //
 // The full-tile loop prefetches across the first step of each pair only: its
 // second prefetch is conditional, so the wave waits for all outstanding loads
@@ -254,12 +261,13 @@ __device__ __forceinline__ void rank_sums_streamed(const RowTable<CAP>& rows, in
 // single pass and the reduce on the 7.5B shard) and much faster than no
 // prefetch (23-31%); with fp32 rows the two prefetching loops measured within
 // 1.2% of each other.
-template <typename In, int C, int G, int CAP, int BS, bool FULL, typename Sink>
+template <typename In, int C, int G, int CAP, int BS, bool FULL, bool RAGGED = false, typename Sink>
 __device__ __forceinline__ void rank_sums_rank_major(const RowTable<CAP>& rows, int nw, int64_t base,
                                                      int64_t end, int ng, f32x4* sums, Sink&& sink) {
   using L = Lanes<In>;
   using Vec = typename L::Vec;
-  const int nch = nw / C;
+  const int nch = nw / C;                 // whole chunks
+  const int rem = RAGGED ? nw - nch * C : 0;  // ranks after them
 #pragma unroll
   for (int k = 0; k < G; ++k) sums[k * BS + threadIdx.x] = f32x4{-0.0f, -0.0f, -0.0f, -0.0f};
   auto load = [&](int c, int k, Vec* buf) {
@@ -273,7 +281,7 @@ __device__ __forceinline__ void rank_sums_rank_major(const RowTable<CAP>& rows, 
     float acc[4] = {s[0], s[1], s[2], s[3]};
 #pragma unroll
     for (int u = 0; u < C; ++u) L::add(buf[u], acc);
-    if (c + 1 == nch) sink(k, acc);
+    if ((!RAGGED || rem == 0) && c + 1 == nch) sink(k, acc);
     else sums[k * BS + threadIdx.x] = f32x4{acc[0], acc[1], acc[2], acc[3]};
   };
   Vec a[C], b[C];
@@ -325,6 +333,43 @@ __device__ __forceinline__ void rank_sums_rank_major(const RowTable<CAP>& rows, 
     } else {
       consume(c0, k0, a);
     }
+  }
+  if constexpr (RAGGED) {
+    // ranks nch*C .. nw-1, R of them, over the same groups; the group loop is
+    // the full-tile loop's, with R rows per step
+    auto tail = [&](auto rr) {
+      constexpr int R = decltype(rr)::value;
+      const int NG = FULL ? G : ng;
+      auto tload = [&](int k, Vec* buf) {
+        const int64_t qq = base + (int64_t)k * BS + threadIdx.x;
+        const int64_t q = qq < end ? qq : end - 1;
+#pragma unroll
+        for (int u = 0; u < R; ++u) buf[u] = ld_nt(static_cast<const Vec*>(rows.p[nch * C + u]) + q);
+      };
+      auto tcons = [&](int k, const Vec* buf) {
+        const f32x4 s = sums[k * BS + threadIdx.x];
+        float acc[4] = {s[0], s[1], s[2], s[3]};
+#pragma unroll
+        for (int u = 0; u < R; ++u) L::add(buf[u], acc);
+        sink(k, acc);
+      };
+      Vec ta[R], tb[R];
+      tload(0, ta);
+#pragma unroll 1
+      for (int k = 0; k < NG; k += 2) {
+        if (k + 1 < NG) tload(k + 1, tb);
+        tcons(k, ta);
+        if (k + 1 >= NG) break;
+        if (k + 2 < NG) tload(k + 2, ta);
+        tcons(k + 1, tb);
+      }
+    };
+    if (rem == 1) tail(std::integral_constant<int, 1>{});
+    if constexpr (C > 2) {
+      if (rem == 2) tail(std::integral_constant<int, 2>{});
+      if (rem == 3) tail(std::integral_constant<int, 3>{});
+    }
+    static_assert(C <= 4, "the tail walk is built for chunks of up to 4 ranks");
   }
 }
 

@@ -148,8 +148,9 @@ def test_adamw_misaligned_and_8byte_slot():
     _adamw(50001, 2, hparams(), seed=323, out_offset=2)      # bf16 slot on a 4-byte boundary
 
 
-# every launch shape of the single pass: one-wave (4, 8), group-major 4-wave
-# (33), rank-major 8-wave (64; 16 with fp32 rows); the sizes leave the last
+# every launch shape of the single pass: one-wave (4, 8), rank-major 8-wave
+# with a short last chunk of ranks (33), rank-major 8-wave (64; 16 with fp32
+# rows); the sizes leave the last
 # wave of every shape with 1 or 37 live lanes, so the bf16 words that straddle
 # two lanes' groups meet a missing neighbour mid-wave as well as at lane 63
 @pytest.mark.parametrize("world,dtype,n", [(4, "bf16", 262144 * 3 + 5), (8, "bf16", 262144 * 3 + 4 * 37 + 3),
@@ -253,10 +254,10 @@ def test_cast_at_every_offset_in_a_cache_line():
 
 # world sizes: the one-wave shape (< 16; 2, 4 and 8 have kernels of their
 # own), the rank-major 8-wave shape (16, 32, 64, and 48 and 100 through the
-# kernels for any N up to 64 and up to 256; 30 with fp32 rows), and the
-# group-major 4-wave shape that takes over when the rank-major chunk does not
-# divide N (30 and 33 with bf16 rows, 33 with fp32 rows, 65 above 64); sizes
-# span several tiles of each and a ragged tail
+# kernels for any N up to 64 and up to 256; 30 with fp32 rows), and the same
+# shape with a short last chunk of ranks where the chunk does not divide N (30
+# and 33 with bf16 rows, 33 with fp32 rows, 65 above 64); sizes span several
+# tiles of each and a ragged tail
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("world", [1, 2, 3, 4, 8, 16, 30, 32, 33, 48, 64, 65, 100])
 def test_fused_step_is_bitwise_the_two_call_path(dtype, world):

@@ -10,7 +10,7 @@ tiles start and end inside the arrays, cover a varying number of groups per
 lane, and leave some lanes of their last group idle. These cases size the
 launch against the device so that the last round holds 1-2 units per
 workgroup, about 6.5 groups per lane, or a nearly full tile, after zero, one
-or two full rounds, and compare every element with the oracle's
+or two full rounds (with N = 33 the walk's last chunk of ranks is short), and compare every element with the oracle's
 ascending-rank fp32 mean ("Data parallelism and ZeRO memory sharding" s3.1)
 and the ZeRO-2 sum ("Lesson 5: ZeRO and FSDP" s3, ZeRO-2 step 1), and the
 single pass bit for bit with the two calls. Output buffers start as NaN, so a
@@ -32,11 +32,10 @@ LDS_PER_CU = 160 * 1024  # gfx950
 
 def _shape(world, dtype):
     """(lanes, groups per lane, resident workgroups per CU) of the multi-group
-    shape the dispatch picks for `world` >= 16 contributions."""
-    chunk = 4 if dtype == "bf16" else 2
-    if world % chunk == 0:
-        return 512, 16, LDS_PER_CU // (512 * 16 * 16)  # rank-major, 128 KiB of LDS
-    return 256, 16, LDS_PER_CU // (256 * 16 * 16)  # group-major, 64 KiB
+    shape the dispatch picks for `world` >= 16 contributions: the rank-major
+    walk in 8-wave workgroups with 128 KiB of LDS (its last chunk of ranks
+    short when the chunk, 4 bf16 or 2 fp32 rows, does not divide `world`)."""
+    return 512, 16, LDS_PER_CU // (512 * 16 * 16)
 
 
 def _sizes(world, dtype):
@@ -53,7 +52,7 @@ def _sizes(world, dtype):
     return {k: 4 * v + 3 for k, v in groups.items()}  # a ragged tail of 3 elements
 
 
-CASES = [(16, "bf16"), (64, "f32"), (33, "bf16")]
+CASES = [(16, "bf16"), (64, "f32"), (33, "bf16"), (33, "f32")]  # 33: a short last chunk
 
 
 @pytest.mark.parametrize("world, dtype", CASES)
