@@ -10,7 +10,7 @@ tiles start and end inside the arrays, cover a varying number of groups per
 lane, and leave some lanes of their last group idle. These cases size the
 launch against the device so that the last round holds 1-2 units per
 workgroup, about 6.5 groups per lane, or a nearly full tile, after zero, one
-or two full rounds (with N = 33 the walk's last chunk of ranks is short), and compare every element with the oracle's
+or two full rounds (with N = 31 and 33 the last 3 or 1 ranks take a second walk), and compare every element with the oracle's
 ascending-rank fp32 mean ("Data parallelism and ZeRO memory sharding" s3.1)
 and the ZeRO-2 sum ("Lesson 5: ZeRO and FSDP" s3, ZeRO-2 step 1), and the
 single pass bit for bit with the two calls. Output buffers start as NaN, so a
@@ -52,7 +52,7 @@ def _sizes(world, dtype):
     return {k: 4 * v + 3 for k, v in groups.items()}  # a ragged tail of 3 elements
 
 
-CASES = [(16, "bf16"), (64, "f32"), (33, "bf16"), (33, "f32")]  # 33: a short last chunk
+CASES = [(16, "bf16"), (64, "f32"), (33, "bf16"), (31, "bf16"), (33, "f32")]  # 31, 33: 3 and 1 ranks after the whole chunks
 
 
 @pytest.mark.parametrize("world, dtype", CASES)
