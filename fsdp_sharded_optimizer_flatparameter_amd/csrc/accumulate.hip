@@ -121,7 +121,7 @@ __global__ __launch_bounds__(BS) void k_accum(RowTable<CAP> rows, int world, Mea
           slot[k * BS + threadIdx.x] = ld_nt(reinterpret_cast<const f32x4*>(acc) + q);
         }
       }
-      rank_sums_streamed<In, 8, G, CAP, BS>(rows, nw, base, end, NG, [&](int k, const float* s) {
+      rank_sums_streamed<In, 8, G, CAP, BS, RAGGED>(rows, nw, base, end, NG, [&](int k, const float* s) {
         const int64_t qq = base + (int64_t)k * BS + threadIdx.x;
         f32x4 o;
 #pragma unroll
@@ -272,8 +272,16 @@ void run_accum(const void* const* rows, int world, int64_t n, float* acc, float 
     launch_accum_shape<16, 256, NW, CAP, In, SUMSQ, FIRST, SCALE>(t, world, n, acc, scale, partials, grid_out, 0, s);
   else if (tuning().accum_shape == 1)
     launch_accum_shape<4, 256, NW, CAP, In, SUMSQ, FIRST, SCALE>(t, world, n, acc, scale, partials, grid_out, 0, s);
-  else  // one wave, 13 KiB of LDS: 12 workgroups per CU (3% faster than 10 on the GPT-2 shard)
+  else {  // one wave, 13 KiB of LDS: 12 workgroups per CU (3% faster than 10 on the GPT-2 shard)
+    if constexpr (NW == 0 && CAP == 64) {
+      if (world > 8 && world < 16) {  // 9-15 ranks: one batch of row loads (rank_sums_streamed)
+        launch_accum_shape<1, 64, NW, CAP, In, SUMSQ, FIRST, SCALE, false, true>(t, world, n, acc, scale, partials,
+                                                                                 grid_out, 13312, s);
+        return;
+      }
+    }
     launch_accum_shape<1, 64, NW, CAP, In, SUMSQ, FIRST, SCALE>(t, world, n, acc, scale, partials, grid_out, 13312, s);
+  }
 }
 
 template <typename In, bool SUMSQ, bool FIRST, bool SCALE>

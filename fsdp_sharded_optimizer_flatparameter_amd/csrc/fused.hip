@@ -60,7 +60,7 @@ __global__ __launch_bounds__(BS) void k_fused(RowTable<CAP> rows, int world, Mea
       };
       if constexpr (RM)
         rank_sums_rank_major<In, C, G, CAP, BS, FULL, RAGGED>(rows, nw, base, end, ng, gl, sink);
-      else rank_sums_streamed<In, C, G, CAP, BS>(rows, nw, base, end, FULL ? G : ng, sink);
+      else rank_sums_streamed<In, C, G, CAP, BS, RAGGED>(rows, nw, base, end, FULL ? G : ng, sink);
       // phase 2: with bf16 contributions double-buffered (group k+1's state
       // loads are in flight while group k is updated and stored); after the
       // rank-major walk each wave updates its own run of groups
@@ -261,6 +261,12 @@ void dispatch_world(const void* const* rows, int world, int64_t n, float* th, fl
     case 32: run_fused<32, 32, G, C, BS, In>(rows, world, n, th, m, v, c, scale, out, lds, s); break;
     case 64: run_fused<64, 64, G, C, BS, In>(rows, world, n, th, m, v, c, scale, out, lds, s); break;
     default:
+      if constexpr (G == 1 && C == 8 && BS == 64) {
+        if (world > 8 && world < 16) {  // 9-15 ranks: one batch of row loads (rank_sums_streamed)
+          run_fused<0, 64, G, C, BS, In, false, true>(rows, world, n, th, m, v, c, scale, out, lds, s);
+          break;
+        }
+      }
       if (world <= 64) run_fused<0, 64, G, C, BS, In>(rows, world, n, th, m, v, c, scale, out, lds, s);
       else run_fused<0, ZS_MAX_WORLD, G, C, BS, In>(rows, world, n, th, m, v, c, scale, out, lds, s);
   }

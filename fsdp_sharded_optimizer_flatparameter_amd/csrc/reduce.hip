@@ -78,7 +78,7 @@ __global__ __launch_bounds__(BS) void k_reduce(RowTable<CAP> rows, int world, Me
       };
       if constexpr (RM)
         rank_sums_rank_major<In, C, G, CAP, BS, FULL, RAGGED>(rows, nw, base, end, ng, gl, sink);
-      else rank_sums_streamed<In, C, G, CAP, BS>(rows, nw, base, end, FULL ? G : ng, sink);
+      else rank_sums_streamed<In, C, G, CAP, BS, RAGGED>(rows, nw, base, end, FULL ? G : ng, sink);
       if (G > 1) {
         // group-major: each lane writes back its own entries; rank-major: each
         // wave writes its own run of groups
@@ -194,6 +194,10 @@ hipError_t dispatch_world(const void* const* rows, int world, int64_t n, float* 
     case 32: return run_vec<32, 32, G, C, In>(rows, world, n, g, partials, grid, s);
     case 64: return run_vec<64, 64, G, C, In>(rows, world, n, g, partials, grid, s);
     default:
+      if constexpr (G == 1 && C == 8) {
+        if (world > 8 && world < 16)  // 9-15 ranks: one batch of row loads (rank_sums_streamed)
+          return run_vec<0, 64, G, C, In, false, true>(rows, world, n, g, partials, grid, s);
+      }
       if (world <= 64) return run_vec<0, 64, G, C, In>(rows, world, n, g, partials, grid, s);
       return run_vec<0, ZS_MAX_WORLD, G, C, In>(rows, world, n, g, partials, grid, s);
   }

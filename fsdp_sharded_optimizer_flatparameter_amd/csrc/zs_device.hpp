@@ -194,11 +194,45 @@ struct Lanes<float> {
 // every x, signed zeros included), and adds ranks in ascending order, so it
 // equals c_0 + c_1 + ... + c_{N-1} evaluated left to right in fp32.
 // sink(k, acc) receives group k's finished sums.
-template <typename In, int C, int G, int CAP, int BS = kThreads, typename Sink>
+//
+// RAGGED (one group per lane, 9 to 16 ranks, C = 8): the ranks are loaded in
+// one batch whose row count a switch makes a compile-time constant. The
+// chunked walk's second chunk had its row loads predicated on the world size,
+// which made the wave wait for every load in flight: the single pass ran at
+// 52-61% of peak for N = 10-15, against 78% at N = 8. With one chunk (up to 8
+// ranks) the chunked walk is fine, and the launchers keep it; compiled into
+// the same kernel, the batch code made N = 5 and 7 1.5-5% slower.
+template <typename In, int C, int G, int CAP, int BS = kThreads, bool RAGGED = false, typename Sink>
 __device__ __forceinline__ void rank_sums_streamed(const RowTable<CAP>& rows, int nw, int64_t base,
                                                    int64_t end, int ng, Sink&& sink) {
   using L = Lanes<In>;
   using Vec = typename L::Vec;
+  if constexpr (G == 1 && RAGGED) {
+    if (nw > 8 && nw <= 16) {
+      auto batch = [&](auto rr) {
+        constexpr int R = decltype(rr)::value;
+        const int64_t qq = base + threadIdx.x;
+        const int64_t q = qq < end ? qq : end - 1;  // clamped: loads stay in bounds
+        Vec v[R];
+#pragma unroll
+        for (int u = 0; u < R; ++u) v[u] = ld_nt(static_cast<const Vec*>(rows.p[u]) + q);
+        float acc[4] = {-0.0f, -0.0f, -0.0f, -0.0f};
+#pragma unroll
+        for (int u = 0; u < R; ++u) L::add(v[u], acc);
+        sink(0, acc);
+      };
+      switch (nw) {
+        case 9: batch(std::integral_constant<int, 9>{}); return;
+        case 10: batch(std::integral_constant<int, 10>{}); return;
+        case 11: batch(std::integral_constant<int, 11>{}); return;
+        case 12: batch(std::integral_constant<int, 12>{}); return;
+        case 13: batch(std::integral_constant<int, 13>{}); return;
+        case 14: batch(std::integral_constant<int, 14>{}); return;
+        case 15: batch(std::integral_constant<int, 15>{}); return;
+        default: batch(std::integral_constant<int, 16>{}); return;
+      }
+    }
+  }
   const int nch = (nw + C - 1) / C;  // chunks per group
   const int total = (G == 1 ? 1 : ng) * nch;
   auto load = [&](int idx, Vec* buf) {
