@@ -33,28 +33,17 @@ constexpr int kThreads = 256;  // 4 wave64 per workgroup
 template <typename T>
 using gptr = __attribute__((address_space(1))) T*;
 
-#ifndef ZS_NT_LOADS
-#define ZS_NT_LOADS 1
-#endif
+// Nontemporal: each byte these kernels stream is used once (cached loads or
+// stores measured 10-20% slower for every kernel of the step).
 template <typename T>
 __device__ __forceinline__ T ld_nt(const T* p) {
-#if ZS_NT_LOADS
   return __builtin_nontemporal_load((const __attribute__((address_space(1))) T*)p);
-#else
-  return *(const __attribute__((address_space(1))) T*)p;
-#endif
 }
-#ifndef ZS_NT_STORES
-#define ZS_NT_STORES 1
-#endif
 template <typename T>
 __device__ __forceinline__ void st_nt(T v, T* p) {
-#if ZS_NT_STORES
   __builtin_nontemporal_store(v, (gptr<T>)p);
-#else
-  *(gptr<T>)p = v;
-#endif
 }
+
 // Plain (cached) element accesses to global memory.
 template <typename T>
 __device__ __forceinline__ T ld_g(const T* p) {
