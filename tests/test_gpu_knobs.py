@@ -9,7 +9,9 @@ case below runs the same seeded update in a child process under one setting
 loop) and compares all outputs with the default setting's, bitwise: the
 single pass and the two calls, the accumulation, the cast, the flat and dim-0
 copy-outs (the latter with odd-sized chunks, so through the realigning copy),
-the single pass into a bf16 slot on a 2-byte boundary, and the pack.
+the single pass into a bf16 slot on a 2-byte boundary, and the pack. The world
+sizes take every default launch shape: one-wave (8; 12 with its rows in one
+batch), rank-major (16, 64; 33 with a short second walk of 1 rank).
 """
 import os
 import subprocess
@@ -35,7 +37,8 @@ hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
 def h(t):
     t = t.detach().cpu()
     return t.view(torch.int16).numpy() if t.dtype == torch.bfloat16 else t.view(torch.int32).numpy()
-for world, dt, n in ((8, torch.bfloat16, 300_007), (64, torch.bfloat16, 70_001), (16, torch.float32, 50_003)):
+for world, dt, n in ((8, torch.bfloat16, 300_007), (64, torch.bfloat16, 70_001), (16, torch.float32, 50_003),
+                     (33, torch.bfloat16, 90_007), (12, torch.bfloat16, 120_003)):
     g0 = gen.device_generator(900 + world)
     rows = [gen.device_normal(g0, n, 1e-3, dt) for _ in range(world)]
     st = [gen.device_normal(g0, n, 0.02), gen.device_normal(g0, n, 1e-4), gen.device_normal(g0, n, 1e-6).abs_()]
@@ -107,7 +110,7 @@ def _run(tmp_path, env_over, tag):
 
 def test_no_knob_changes_a_result(tmp_path):
     base = _run(tmp_path, SETTINGS[0], "base")
-    for w in (8, 64, 16):  # the single pass is bitwise the two calls under the defaults
+    for w in (8, 64, 16, 33, 12):  # the single pass is bitwise the two calls under the defaults
         for i in range(3):
             assert np.array_equal(base[f"{w}_fused{i}"], base[f"{w}_two{i}"])
         assert np.array_equal(base[f"{w}_slot"], base[f"{w}_slot2"])
