@@ -154,10 +154,18 @@ __global__ __launch_bounds__(kThreads) void k_sumsq_finalize(const double* __res
 
 // One group per lane goes with one-wave workgroups (measured 4% faster at
 // N=8 than 4-wave ones); staged groups with 4-wave workgroups.
-// The one-wave shape reserves LDS it does not use, to hold residency at 14
-// workgroups per CU: 1.4-2.8% faster than full residency at N=8 (with and
-// without the sum of squares), where 10 or 20 per CU gained less.
-constexpr size_t kOneWaveLds = 11264;
+// The one-wave shape reserves LDS it does not use, to cap the workgroups
+// resident per CU by world size. From N = 8 up, 14 per CU (11 KiB): 1.4-2.8%
+// faster than full residency at N = 8 (with and without the sum of squares),
+// where 10 or 20 per CU gained less, and 1.5-3.4% faster at N = 10-15. With
+// fewer contributions each workgroup moves fewer bytes per memory round trip
+// and more of them must be in flight: full residency was 24-31% faster at
+// N = 2-4 and 14% at N = 5, 20 per CU (8 KiB) 7% faster at N = 6 and 2% at 7.
+inline size_t one_wave_lds(int world) {
+  if (world <= 5) return 0;
+  if (world <= 7) return 8192;
+  return 11264;
+}
 
 template <int NW, int CAP, int G, int C, typename In, bool RM = false, bool RAGGED = false>
 hipError_t run_vec(const void* const* rows, int world, int64_t n, float* g, double* partials,
@@ -167,7 +175,7 @@ hipError_t run_vec(const void* const* rows, int world, int64_t n, float* g, doub
   for (int i = 0; i < CAP; ++i) t.p[i] = i < world ? rows[i] : nullptr;
   const int64_t ngroups = n / 4;
   const int64_t span = (int64_t)BS * G;
-  const size_t lds = G > 1 ? (size_t)G * BS * 16 : kOneWaveLds;
+  const size_t lds = G > 1 ? (size_t)G * BS * 16 : one_wave_lds(world);
   auto go = [&](auto kernel) {
     const void* k = reinterpret_cast<const void*>(kernel);
     const TilePlan plan = span > 64 ? balanced_tiles(ngroups, span, device_slots(s, k, BS, lds))
