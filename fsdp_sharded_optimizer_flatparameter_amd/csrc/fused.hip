@@ -241,10 +241,11 @@ Shape fused_shape(int world) {
   if (sh.bs == 64 && sh.g > 4) sh.g = 4;  // one-wave workgroups are built for 1, 2 or 4 groups
   if (sh.rm) sh.g = 16;                     // the rank-major shape is built for 16 groups
   const size_t need = (size_t)sh.g * sh.bs * 16;
-  // one-wave workgroups: 10 per CU (16 KiB) from N = 8 up; 20 per CU (8 KiB)
+  // one-wave workgroups: 10 per CU (16 KiB) at N = 8; 20 per CU (8 KiB)
   // below, which measured 4% faster at N = 2, 3% at N = 6 and the same at N = 4
-  // (and 4.6% slower at N = 8)
-  const size_t one_wave = world <= 7 ? 8192 : 16384;
+  // (and 4.6% slower at N = 8); 13 per CU (12 KiB) at N = 9-15, 8% faster at
+  // N = 10, 6% at 12 and 2% at 15 (and 2% slower at N = 8)
+  const size_t one_wave = world <= 7 ? 8192 : (world > 8 && world < 16 ? 12288 : 16384);
   sh.lds = tuning().fused_lds > 0 ? (size_t)tuning().fused_lds : (sh.bs == 64 ? one_wave : 65536);
   if (sh.lds < need) sh.lds = need;
   return sh;
