@@ -277,9 +277,11 @@ void run_accum(const void* const* rows, int world, int64_t n, float* acc, float 
     // 10 on the GPT-2 shard); with fewer contributions more workgroups must be
     // in flight: full residency measured 41% faster at N = 2 and 33% at N = 4,
     // 20 per CU (8 KiB) 23% faster at N = 6 (both 3-4% slower at N = 8). The
-    // one-batch walk of N = 9-15 takes 16 per CU (10 KiB): 7-8% faster than 12
-    // at N = 9-12, 1% at 14-15
-    const size_t lds = world <= 5 ? 0 : (world <= 7 ? 8192 : (world > 8 && world < 16 ? 10240 : 13312));
+    // one-batch walk of N = 9-15 over bf16 rows takes 16 per CU (10 KiB): 7-8%
+    // faster than 12 at N = 9-12, 1% at 14-15 (and 3-4% slower with fp32 rows)
+    constexpr bool bf16 = sizeof(In) == 2;
+    const size_t lds =
+        world <= 5 ? 0 : (world <= 7 ? 8192 : (bf16 && world > 8 && world < 16 ? 10240 : 13312));
     if constexpr (NW == 0 && CAP == 64) {
       if (world > 8 && world < 16) {  // 9-15 ranks: one batch of row loads (rank_sums_streamed)
         launch_accum_shape<1, 64, NW, CAP, In, SUMSQ, FIRST, SCALE, false, true>(t, world, n, acc, scale, partials,

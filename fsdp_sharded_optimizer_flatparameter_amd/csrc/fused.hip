@@ -232,7 +232,7 @@ constexpr int rm_chunk() { return sizeof(In) == 2 ? 4 : 2; }
 // the Llama-3-8B shard at N=8 11% faster than 4-wave workgroups (which were
 // best with 2 groups and 64 KiB); residency matters sharply there (5 waves
 // per CU ran 35% slower, 20 waves 8% slower).
-Shape fused_shape(int world) {
+Shape fused_shape(int world, bool bf16) {
   Shape sh;
   const bool many = world >= 16;
   sh.bs = tuning().fused_bs > 0 ? tuning().fused_bs : (many ? 512 : 64);
@@ -243,9 +243,10 @@ Shape fused_shape(int world) {
   const size_t need = (size_t)sh.g * sh.bs * 16;
   // one-wave workgroups: 10 per CU (16 KiB) at N = 8; 20 per CU (8 KiB)
   // below, which measured 4% faster at N = 2, 3% at N = 6 and the same at N = 4
-  // (and 4.6% slower at N = 8); 13 per CU (12 KiB) at N = 9-15, 8% faster at
-  // N = 10, 6% at 12 and 2% at 15 (and 2% slower at N = 8)
-  const size_t one_wave = world <= 7 ? 8192 : (world > 8 && world < 16 ? 12288 : 16384);
+  // (and 4.6% slower at N = 8); with bf16 rows 13 per CU (12 KiB) at N = 9-15,
+  // 8% faster at N = 10, 6% at 12 and 2% at 15 (and 2% slower at N = 8), but
+  // 2-4% slower there with fp32 rows, which move twice the bytes per round trip
+  const size_t one_wave = world <= 7 ? 8192 : (bf16 && world > 8 && world < 16 ? 12288 : 16384);
   sh.lds = tuning().fused_lds > 0 ? (size_t)tuning().fused_lds : (sh.bs == 64 ? one_wave : 65536);
   if (sh.lds < need) sh.lds = need;
   return sh;
@@ -337,7 +338,7 @@ void dispatch_world_rm(const void* const* rows, int world, int64_t n, float* th,
 template <typename In>
 void dispatch(const void* const* rows, int world, int64_t n, float* th, float* m, float* v,
               const AdamConsts& c, const float* scale, uint16_t* out, hipStream_t s) {
-  const Shape sh = fused_shape(world);
+  const Shape sh = fused_shape(world, sizeof(In) == 2);
   if (sh.rm) dispatch_world_rm<In>(rows, world, n, th, m, v, c, scale, out, sh.lds, s);
   else if (tuning().rank_chunk == 4) dispatch_g<In, 4>(sh, rows, world, n, th, m, v, c, scale, out, s);
   else dispatch_g<In, 8>(sh, rows, world, n, th, m, v, c, scale, out, s);
