@@ -244,9 +244,14 @@ Shape fused_shape(int world, bool bf16) {
   // one-wave workgroups: 10 per CU (16 KiB) at N = 8; 20 per CU (8 KiB)
   // below, which measured 4% faster at N = 2, 3% at N = 6 and the same at N = 4
   // (and 4.6% slower at N = 8); with bf16 rows 13 per CU (12 KiB) at N = 9-15,
-  // 8% faster at N = 10, 6% at 12 and 2% at 15 (and 2% slower at N = 8), but
-  // 2-4% slower there with fp32 rows, which move twice the bytes per round trip
-  const size_t one_wave = world <= 7 ? 8192 : (bf16 && world > 8 && world < 16 ? 12288 : 16384);
+  // 8% faster at N = 10, 6% at 12 and 2% at 15 (and 2% slower at N = 8). fp32
+  // rows move twice the bytes per round trip and want fewer workgroups: from
+  // N = 8, 8 per CU (20 KiB) measured 0.3-3.5% faster than 10 and 12 per CU
+  // 2-4% slower; at N = 4-7, 10 per CU 7-9% faster than 20, and at N = 2-3 13
+  // per CU (12 KiB), 6% faster at N = 2
+  const size_t fp32_wave = world <= 3 ? 12288 : (world <= 7 ? 16384 : 20480);
+  const size_t one_wave =
+      !bf16 ? fp32_wave : (world <= 7 ? 8192 : (world > 8 && world < 16 ? 12288 : 16384));
   sh.lds = tuning().fused_lds > 0 ? (size_t)tuning().fused_lds : (sh.bs == 64 ? one_wave : 65536);
   if (sh.lds < need) sh.lds = need;
   return sh;

@@ -161,10 +161,12 @@ __global__ __launch_bounds__(kThreads) void k_sumsq_finalize(const double* __res
 // fewer contributions each workgroup moves fewer bytes per memory round trip
 // and more of them must be in flight: full residency was 24-31% faster at
 // N = 2-4 and 14% at N = 5, 20 per CU (8 KiB) 7% faster at N = 6 and 2% at 7.
-inline size_t one_wave_lds(int world) {
+// fp32 rows move twice the bytes per round trip: from N = 8 they take 10 per
+// CU (16 KiB), 1-3% faster than 14.
+inline size_t one_wave_lds(int world, bool bf16) {
   if (world <= 5) return 0;
   if (world <= 7) return 8192;
-  return 11264;
+  return bf16 ? 11264 : 16384;
 }
 
 template <int NW, int CAP, int G, int C, typename In, bool RM = false, bool RAGGED = false>
@@ -175,7 +177,7 @@ hipError_t run_vec(const void* const* rows, int world, int64_t n, float* g, doub
   for (int i = 0; i < CAP; ++i) t.p[i] = i < world ? rows[i] : nullptr;
   const int64_t ngroups = n / 4;
   const int64_t span = (int64_t)BS * G;
-  const size_t lds = G > 1 ? (size_t)G * BS * 16 : one_wave_lds(world);
+  const size_t lds = G > 1 ? (size_t)G * BS * 16 : one_wave_lds(world, sizeof(In) == 2);
   auto go = [&](auto kernel) {
     const void* k = reinterpret_cast<const void*>(kernel);
     const TilePlan plan = span > 64 ? balanced_tiles(ngroups, span, device_slots(s, k, BS, lds))
