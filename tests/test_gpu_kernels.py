@@ -252,6 +252,27 @@ def test_cast_at_every_offset_in_a_cache_line():
             assert np.all(b[:8 + off] == nan16) and np.all(b[8 + off + n:] == nan16), (off, n)
 
 
+def test_cast_with_the_source_off_its_line_grid():
+    # the source 16-byte aligned but 1-7 groups past its 128-byte grid, the
+    # output at offsets on and off its 8-byte grid: the vector part starts
+    # where the output's lines do, so source and output sit at different
+    # offsets within their lines; lengths shorter than that start, several
+    # tiles with a ragged tail, and the guard elements around the slot
+    base = device_rows(650, 1, 300_000 + 64, "f32")[0]
+    nan16 = torch.tensor(float("nan"), dtype=torch.bfloat16).view(torch.int16).item() & 0xFFFF
+    for soff in (4, 8, 12, 16, 20, 24, 28):  # elements past a 128-byte boundary
+        for off in (0, 4, 12, 28, 32, 60, 1, 2):
+            for n in (5, 255, 256 + 64 + 3, 1000, 64 * 256 * 17 + 4 * 37 + 3, 300_000):
+                x = base[soff:soff + n]
+                buf = torch.full((n + 64 + 16,), float("nan"), device="cuda", dtype=torch.bfloat16)
+                out = buf[8 + off:8 + off + n]
+                zs.zs_cast_for_gather(x, out)
+                torch.cuda.synchronize()
+                assert np.array_equal(host(out), obf16.to_bf16_bits(host(x))), (soff, off, n)
+                b = host(buf)
+                assert np.all(b[:8 + off] == nan16) and np.all(b[8 + off + n:] == nan16), (soff, off, n)
+
+
 # world sizes: the one-wave shape (< 16; 2, 4 and 8 have kernels of their
 # own, 9-15 load all their rows in one batch), the rank-major 8-wave shape (16, 32, 64, and 48 and 100 through the
 # kernels for any N up to 64 and up to 256; 30 with fp32 rows), and the same
