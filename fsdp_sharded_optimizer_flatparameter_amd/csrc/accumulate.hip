@@ -278,10 +278,14 @@ void run_accum(const void* const* rows, int world, int64_t n, float* acc, float 
     // in flight: full residency measured 41% faster at N = 2 and 33% at N = 4,
     // 20 per CU (8 KiB) 23% faster at N = 6 (both 3-4% slower at N = 8). The
     // one-batch walk of N = 9-15 over bf16 rows takes 16 per CU (10 KiB): 7-8%
-    // faster than 12 at N = 9-12, 1% at 14-15 (and 3-4% slower with fp32 rows)
+    // faster than 12 at N = 9-12, 1% at 14-15 (and 3-4% slower with fp32 rows).
+    // fp32 rows at N = 5-7 take 13 per CU (12 KiB): 2-5% faster than full
+    // residency at N = 5 and than 20 per CU at N = 6-7
     constexpr bool bf16 = sizeof(In) == 2;
     const size_t lds =
-        world <= 5 ? 0 : (world <= 7 ? 8192 : (bf16 && world > 8 && world < 16 ? 10240 : 13312));
+        (!bf16 && world >= 5 && world <= 7)
+            ? 12288
+            : (world <= 5 ? 0 : (world <= 7 ? 8192 : (bf16 && world > 8 && world < 16 ? 10240 : 13312)));
     if constexpr (NW == 0 && CAP == 64) {
       if (world > 8 && world < 16) {  // 9-15 ranks: one batch of row loads (rank_sums_streamed)
         launch_accum_shape<1, 64, NW, CAP, In, SUMSQ, FIRST, SCALE, false, true>(t, world, n, acc, scale, partials,

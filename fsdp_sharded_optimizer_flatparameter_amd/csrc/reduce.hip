@@ -162,8 +162,10 @@ __global__ __launch_bounds__(kThreads) void k_sumsq_finalize(const double* __res
 // and more of them must be in flight: full residency was 24-31% faster at
 // N = 2-4 and 14% at N = 5, 20 per CU (8 KiB) 7% faster at N = 6 and 2% at 7.
 // fp32 rows move twice the bytes per round trip: from N = 8 they take 10 per
-// CU (16 KiB), 1-3% faster than 14.
+// CU (16 KiB), 1-3% faster than 14; at N = 6-7 also 10 per CU, 3% faster than
+// 20; at N = 5 13 per CU (12 KiB), 4% faster than full residency.
 inline size_t one_wave_lds(int world, bool bf16) {
+  if (!bf16 && world >= 5 && world <= 7) return world == 5 ? 12288 : 16384;
   if (world <= 5) return 0;
   if (world <= 7) return 8192;
   return bf16 ? 11264 : 16384;
