@@ -24,12 +24,13 @@ def _zero2(mbs, n, scale, sumsq=False, offset=0):
     return host(acc), (float(s.item()) if sumsq else None)
 
 
-# world sizes of each launch shape: one-wave (3, 8; 12 loading its rows in one
-# batch), rank-major 8-wave (16, 64,
+# world sizes of each launch shape: one-wave (3, 5-7, 8, with reservations
+# that change with N and the row type; 12 loading its rows in one batch),
+# rank-major 8-wave (16, 64,
 # 100; 30 with fp32 rows), rank-major with the last 1-3 ranks in a short second
 # walk (30 and 31 with bf16 rows, 31, 33, 65)
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("world", [3, 8, 12, 16, 30, 31, 33, 64, 65, 100])
+@pytest.mark.parametrize("world", [3, 5, 6, 7, 8, 12, 16, 30, 31, 33, 64, 65, 100])
 def test_zero2_accumulation_matches_oracle(dtype, world):
     n = 262144 + 5
     # four micro-batches (the sum of squares with the last), and one alone
